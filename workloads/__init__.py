@@ -1,0 +1,19 @@
+"""Seeded synthetic inputs for one round of tree-structured verification.
+
+This package only draws random numbers and lays them out in the shapes the
+round consumes.  It performs none of the method's own arithmetic (no top-k,
+no tree selection, no attention, no argmax walk, no commit), so that both the
+GPU path and the CPU oracle can take their inputs from it.
+"""
+
+from .gen import (  # noqa: F401
+    CONFIGS,
+    Config,
+    Cost,
+    attention_inputs,
+    config,
+    drafter_logits,
+    marginals,
+    prefix_lengths,
+    target_logits,
+)
