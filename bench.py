@@ -1,0 +1,254 @@
+"""Throughput of one tree-structured verification round on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one round of the whole hot path -- build_tree, tree_verify_attn,
+accept_walk, commit_path (one attention layer) -- over one batch of the
+grouped-query bf16 workload: 16 requests, 32 query / 8 KV heads x 128,
+prefix 4096, 16 drafter positions over a 151936-token vocabulary, top-32,
+fixed budget 32 (synthetic, seeded; see workloads/gen.py).  Inputs are
+resident in HBM before timing; three copies of every large input rotate
+across steps so the 256 MB last-level cache cannot serve a step from the
+previous one.  Each step commits into its own copy of the prefix lengths, so
+every step does identical work.
+
+Reported: verified tree tokens/s = sum_b n_b * K / wall time of K steps
+(bracketed by device synchronisation), the attention entry point's achieved
+HBM bandwidth on its algorithmic bytes (HIP events around each call on the
+launch stream), and the CPU oracle timed on the same workload on this
+host's cores.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import tree_structured_verification_amd as tsv  # noqa: E402
+from tree_structured_verification_amd import _lib  # noqa: E402
+from workloads import attention_inputs, config, marginals, target_logits  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = 2
+ROTATE = 3
+
+
+def attention_bytes(cfg, prefix, n):
+    """Algorithmic bytes of one tree_verify_attn launch: every prefix K/V row
+    once, every tree node's Q, scratch K/V and output once, plus lse."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    kv_row = cfg.Hkv * (cfg.d_qk + cfg.d_v) * es if not cfg.mla else cfg.d_qk * es
+    live = n > 0
+    prefix_bytes = int(np.sum(prefix[live].astype(np.int64))) * kv_row
+    nodes = int(np.sum(n))
+    per_node = cfg.Hq * cfg.d_qk * es + kv_row + cfg.Hq * cfg.d_v * es + cfg.Hq * 4
+    return prefix_bytes + nodes * per_node
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=16,
+                    help="requests of the workload the CPU oracle runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    cfg = config(WORKLOAD)
+    print(f"[bench] generating workload {cfg.name} on {torch.cuda.get_device_name(dev)}",
+          file=sys.stderr, flush=True)
+    L = _lib.lib()
+    marg0 = marginals(cfg, 0, dev)
+    ins0 = attention_inputs(cfg, 0, dev)
+    prefix0 = ins0["prefix_len"].clone()
+    # tree of the workload (deterministic), used to lay out the target rows
+    tree0 = tsv.build_tree(marg0, cfg.top_k, cfg.n_budget, cfg.N_max)
+    torch.cuda.synchronize()
+    depth0 = tree0["depth"].cpu().numpy()
+    n0 = tree0["n_nodes"].cpu().numpy()
+    tl0 = target_logits(cfg, 0, depth0, n0, dev)
+
+    sets = []
+    for r in range(ROTATE):
+        c = lambda t: t if r == 0 else t.clone()
+        sets.append(dict(marg=c(marg0), q=c(ins0["q"]), kc=c(ins0["k_cache"]),
+                         vc=c(ins0["v_cache"]), kt=c(ins0["k_tree"]), vt=c(ins0["v_tree"]),
+                         tl=c(tl0)))
+    K, W = args.steps, args.warmup
+    prefixes = [prefix0.clone() for _ in range(K + W)]
+
+    # outputs and workspaces, allocated once
+    B, N, Wd = cfg.B, cfg.N_max, (cfg.N_max + 31) // 32
+    i32 = dict(dtype=torch.int32, device=dev)
+    tr = dict(n_nodes=torch.empty(B, **i32), parent=torch.empty(B, N, **i32),
+              token=torch.empty(B, N, **i32), depth=torch.empty(B, N, **i32),
+              score=torch.empty(B, N, dtype=torch.float32, device=dev),
+              anc_bits=torch.empty(B, N, Wd, **i32))
+    out = torch.empty(B, N, cfg.Hq, cfg.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, N, cfg.Hq, dtype=torch.float32, device=dev)
+    wk = dict(accept_len=torch.empty(B, **i32), accept_nodes=torch.empty(B, cfg.gamma, **i32),
+              out_tokens=torch.empty(B, cfg.gamma + 1, **i32))
+    status = torch.empty(B, **i32)
+    ws_b = tsv.workspace(tsv.workspace_size(0, B, cfg.gamma, cfg.V, cfg.top_k, N), dev)
+    ws_a = tsv.workspace(tsv.workspace_size(1, B, 1, 1, 1, N, cfg.L_cap, cfg.Hq, cfg.Hkv,
+                                            cfg.d_qk, cfg.d_v, tsv.TSV_BF16), dev)
+    ws_w = tsv.workspace(tsv.workspace_size(2, B, cfg.gamma, cfg.V, 1, N, dtype=tsv.TSV_BF16), dev)
+
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stride = cfg.kv_stride
+
+    # pre-marshalled argument tuples: the timed loop only calls the library
+    def step_args(s):
+        st = sets[s % ROTATE]
+        pl = prefixes[s]
+        a_build = (P(st["marg"]), B, cfg.gamma, cfg.V, cfg.top_k, cfg.n_budget, None, None, N,
+                   P(tr["n_nodes"]), P(tr["parent"]), P(tr["token"]), P(tr["depth"]),
+                   P(tr["score"]), P(tr["anc_bits"]), None, None, P(ws_b), ws_b.numel(), sp)
+        a_attn = (P(st["q"]), P(st["kc"]), P(st["vc"]), P(st["kt"]), P(st["vt"]), stride,
+                  P(pl), P(tr["n_nodes"]), P(tr["anc_bits"]), B, N, cfg.L_cap, cfg.Hq, cfg.Hkv,
+                  cfg.d_qk, cfg.d_v, tsv.TSV_BF16, ctypes.c_float(cfg.sm_scale), P(out), P(lse),
+                  P(ws_a), ws_a.numel(), sp)
+        a_walk = (P(st["tl"]), tsv.TSV_BF16, B, N, cfg.V, cfg.gamma, P(tr["n_nodes"]),
+                  P(tr["parent"]), P(tr["token"]), P(wk["accept_len"]), P(wk["accept_nodes"]),
+                  P(wk["out_tokens"]), P(ws_w), ws_w.numel(), sp)
+        a_commit = (P(st["kc"]), P(st["vc"]), P(pl), P(st["kt"]), P(st["vt"]), stride,
+                    P(wk["accept_len"]), P(wk["accept_nodes"]), B, N, cfg.L_cap, cfg.Hkv,
+                    cfg.d_qk, cfg.d_v, cfg.gamma, tsv.TSV_BF16, P(status), sp)
+        return a_build, a_attn, a_walk, a_commit
+
+    all_args = [step_args(s) for s in range(K + W)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K + W)]
+
+    def run(s):
+        a_build, a_attn, a_walk, a_commit = all_args[s]
+        e = ev[s]
+        e[0].record(stream)
+        rc = L.build_tree(*a_build)
+        e[1].record(stream)
+        rc |= L.tree_verify_attn(*a_attn)
+        e[2].record(stream)
+        rc |= L.accept_walk(*a_walk)
+        e[3].record(stream)
+        rc |= L.commit_path(*a_commit)
+        e[4].record(stream)
+        return rc
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for s in range(W):
+        if run(s) != 0:
+            raise RuntimeError("library call failed during warmup")
+    torch.cuda.synchronize()
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    rc = 0
+    for s in range(W, W + K):
+        rc |= run(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if rc != 0:
+        raise RuntimeError("library call failed in the timed loop")
+    if not bool((status == 0).all()):
+        raise RuntimeError("commit reported a non-zero status")
+
+    ms = lambda a, b: np.array([ev[s][a].elapsed_time(ev[s][b]) for s in range(W, W + K)])
+    t_build, t_attn, t_walk, t_commit = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
+    n_np = tr["n_nodes"].cpu().numpy()
+    prefix_np = prefix0.cpu().numpy()
+    tokens = int(n_np.sum())
+    accepted = int(wk["accept_len"].cpu().numpy().sum()) + B
+    value = tokens * K / wall
+    attn_bytes = attention_bytes(cfg, prefix_np, n_np)
+    attn_s = float(np.mean(t_attn)) / 1e3
+    achieved = attn_bytes / attn_s / 1e9
+
+    line = {
+        "metric": "verified tree tokens/s per GPU",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gqa_bf16: 16 requests, Hq 32 / Hkv 8 x 128, prefix 4096, "
+                               "gamma 16, V 151936, top-32, fixed budget 32",
+                   "B": B, "gamma": cfg.gamma, "V": cfg.V, "top_k": cfg.top_k,
+                   "budget": cfg.n_budget, "prefix": cfg.prefix, "Hq": cfg.Hq,
+                   "Hkv": cfg.Hkv, "head_dim": cfg.d_qk},
+        "accepted_tokens_per_s": round(accepted * K / wall, 1),
+        "kernel_ms": {"build_tree": round(float(np.mean(t_build)), 4),
+                      "tree_verify_attn": round(float(np.mean(t_attn)), 4),
+                      "accept_walk": round(float(np.mean(t_walk)), 4),
+                      "commit_path": round(float(np.mean(t_commit)), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "tree_verify_attn",
+                     "algorithmic_bytes": attn_bytes},
+    }
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = run_cpu_baseline(cfg, sets[0], marg0, prefix_np, n_np,
+                                                args.cpu_requests)
+    print(json.dumps(line), flush=True)
+
+
+def run_cpu_baseline(cfg, st, marg_dev, prefix_np, n_gpu, n_req):
+    """One round of the oracle over the first n_req requests of the same
+    inputs (copied to the host before timing), single-threaded BLAS."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    reqs = list(range(min(n_req, cfg.B)))
+    f32 = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+    marg = marg_dev[reqs].cpu().numpy()
+    q, kc, vc = f32(st["q"][reqs]), f32(st["kc"][reqs]), f32(st["vc"][reqs])
+    kt, vt = f32(st["kt"][reqs]), f32(st["vt"][reqs])
+    tl = f32(st["tl"][reqs])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        idx, p = oracle.topk_per_position(marg, cfg.top_k)
+        trees = [oracle.select_tree(idx[j], p[j], cfg.n_budget, cfg.N_max) for j in range(len(reqs))]
+        for j, t in enumerate(trees):
+            oracle.attend_request(q[j], kc[j], vc[j], kt[j], vt[j], int(prefix_np[j]), t.n,
+                                  t.parent, cfg.sm_scale)
+        alen = np.zeros(len(reqs), np.int32)
+        anodes = np.full((len(reqs), cfg.gamma), -1, np.int32)
+        for j, t in enumerate(trees):
+            m, nodes, _ = oracle.accept_walk(tl[j], t.n, t.parent, t.token, cfg.gamma)
+            alen[j], anodes[j] = m, nodes
+        pl = prefix_np[reqs].copy()
+        oracle.commit_path(kc, vc, pl, kt, vt, alen, anodes, cfg.gamma)
+        dt = time.perf_counter() - t0
+    tokens = sum(t.n for t in trees)
+    if [t.n for t in trees] != n_gpu[reqs].tolist():
+        raise RuntimeError("oracle and GPU trees differ in size")
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full round (top-k, tree, attention of all {tokens} nodes, walk, "
+                      f"commit) of {len(reqs)} of the {cfg.B} requests, {dt:.1f} s, "
+                      "numpy with BLAS limited to one thread"}
+
+
+if __name__ == "__main__":
+    main()

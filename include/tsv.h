@@ -1,0 +1,214 @@
+/*
+ * tsv.h -- one round of tree-structured speculative verification on AMD
+ * Instinct MI355X (gfx950), as a C ABI.
+ *
+ * Sources of the method (cited by page title and section):
+ *   [review]   "Adapting Tree-Structured Speculative Decoding to DeepSeek-V4 for
+ *              Efficient Inference" -- blog review of arXiv 2609.24698
+ *   [dspark]   "DSpark: Speculative decoding ... LLM inference acceleration"
+ *   [caddtree] "Cost-Aware Diffusion Draft Trees for Speculative Decoding"
+ *              -- summary of arXiv 2606.01813
+ *
+ * A round is four calls, in this order:
+ *   build_tree        drafter marginals -> best-first draft tree (+ budget)
+ *   tree_verify_attn  branch-aware attention of every tree node
+ *   accept_walk       target argmax -> longest accepted root-to-node path
+ *   commit_path       accepted scratch KV -> persistent cache
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer to a caller-owned, contiguous,
+ *     row-major buffer, except `cost` (host).  The library never allocates,
+ *     frees or synchronises, never reads device memory from the host and
+ *     keeps no state between calls; calls are reentrant.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns before it runs.
+ *   - Host-side argument checks fail with a negative status before anything is
+ *     launched.  A failed launch returns TSV_EHIP.  Conditions only the device
+ *     can see are reported per request through output arrays (commit_path's
+ *     `status`); no kernel traps.
+ *   - Ragged per-request sizes (prefix lengths, node counts, accepted lengths)
+ *     are read on the device only; out-of-range values are clamped, so a
+ *     wrong size never leads to an access outside the documented shapes.
+ *   - Floating-point inputs must be finite (marginals also non-negative);
+ *     results for NaN inputs are unspecified but memory-safe.
+ *   - `ws` is device scratch of at least tsv_workspace_size(...) bytes, owned
+ *     by the caller, 256-byte aligned; its contents on entry do not matter.
+ *     Two calls that run concurrently need distinct workspaces.
+ *
+ * Notation: B requests; gamma drafter positions (= maximum tree depth);
+ * V vocabulary; k top-k branches per position; N_max node capacity
+ * (<= 128); n_b nodes of request b (the root excluded); l_b persistent
+ * prefix length of request b (it includes the root, the last accepted
+ * token); Hq / Hkv query / KV heads; d_qk / d_v key and value widths;
+ * L_cap cache rows per request.
+ */
+#ifndef TSV_H
+#define TSV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { TSV_F32 = 0, TSV_BF16 = 1 };
+
+enum {
+  TSV_OK = 0,
+  TSV_EINVAL = -1,       /* bad pointer, size or argument combination        */
+  TSV_EUNSUPPORTED = -2, /* well-formed but outside what the kernels support */
+  TSV_EWORKSPACE = -3,   /* workspace missing, misaligned or too small       */
+  TSV_EHIP = -4          /* a kernel launch failed                           */
+};
+
+/* Round-cost coefficients ([caddtree] Methodology, item 1, with item 5's
+ * convex, monotone verification cost):
+ *   C(n; l) = c_d + C_v(n; l),  C_v(n; l) = a + b*n + c*n^2 + e*l*n.
+ * Requirements: a + c_d > 0 and b, c, e >= 0 (so C > 0, convex, monotone). */
+typedef struct {
+  double a, b, c, e, c_d;
+} tsv_cost;
+
+/*
+ * build_tree -- per-position top-k, then the greedy best-first tree.
+ *
+ * [caddtree] Methodology, items 2-4: the drafter's single-pass per-position
+ * marginals give each candidate node a prefix probability (the product of the
+ * marginals along its path); for a fixed node budget n the best tree holds
+ * the n candidates of highest prefix probability, and the budget n* of a
+ * round is found greedily by adding nodes best-first while the throughput
+ * (1 + Phi_n) / C(n; l) still rises.  [review] "How it works", steps 1-2:
+ * top-k branches per drafting step, pruned to the budget by score.
+ *
+ * Inputs
+ *   marginals   fp32 [B][gamma][V]  drafter probabilities (finite, >= 0)
+ *   top_k       1 <= top_k <= min(V, 128)
+ *   n_budget    cost == NULL: the fixed budget D (n_b = min(D, #candidates));
+ *               cost != NULL: the cap of the adaptive budget.  0 <= n_budget
+ *               <= N_max.
+ *   cost        HOST pointer or NULL (fixed budget)
+ *   prefix_len  int32 [B], read only when cost != NULL (l in C_v)
+ *   N_max       1 <= N_max <= 128; gamma <= 64; gamma * top_k <= 8192
+ * Outputs (device, written for every b and every i < N_max)
+ *   n_nodes     int32 [B]
+ *   parent      int32 [B][N_max]  parent node index, -1 = child of the root
+ *   token       int32 [B][N_max]  drafted token id
+ *   depth       int32 [B][N_max]  1-based depth (= drafter position + 1)
+ *   score       fp32  [B][N_max]  prefix probability
+ *   anc_bits    uint32 [B][N_max][ceil(N_max/32)]  bit j of row i set iff node
+ *               j is node i or one of its ancestors
+ *   topk_idx    int32 [B][gamma][top_k] or NULL   the per-position top-k ids
+ *   topk_p      fp32  [B][gamma][top_k] or NULL   and their probabilities
+ *   Entries i >= n_nodes[b] are -1 (ints), 0.0f (score) and 0 (anc_bits).
+ * Order and ties
+ *   top-k: probability descending, then token id ascending (-0 == +0).
+ *   nodes: numbered in best-first order, i.e. ascending by the nested key
+ *   (-score, depth, key(parent), rank), so parents precede children.
+ *   Scores are fp32 products parent_score * q (root 1, round-to-nearest,
+ *   never fused); Phi and C are fp64 in the order
+ *   c_d + (((a + b*n) + c*(n*n)) + (e*l)*n); a node is added iff
+ *   (1 + Phi_{n+1}) / C(n+1) > (1 + Phi_n) / C(n).
+ */
+int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
+               int n_budget, const tsv_cost* cost, const int* prefix_len,
+               int N_max, int* n_nodes, int* parent, int* token, int* depth,
+               float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
+               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tree_verify_attn -- branch-aware tree attention over a shared prefix.
+ *
+ * [review] Difficulty 1 (paper section 3.1) and "How it works", step 3: each
+ * candidate attends only to its own ancestors, never to other branches;
+ * section 6 as quoted: with dense attention the tree is a mask over the
+ * shared KV.  For request b, node i < n_b and query head h the keys are the
+ * prefix rows 0..l_b-1 plus the scratch rows j whose bit is set in
+ * anc_bits[b][i]; out = softmax(sm_scale * q.K^T) V and
+ * lse = log(sum(exp(sm_scale * q.K^T))) (natural log).  Query head h uses KV
+ * head h / (Hq / Hkv).
+ *
+ * Layouts (dtype TSV_BF16 or TSV_F32 for q, caches, scratch and out)
+ *   q         [B][N_max][Hq][d_qk]
+ *   k_cache   [B][L_cap] rows of kv_row_stride elements; KV head g's key is
+ *             at element offset g*d_qk of a row
+ *   v_cache   same row layout; head g's value is at offset g*d_v.  A latent
+ *             cache (one head whose value is the first d_v columns of the
+ *             key) passes v_cache == k_cache.
+ *   k_tree, v_tree  [B][N_max] rows of kv_row_stride elements (scratch pad)
+ *   prefix_len int32 [B]  (clamped to [0, L_cap])
+ *   n_nodes   int32 [B]   (clamped to [0, N_max])
+ *   anc_bits  uint32 [B][N_max][ceil(N_max/32)]  as written by build_tree
+ *   out       [B][N_max][Hq][d_v]  rows i >= n_b are left untouched
+ *   lse       fp32 [B][N_max][Hq] or NULL
+ * Requirements: Hq % Hkv == 0; kv_row_stride >= Hkv*max(d_qk, d_v);
+ * 1 <= d_qk, d_v <= 576.  Accumulation is fp32.
+ */
+int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const void* k_tree, const void* v_tree, long kv_row_stride,
+                     const int* prefix_len, const int* n_nodes,
+                     const unsigned* anc_bits, int B, int N_max, int L_cap,
+                     int Hq, int Hkv, int d_qk, int d_v, int dtype,
+                     float sm_scale, void* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * accept_walk -- greedy acceptance of the longest matching path.
+ *
+ * [review] "How it works", steps 5-6 and [dspark] decoding cycle: the target
+ * verifies all branches at once; the accepted tokens are the longest
+ * root-to-node path whose every token equals the target's argmax at its
+ * parent, followed by the target's own next token (the bonus).
+ *
+ *   target_logits  dtype [B][1 + N_max][V]; row 0 = the root's prediction,
+ *                  row 1+i = node i's.  Only rows 0..n_b are read.
+ *   n_nodes, parent, token  as written by build_tree
+ * Outputs
+ *   accept_len   int32 [B]          m_b, accepted tree nodes (bonus excluded)
+ *   accept_nodes int32 [B][gamma]   accepted node indices, then -1
+ *   out_tokens   int32 [B][gamma+1] accepted tokens, the bonus, then -1
+ * argmax ties go to the lowest token id; the walk stops after gamma steps;
+ * if several children of a node carry the argmax token (impossible for trees
+ * from build_tree) the lowest node index is taken.
+ */
+int accept_walk(const void* target_logits, int dtype, int B, int N_max, int V,
+                int gamma, const int* n_nodes, const int* parent,
+                const int* token, int* accept_len, int* accept_nodes,
+                int* out_tokens, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * commit_path -- write the accepted chain into the persistent cache.
+ *
+ * [review] "Secret weapon" (paper section 4.2 as quoted) and "How it works",
+ * step 6: tentative branch state stays in the scratch pad; after selection
+ * only the accepted path's KV is written to the persistent cache and the
+ * rest is discarded; the next round starts from the extended prefix.
+ *
+ * For j < m_b: cache row l_b + j <- scratch row accept_nodes[b][j] (the first
+ * Hkv*d_k elements of a key row and Hkv*d_v of a value row); then
+ * prefix_len[b] += m_b.  v_cache/v_tree may be NULL (latent cache).
+ * status int32 [B]: 0 committed; 1 l_b + m_b > L_cap (nothing written);
+ * 2 m_b outside [0, gamma], l_b < 0 or a node index outside [0, N_max)
+ * (nothing written).  Rows of rejected nodes are never read.
+ */
+int commit_path(void* k_cache, void* v_cache, int* prefix_len,
+                const void* k_tree, const void* v_tree, long kv_row_stride,
+                const int* accept_len, const int* accept_nodes, int B,
+                int N_max, int L_cap, int Hkv, int d_k, int d_v, int gamma,
+                int dtype, int* status, void* stream);
+
+/* Workspace bytes needed by entry point `which` (0 build_tree,
+ * 1 tree_verify_attn, 2 accept_walk, 3 commit_path) for these sizes.
+ * Arguments an entry point does not use are ignored.  Returns 0 for
+ * invalid sizes. */
+size_t tsv_workspace_size(int which, int B, int gamma, int V, int top_k,
+                          int N_max, int L_cap, int Hq, int Hkv, int d_qk,
+                          int d_v, int dtype);
+
+/* Static description of a status code. */
+const char* tsv_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSV_H */

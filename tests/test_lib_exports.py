@@ -1,0 +1,81 @@
+"""The C-ABI library loads without a GPU, exports every symbol the header
+declares, and rejects bad arguments on the host before any launch (CPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_structured_verification_amd as tsv
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "tsv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_all_declared_symbols_exported():
+    names = _declared()
+    assert names == sorted(["build_tree", "tree_verify_attn", "accept_walk", "commit_path",
+                            "tsv_workspace_size", "tsv_status_string"])
+    lib = ctypes.CDLL(tsv._lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert tsv.status_string(0) == "ok"
+    assert "workspace" in tsv.status_string(-3)
+    assert tsv.status_string(123) == "unknown status"
+
+
+def test_workspace_sizes():
+    ws = tsv.workspace_size
+    assert ws(0, 16, 16, 151936, 32, 32) > 0
+    assert ws(0, 1, 65, 16, 8, 8) == 0              # gamma too large
+    assert ws(0, 1, 4, 16, 8, 129) == 0             # N_max too large
+    assert ws(1, 16, 1, 1, 1, 32, 4112, 32, 8, 128, 128, 1) > 0
+    assert ws(1, 16, 1, 1, 1, 32, 4112, 30, 8, 128, 128, 1) == 0    # Hq % Hkv
+    assert ws(2, 16, 16, 151936, 1, 32, dtype=1) > 0
+    assert ws(3) == 0
+    # larger caps never need less workspace
+    assert ws(1, 64, 1, 1, 1, 128, 32784, 32, 8, 128, 128, 1) >= ws(1, 16, 1, 1, 1, 32, 4112, 32, 8, 128, 128, 1)
+
+
+def test_host_validation_without_launch():
+    L = tsv.lib()
+    nul = None
+    # null pointers
+    assert L.build_tree(nul, 1, 1, 1, 1, 1, None, nul, 1, nul, nul, nul, nul, nul, nul,
+                        nul, nul, nul, 0, nul) == -1
+    assert L.tree_verify_attn(nul, nul, nul, nul, nul, 64, nul, nul, nul, 1, 1, 1, 1, 1, 64,
+                              64, 0, 0.1, nul, nul, nul, 0, nul) == -1
+    assert L.accept_walk(nul, 0, 1, 1, 1, 1, nul, nul, nul, nul, nul, nul, nul, 0, nul) == -1
+    assert L.commit_path(nul, nul, nul, nul, nul, 1, nul, nul, 1, 1, 1, 1, 1, 1, 1, 0, nul,
+                         nul) == -1
+    # non-null fake device addresses that are never dereferenced: argument
+    # checks fail first, so nothing is launched
+    p = ctypes.c_void_p(0x1000)
+    assert L.build_tree(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                        1 << 20, nul) == -1                       # top_k > V
+    assert L.build_tree(p, 1, 2, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                        16, nul) == -3                            # workspace too small
+    assert L.tree_verify_attn(p, p, p, p, p, 64, p, p, p, 1, 4, 10, 4, 3, 64, 64, 1, 0.1,
+                              p, nul, p, 1 << 30, nul) == -1      # Hq % Hkv
+    assert L.tree_verify_attn(p, p, p, p, p, 10, p, p, p, 1, 4, 10, 4, 2, 64, 64, 1, 0.1,
+                              p, nul, p, 1 << 30, nul) == -1      # stride < Hkv * d
+    assert L.tree_verify_attn(p, p, p, p, p, 1200, p, p, p, 1, 4, 10, 4, 2, 600, 64, 1, 0.1,
+                              p, nul, p, 1 << 30, nul) == -2      # head dim > 576
+    assert L.accept_walk(p, 1, 1, 4, 8, 65, p, p, p, p, p, p, p, 1 << 20, nul) == -2  # gamma
+    assert L.commit_path(p, nul, p, p, p, 64, p, p, 1, 4, 8, 1, 64, 64, 2, 1, p, nul) == -1
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        tsv.build_tree(torch.zeros(1, 2, 8), 2, 2, 4)

@@ -1,0 +1,167 @@
+"""tree_verify_attn on the GPU vs the fp64 oracle (tolerance 1e-5 fp32,
+2e-2 bf16), plus bitwise properties: sibling isolation and determinism."""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_structured_verification_amd as tsv
+from tests._helpers import DEV, TOL, check_attention, np32, oracle_trees
+from workloads import attention_inputs, config, marginals
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_trees(rng, B, N_max, n_list):
+    """Random ancestor-closed trees (parents precede children)."""
+    trees = []
+    for b in range(B):
+        n = n_list[b]
+        parent = np.full(N_max, -1, dtype=np.int32)
+        for i in range(1, n):
+            parent[i] = rng.integers(-1, i)
+        t = oracle.tree.TreeResult(n, parent, np.full(N_max, -1, np.int32),
+                                   np.full(N_max, -1, np.int32), np.zeros(N_max, np.float32),
+                                   oracle.ancestor_bits(parent, n, N_max))
+        trees.append(t)
+    return trees
+
+
+def _inputs(rng, B, N_max, L_cap, Hq, Hkv, d_qk, d_v, dtype, prefix, mla=False):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(int(rng.integers(1 << 30)))
+    rn = lambda *s: torch.randn(*s, generator=g, device=DEV, dtype=torch.float32).to(dtype)
+    q = rn(B, N_max, Hq, d_qk)
+    if mla:
+        kc = rn(B, L_cap, d_qk)
+        kt = rn(B, N_max, d_qk)
+        vc, vt = kc, kt
+    else:
+        kc = rn(B, L_cap, Hkv, d_qk)
+        kt = rn(B, N_max, Hkv, d_qk)
+        vc = rn(B, L_cap, Hkv, d_v)
+        vt = rn(B, N_max, Hkv, d_v)
+    pl = torch.tensor(prefix, dtype=torch.int32, device=DEV)
+    return q, kc, vc, kt, vt, pl
+
+
+def _run(q, kc, vc, kt, vt, pl, trees, Hkv, d_v, scale):
+    B, N_max = q.shape[:2]
+    n = torch.tensor([t.n for t in trees], dtype=torch.int32, device=DEV)
+    anc = torch.from_numpy(np.stack([t.anc_bits for t in trees]).view(np.int32)).to(DEV)
+    out = torch.full((B, N_max, q.shape[2], d_v), float("nan"), dtype=q.dtype, device=DEV)
+    o, lse = tsv.tree_verify_attn(q, kc, vc, kt, vt, pl, n, anc, Hkv, d_v, scale, out=out)
+    torch.cuda.synchronize()
+    return o, lse, n, anc
+
+
+CASES = [
+    # name, B, N_max, Hq, Hkv, d_qk, d_v, dtype, prefix, n, mla
+    ("fp32_mha", 2, 8, 4, 4, 64, 64, torch.float32, [100, 37], [8, 3], False),
+    ("fp32_gqa_long", 1, 20, 8, 2, 32, 32, torch.float32, [3000], [20], False),
+    ("bf16_gqa_mfma", 3, 40, 8, 2, 128, 128, torch.bfloat16, [700, 64, 1], [40, 5, 0], False),
+    ("bf16_gqa_g4", 4, 32, 32, 8, 128, 128, torch.bfloat16, [257, 4096, 1000, 63], [32, 1, 17, 32], False),
+    ("bf16_many_splits", 1, 32, 16, 4, 128, 128, torch.bfloat16, [20000], [31], False),
+    ("bf16_latent_mfma", 2, 8, 16, 1, 576, 512, torch.bfloat16, [300, 33], [8, 2], True),
+    ("bf16_latent_long", 1, 16, 128, 1, 576, 512, torch.bfloat16, [5000], [16], True),
+    ("bf16_valu_d64", 2, 12, 6, 3, 64, 64, torch.bfloat16, [500, 9], [12, 7], False),
+    ("bf16_n128_prefix0", 1, 128, 4, 1, 128, 128, torch.bfloat16, [0], [128], False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_small_cases(case):
+    name, B, N_max, Hq, Hkv, d_qk, d_v, dtype, prefix, n_list, mla = case
+    print(f"attention case {name}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    L_cap = max(prefix) + 16
+    q, kc, vc, kt, vt, pl = _inputs(rng, B, N_max, L_cap, Hq, Hkv, d_qk, d_v, dtype, prefix, mla)
+    trees = _random_trees(rng, B, N_max, n_list)
+    scale = 1.0 / math.sqrt(d_qk)
+    o, lse, _, _ = _run(q, kc, vc, kt, vt, pl, trees, Hkv, d_v, scale)
+    check_attention(o, lse, q, kc, vc, kt, vt, prefix, trees, scale, TOL[dtype], mla, d_v)
+    # rows past n_b are never written
+    on = o.float().cpu().numpy()
+    for b in range(B):
+        assert np.isnan(on[b, n_list[b]:]).all()
+
+
+def test_sibling_isolation_and_determinism():
+    """Perturbing scratch rows that are not ancestors of node i leaves node i's
+    output bit-identical; two identical calls give identical bits."""
+    rng = np.random.default_rng(3)
+    B, N_max, Hq, Hkv, d = 2, 16, 8, 2, 128
+    prefix = [900, 130]
+    q, kc, vc, kt, vt, pl = _inputs(rng, B, N_max, 1000, Hq, Hkv, d, d, torch.bfloat16, prefix)
+    trees = _random_trees(rng, B, N_max, [16, 11])
+    scale = 0.088
+    o1, l1, _, _ = _run(q, kc, vc, kt, vt, pl, trees, Hkv, d, scale)
+    o2, l2, _, _ = _run(q, kc, vc, kt, vt, pl, trees, Hkv, d, scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for b in range(B):
+        for i in range(trees[b].n):
+            anc = {j for j in range(N_max) if trees[b].anc_bits[i, j // 32] >> (j % 32) & 1}
+            others = [j for j in range(trees[b].n) if j not in anc]
+            if not others:
+                continue
+            kt2, vt2 = kt.clone(), vt.clone()
+            kt2[b, others] = (kt2[b, others].float() * -3.0 + 1.0).to(kt.dtype)
+            vt2[b, others] = (vt2[b, others].float() + 5.0).to(vt.dtype)
+            o3, l3, _, _ = _run(q, kc, vc, kt2, vt2, pl, trees, Hkv, d, scale)
+            assert torch.equal(o3[b, i], o1[b, i]) and torch.equal(l3[b, i], l1[b, i])
+            if i == 0 and b == 0:
+                # and an ancestor perturbation does change it
+                kt3 = kt.clone()
+                kt3[b, i] = (kt3[b, i].float() * -2.0).to(kt.dtype)
+                o4, _, _, _ = _run(q, kc, vc, kt3, vt, pl, trees, Hkv, d, scale)
+                assert not torch.equal(o4[b, i], o1[b, i])
+
+
+SAMPLES = {2: 48, 3: 12, 4: 40, 5: 8}
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload(cid):
+    """Full-size inputs, trees built by the oracle; every node checked for
+    the tiny workload, a seeded sample of nodes otherwise."""
+    cfg = config(cid)
+    print(f"attention workload {cid} {cfg.name}", flush=True)
+    ins = attention_inputs(cfg, 0, DEV)
+    pl_np = ins["prefix_len"].cpu().numpy()
+    marg = marginals(cfg, 0, DEV).cpu().numpy()
+    _, _, trees = oracle_trees(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cfg.cost, pl_np)
+    o, lse, _, _ = _run(ins["q"], ins["k_cache"], ins["v_cache"], ins["k_tree"], ins["v_tree"],
+                        ins["prefix_len"], trees, cfg.Hkv, cfg.d_v, cfg.sm_scale)
+    samples = None
+    if cid in SAMPLES:
+        rng = np.random.default_rng(cid)
+        pairs = [(b, i) for b in range(cfg.B) for i in range(trees[b].n)]
+        pick = rng.choice(len(pairs), size=min(SAMPLES[cid], len(pairs)), replace=False)
+        samples = sorted(pairs[j] for j in pick)
+        # always include the last node of the longest request
+        bl = int(np.argmax([t.n for t in trees]))
+        samples.append((bl, trees[bl].n - 1))
+    worst = check_attention(o, lse, ins["q"], ins["k_cache"], ins["v_cache"], ins["k_tree"],
+                            ins["v_tree"], pl_np, trees, cfg.sm_scale, TOL[cfg.torch_dtype],
+                            cfg.mla, cfg.d_v, samples)
+    print(f"workload {cid}: max |gpu - oracle| = {worst:.3e}", flush=True)
+
+
+def test_invalid_arguments():
+    q = torch.zeros(1, 4, 4, 64, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(1, 10, 2, 64, dtype=torch.bfloat16, device=DEV)
+    kt = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16, device=DEV)
+    pl = torch.zeros(1, dtype=torch.int32, device=DEV)
+    n = torch.zeros(1, dtype=torch.int32, device=DEV)
+    anc = torch.zeros(1, 4, 1, dtype=torch.int32, device=DEV)
+    with pytest.raises(tsv.TsvError) as e:
+        tsv.tree_verify_attn(q, kc, kc, kt, kt, pl, n, anc, 3, 64, 0.1)   # Hq % Hkv
+    assert e.value.code == -1
+    with pytest.raises(tsv.TsvError) as e:
+        tsv.tree_verify_attn(q, kc, kc, kt, kt, pl, n, anc, 2, 64, 0.1,
+                             ws=torch.empty(64, dtype=torch.uint8, device=DEV))
+    assert e.value.code == -3

@@ -1,0 +1,116 @@
+"""build_tree on the GPU vs the oracle: bit-exact top-k lists and trees."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import tree_structured_verification_amd as tsv
+from tests._helpers import DEV, assert_tree_equal, oracle_trees
+from workloads import Cost, config, marginals, prefix_lengths
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(marg_np, top_k, n_budget, N_max, cost=None, prefix=None):
+    m = torch.from_numpy(np.ascontiguousarray(marg_np, dtype=np.float32)).to(DEV)
+    pl = None if prefix is None else torch.from_numpy(np.asarray(prefix, np.int32)).to(DEV)
+    g = tsv.build_tree(m, top_k, n_budget, N_max, cost=cost, prefix_len=pl, with_topk=True)
+    torch.cuda.synchronize()
+    idx, p, trees = oracle_trees(marg_np, top_k, n_budget, N_max, cost, prefix)
+    assert_tree_equal(g, idx, p, trees)
+    return g, trees
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload(cid):
+    cfg = config(cid)
+    print(f"build_tree workload {cid} {cfg.name}", flush=True)
+    marg = marginals(cfg, 0, DEV)
+    pl = prefix_lengths(cfg) if cfg.cost is not None else None
+    _run(marg.cpu().numpy(), cfg.top_k, cfg.n_budget, cfg.N_max, cfg.cost, pl)
+
+
+def _quantised(rng, shape, levels):
+    """Probabilities drawn from a few values: many exact ties."""
+    x = rng.integers(0, levels, size=shape).astype(np.float64) + 1.0
+    x /= x.sum(-1, keepdims=True)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("top_k", [1, 5, 63, 64, 65, 128])
+@pytest.mark.parametrize("V", [10000, 9999])
+def test_ties_segments_and_vocab_tail(top_k, V):
+    """Several scan segments per row, a vocabulary that is not a multiple of
+    the vector width, and quantised probabilities (ties at every level)."""
+    rng = np.random.default_rng(top_k * 7 + V)
+    marg = _quantised(rng, (3, 5, V), 4)
+    N_max = 128
+    for n_budget in (0, 1, 17, 128):
+        _run(marg, top_k, n_budget, N_max)
+
+
+def test_uniform_marginals_total_ties():
+    marg = np.full((2, 4, 300), 1.0 / 300, dtype=np.float32)
+    for k in (1, 3, 16):
+        _run(marg, k, 40, 64)
+
+
+def test_signed_zero_and_tiny_values():
+    rng = np.random.default_rng(5)
+    marg = rng.random((2, 3, 4000)).astype(np.float32) * 1e-38   # denormal products
+    marg[:, :, ::7] = 0.0
+    marg[:, :, 3::11] = -0.0
+    marg[0, 0, 17] = 0.9
+    _run(marg, 8, 30, 32)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_adaptive_budget(seed):
+    rng = np.random.default_rng(seed)
+    B, gamma, V = 6, 12, 3000
+    lg = rng.normal(0, 3, size=(B, gamma, V)) / rng.uniform(0.3, 2.0, size=(B, 1, 1))
+    marg = np.exp(lg - lg.max(-1, keepdims=True))
+    marg = (marg / marg.sum(-1, keepdims=True)).astype(np.float32)
+    prefix = rng.integers(0, 200000, size=B).astype(np.int32)
+    base = Cost(a=1.0, b=0.02, c=1e-4, e=1e-6, c_d=0.5)
+    for cost in (base, dataclasses.replace(base, c=0.0, b=0.001),
+                 dataclasses.replace(base, a=0.75, b=0.5, c=0.0, e=0.0, c_d=0.25)):
+        for cap in (0, 7, 100):
+            _run(marg, 32, cap, 100, cost, prefix)
+
+
+def test_exact_zero_gain_stops():
+    """(1 + 0.5) / (1 + 0.5) equals 1 / 1 exactly: the first node is not added."""
+    marg = np.zeros((1, 2, 8), dtype=np.float32)
+    marg[0, 0, 3] = 0.5
+    marg[0, 1, 1] = 0.25
+    cost = Cost(a=0.75, b=0.5, c=0.0, e=0.0, c_d=0.25)
+    g, trees = _run(marg, 2, 4, 4, cost, [0])
+    assert trees[0].n == 0 and int(g["n_nodes"][0]) == 0
+
+
+def test_chain_and_small_shapes():
+    rng = np.random.default_rng(9)
+    marg = rng.dirichlet(np.ones(50), size=(4, 7)).astype(np.float32)
+    _run(marg, 1, 5, 8)      # linear: top-1 chain
+    _run(marg, 1, 8, 8)      # budget above the 7 candidates
+    _run(marg[:, :1], 3, 3, 3)
+    _run(marg, 50, 1, 1)     # k = V
+
+
+def test_invalid_arguments_return_status():
+    m = torch.zeros((1, 2, 8), dtype=torch.float32, device=DEV)
+    with pytest.raises(tsv.TsvError) as e:
+        tsv.build_tree(m, 9, 2, 4)       # k > V
+    assert e.value.code == -1
+    with pytest.raises(tsv.TsvError):
+        tsv.build_tree(m, 2, 5, 4)       # budget > N_max
+    with pytest.raises(tsv.TsvError) as e:
+        tsv.build_tree(m, 2, 2, 129)     # N_max > 128
+    assert e.value.code in (-1, -2)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(tsv.TsvError) as e:
+        tsv.build_tree(m, 2, 2, 4, ws=ws)
+    assert e.value.code == -3

@@ -1,0 +1,20 @@
+"""Tree-structured speculative verification on AMD Instinct MI355X (gfx950).
+
+One verification round = four calls into the HIP library libtsv.so
+(include/tsv.h): build_tree, tree_verify_attn, accept_walk, commit_path.
+This package is the thin Python binding over that C ABI.
+"""
+
+from ._lib import (  # noqa: F401
+    TSV_BF16,
+    TSV_F32,
+    TsvError,
+    accept_walk,
+    build_tree,
+    commit_path,
+    lib,
+    status_string,
+    tree_verify_attn,
+    workspace,
+    workspace_size,
+)

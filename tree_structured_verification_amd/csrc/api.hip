@@ -1,0 +1,260 @@
+// C ABI of the tree-structured verification library: argument checks,
+// workspace layout and kernel launches.  Nothing here allocates, frees,
+// synchronises or reads device memory.
+
+#include <math.h>
+
+#include "tsv_internal.hpp"
+
+using namespace tsv;
+
+namespace {
+
+constexpr int kMaxNodes = 128;
+constexpr int kMaxGamma = 64;
+constexpr int kMaxTopk = 128;
+constexpr int kMaxTopkTable = 4096;  // gamma * top_k staged in LDS by the tree kernel
+constexpr int kMaxHeadDim = 576;
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int esize(int dtype) { return dtype == TSV_F32 ? 4 : 2; }
+bool dtype_ok(int dtype) { return dtype == TSV_F32 || dtype == TSV_BF16; }
+
+bool finite_nonneg(double x) { return isfinite(x) && x >= 0.0; }
+
+struct BuildLayout {
+  TopkPlan plan;
+  size_t off_seg, off_idx, off_p, bytes;
+};
+BuildLayout build_layout(int B, int gamma, int V, int top_k) {
+  BuildLayout L;
+  const int rows = B * gamma;
+  L.plan = topk_plan(rows, V, top_k);
+  size_t off = 0;
+  L.off_seg = off;
+  off = align_up(off + topk_ws_bytes(L.plan));
+  L.off_idx = off;
+  off = align_up(off + static_cast<size_t>(rows) * top_k * sizeof(int));
+  L.off_p = off;
+  off = align_up(off + static_cast<size_t>(rows) * top_k * sizeof(float));
+  L.bytes = off;
+  return L;
+}
+
+bool build_sizes_ok(int B, int gamma, int V, int top_k, int N_max) {
+  if (B < 1 || gamma < 1 || V < 1 || top_k < 1 || N_max < 1) return false;
+  if (gamma > kMaxGamma || N_max > kMaxNodes || top_k > kMaxTopk || top_k > V) return false;
+  if (gamma * top_k > kMaxTopkTable) return false;
+  if (static_cast<long long>(B) * gamma > (1LL << 24)) return false;
+  return true;
+}
+
+bool attn_sizes_ok(int B, int N_max, int L_cap, int Hq, int Hkv, int d_qk, int d_v) {
+  if (B < 1 || N_max < 1 || N_max > kMaxNodes || L_cap < 0 || Hq < 1 || Hkv < 1) return false;
+  if (Hq % Hkv != 0) return false;
+  if (d_qk < 1 || d_v < 1 || d_qk > kMaxHeadDim || d_v > kMaxHeadDim) return false;
+  if (static_cast<long long>(B) * N_max * Hq > (1LL << 30)) return false;
+  return true;
+}
+
+size_t attn_bytes_any(const AttnShape& sh) {
+  size_t a = attn_plan(sh, true).bytes, b = attn_plan(sh, false).bytes;
+  return a > b ? a : b;
+}
+
+size_t walk_bytes(int B, int N_max, int V, int dtype) {
+  const int rows = B * (N_max + 1);
+  const ArgmaxPlan p = argmax_plan(rows, V, dtype);
+  return align_up(static_cast<size_t>(rows) * p.nseg * sizeof(uint64_t));
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tsv_status_string(int code) {
+  switch (code) {
+    case TSV_OK: return "ok";
+    case TSV_EINVAL: return "invalid argument";
+    case TSV_EUNSUPPORTED: return "unsupported shape or dtype";
+    case TSV_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case TSV_EHIP: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t tsv_workspace_size(int which, int B, int gamma, int V, int top_k,
+                          int N_max, int L_cap, int Hq, int Hkv, int d_qk,
+                          int d_v, int dtype) {
+  switch (which) {
+    case 0:
+      if (!build_sizes_ok(B, gamma, V, top_k, N_max)) return 0;
+      return build_layout(B, gamma, V, top_k).bytes;
+    case 1: {
+      if (!attn_sizes_ok(B, N_max, L_cap, Hq, Hkv, d_qk, d_v) || !dtype_ok(dtype)) return 0;
+      AttnShape sh{B, N_max, L_cap, Hq, Hkv, d_qk, d_v, dtype};
+      return attn_bytes_any(sh);
+    }
+    case 2:
+      if (B < 1 || N_max < 1 || N_max > kMaxNodes || V < 1 || !dtype_ok(dtype)) return 0;
+      return walk_bytes(B, N_max, V, dtype);
+    case 3:
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
+               int n_budget, const tsv_cost* cost, const int* prefix_len,
+               int N_max, int* n_nodes, int* parent, int* token, int* depth,
+               float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
+               void* ws, size_t ws_bytes, void* stream) {
+  if (!marginals || !n_nodes || !parent || !token || !depth || !score || !anc_bits)
+    return TSV_EINVAL;
+  if ((topk_idx == nullptr) != (topk_p == nullptr)) return TSV_EINVAL;
+  if (B < 1 || gamma < 1 || V < 1 || top_k < 1 || N_max < 1) return TSV_EINVAL;
+  if (top_k > V || n_budget < 0 || n_budget > N_max) return TSV_EINVAL;
+  if (!build_sizes_ok(B, gamma, V, top_k, N_max)) return TSV_EUNSUPPORTED;
+  if (cost) {
+    if (!prefix_len) return TSV_EINVAL;
+    if (!isfinite(cost->a) || !isfinite(cost->c_d) || !(cost->a + cost->c_d > 0.0) ||
+        !finite_nonneg(cost->b) || !finite_nonneg(cost->c) || !finite_nonneg(cost->e))
+      return TSV_EINVAL;
+  }
+  const BuildLayout L = build_layout(B, gamma, V, top_k);
+  if (!ws || ws_bytes < L.bytes || !aligned_to(ws, kAlign)) return TSV_EWORKSPACE;
+  char* w = static_cast<char*>(ws);
+  int* tk_idx = topk_idx ? topk_idx : reinterpret_cast<int*>(w + L.off_idx);
+  float* tk_p = topk_p ? topk_p : reinterpret_cast<float*>(w + L.off_p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_topk(marginals, L.plan, reinterpret_cast<uint64_t*>(w + L.off_seg),
+                             tk_idx, tk_p, s);
+  if (e != hipSuccess) return TSV_EHIP;
+  TreeArgs a;
+  a.tk_idx = tk_idx;
+  a.tk_p = tk_p;
+  a.B = B;
+  a.gamma = gamma;
+  a.k = top_k;
+  a.N_max = N_max;
+  a.cap = n_budget;
+  a.adaptive = cost ? 1 : 0;
+  a.cost = cost ? *cost : tsv_cost{0, 0, 0, 0, 0};
+  a.prefix_len = prefix_len;
+  a.n_nodes = n_nodes;
+  a.parent = parent;
+  a.token = token;
+  a.depth = depth;
+  a.score = score;
+  a.anc_bits = anc_bits;
+  return launch_status(launch_best_first(a, s));
+}
+
+int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const void* k_tree, const void* v_tree, long kv_row_stride,
+                     const int* prefix_len, const int* n_nodes,
+                     const unsigned* anc_bits, int B, int N_max, int L_cap,
+                     int Hq, int Hkv, int d_qk, int d_v, int dtype,
+                     float sm_scale, void* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !k_tree || !v_tree || !prefix_len || !n_nodes ||
+      !anc_bits || !out)
+    return TSV_EINVAL;
+  if (!dtype_ok(dtype) || !isfinite(sm_scale)) return TSV_EINVAL;
+  if (B < 1 || N_max < 1 || L_cap < 0 || Hq < 1 || Hkv < 1 || d_qk < 1 || d_v < 1)
+    return TSV_EINVAL;
+  if (Hq % Hkv != 0) return TSV_EINVAL;
+  const long widest = static_cast<long>(Hkv) * (d_qk > d_v ? d_qk : d_v);
+  if (kv_row_stride < widest) return TSV_EINVAL;
+  if (!attn_sizes_ok(B, N_max, L_cap, Hq, Hkv, d_qk, d_v)) return TSV_EUNSUPPORTED;
+  const int es = esize(dtype);
+  const bool vec = aligned_to(q, 16) && aligned_to(k_cache, 16) && aligned_to(v_cache, 16) &&
+                   aligned_to(k_tree, 16) && aligned_to(v_tree, 16) && aligned_to(out, 16) &&
+                   (kv_row_stride * es) % 16 == 0;
+  AttnShape sh{B, N_max, L_cap, Hq, Hkv, d_qk, d_v, dtype};
+  const AttnPlan P = attn_plan(sh, vec);
+  if (!ws || ws_bytes < P.bytes || !aligned_to(ws, kAlign)) return TSV_EWORKSPACE;
+  char* w = static_cast<char*>(ws);
+  AttnArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.kt = k_tree;
+  a.vt = v_tree;
+  a.stride = kv_row_stride;
+  a.prefix_len = prefix_len;
+  a.n_nodes = n_nodes;
+  a.anc = anc_bits;
+  a.B = B;
+  a.N_max = N_max;
+  a.L_cap = L_cap;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.d_qk = d_qk;
+  a.d_v = d_v;
+  a.W = (N_max + 31) / 32;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  a.info = reinterpret_cast<int*>(w + P.off_info);
+  a.desc = reinterpret_cast<int4*>(w + P.off_desc);
+  a.part_ml = reinterpret_cast<float*>(w + P.off_ml);
+  a.part_acc = reinterpret_cast<float*>(w + P.off_acc);
+  a.RB = P.RB;
+  a.KT = P.KT;
+  a.items_max = P.items_max;
+  a.target_items = P.target_items;
+  a.min_chunk = P.min_chunk;
+  return launch_status(launch_attention(a, P.path, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int accept_walk(const void* target_logits, int dtype, int B, int N_max, int V,
+                int gamma, const int* n_nodes, const int* parent,
+                const int* token, int* accept_len, int* accept_nodes,
+                int* out_tokens, void* ws, size_t ws_bytes, void* stream) {
+  if (!target_logits || !n_nodes || !parent || !token || !accept_len || !accept_nodes ||
+      !out_tokens)
+    return TSV_EINVAL;
+  if (!dtype_ok(dtype) || B < 1 || N_max < 1 || V < 1 || gamma < 1) return TSV_EINVAL;
+  if (N_max > kMaxNodes || gamma > kMaxGamma) return TSV_EUNSUPPORTED;
+  if (static_cast<long long>(B) * (N_max + 1) > (1LL << 26)) return TSV_EUNSUPPORTED;
+  const int rows = B * (N_max + 1);
+  ArgmaxPlan p = argmax_plan(rows, V, dtype);
+  if (!aligned_to(target_logits, 16)) p.vec = false;
+  if (!ws || ws_bytes < walk_bytes(B, N_max, V, dtype) || !aligned_to(ws, kAlign))
+    return TSV_EWORKSPACE;
+  return launch_status(launch_accept_walk(target_logits, dtype, B, N_max, V, gamma, n_nodes,
+                                          parent, token, accept_len, accept_nodes, out_tokens,
+                                          static_cast<uint64_t*>(ws), p,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int commit_path(void* k_cache, void* v_cache, int* prefix_len,
+                const void* k_tree, const void* v_tree, long kv_row_stride,
+                const int* accept_len, const int* accept_nodes, int B,
+                int N_max, int L_cap, int Hkv, int d_k, int d_v, int gamma,
+                int dtype, int* status, void* stream) {
+  if (!k_cache || !prefix_len || !k_tree || !accept_len || !accept_nodes || !status)
+    return TSV_EINVAL;
+  if ((v_cache == nullptr) != (v_tree == nullptr)) return TSV_EINVAL;
+  if (!dtype_ok(dtype) || B < 1 || N_max < 1 || L_cap < 0 || Hkv < 1 || d_k < 1 || gamma < 1)
+    return TSV_EINVAL;
+  if (v_cache && d_v < 1) return TSV_EINVAL;
+  if (gamma > kMaxGamma) return TSV_EUNSUPPORTED;
+  const long vk = static_cast<long>(Hkv) * d_k;
+  const long vv = v_cache ? static_cast<long>(Hkv) * d_v : 0;
+  if (kv_row_stride < vk || kv_row_stride < vv) return TSV_EINVAL;
+  const int es = esize(dtype);
+  return launch_status(launch_commit(k_cache, v_cache, prefix_len, k_tree, v_tree,
+                                     static_cast<size_t>(kv_row_stride) * es, accept_len,
+                                     accept_nodes, B, N_max, L_cap, static_cast<size_t>(vk) * es,
+                                     static_cast<size_t>(vv) * es, gamma, status,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,657 @@
+// tree_verify_attn: branch-aware tree attention over a shared prefix.
+//
+// [review] Difficulty 1 (paper section 3.1) and "How it works", step 3: a tree
+// node attends to the persistent prefix and to its own ancestors in the
+// scratch pad, never to another branch.  Section 6 as quoted: with dense
+// attention the tree is a mask over the shared KV -- here, per-node ancestor
+// bitsets applied to the scratch keys of the last tiles.
+//
+// Work decomposition (all on the device, no host round-trip):
+//   * a query row is (node, query head); the rows of one request that share
+//     a KV head form "units" of RB rows;
+//   * each unit's keys are the virtual sequence prefix[0, l_b) ++ scratch[0,
+//     n_b), split into chunks; one work item = (request, KV head, row block,
+//     chunk).  A one-workgroup planner sizes the chunk from the total work so
+//     that about `target_items` items exist, and writes the item list;
+//   * an item streams its keys through LDS in tiles, keeps an online softmax
+//     per row in fp32 and writes either the final row (single chunk) or a
+//     partial (max, sum, accumulator) for the combine kernel.
+// Grouped/latent bf16 shapes use MFMA (v_mfma_f32_16x16x32_bf16): the score
+// tile is computed transposed (keys x rows) so that its output layout is
+// directly the B operand of the value product, and the value tile is stored
+// transposed in LDS (key pairs packed per dword) for the A operand.
+// Other shapes and fp32 use a plain VALU kernel.
+
+#include "tsv_device.hpp"
+#include "tsv_internal.hpp"
+
+namespace tsv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kValuRows = 16;
+constexpr int kValuKeys = 16;
+constexpr int kValuMaxD = 576;
+
+__device__ __forceinline__ bool anc_bit(const uint32_t* w, int j) {
+  const uint32_t word = (j < 32) ? w[0] : (j < 64) ? w[1] : (j < 96) ? w[2] : w[3];
+  return (word >> (j & 31)) & 1u;
+}
+
+// ---------------------------------------------------------------- planner
+__global__ __launch_bounds__(256) void attn_plan_kernel(AttnArgs a) {
+  __shared__ long long s_red[256];
+  __shared__ int s_scan[256];
+  __shared__ int s_chunk;
+  const int t = threadIdx.x;
+  const int per = (a.B + 255) / 256;
+  const int b0 = min(a.B, t * per), b1 = min(a.B, b0 + per);
+  long long w = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int n = clampi(a.n_nodes[b], 0, a.N_max);
+    const int l = clampi(a.prefix_len[b], 0, a.L_cap);
+    if (n > 0) {
+      const int rb = (n * a.G + a.RB - 1) / a.RB;
+      w += static_cast<long long>(a.Hkv) * rb * (l + n);
+    }
+  }
+  s_red[t] = w;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) s_red[t] += s_red[t + s];
+    __syncthreads();
+  }
+  if (t == 0) {
+    long long c = (s_red[0] + a.target_items - 1) / a.target_items;
+    if (c < a.min_chunk) c = a.min_chunk;
+    c = (c + a.KT - 1) / a.KT * a.KT;
+    if (c > (1LL << 30)) c = 1LL << 30;
+    s_chunk = static_cast<int>(c);
+  }
+  __syncthreads();
+  const int chunk = s_chunk;
+  int items = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int n = clampi(a.n_nodes[b], 0, a.N_max);
+    const int l = clampi(a.prefix_len[b], 0, a.L_cap);
+    if (n > 0) {
+      const int rb = (n * a.G + a.RB - 1) / a.RB;
+      items += a.Hkv * rb * ((l + n + chunk - 1) / chunk);
+    }
+  }
+  s_scan[t] = items;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = t >= off ? s_scan[t - off] : 0;
+    __syncthreads();
+    s_scan[t] += v;
+    __syncthreads();
+  }
+  int base = s_scan[t] - items;
+  for (int b = b0; b < b1; ++b) {
+    const int n = clampi(a.n_nodes[b], 0, a.N_max);
+    const int l = clampi(a.prefix_len[b], 0, a.L_cap);
+    const int rb = n > 0 ? (n * a.G + a.RB - 1) / a.RB : 0;
+    const int splits = n > 0 ? (l + n + chunk - 1) / chunk : 0;
+    a.info[4 * b + 0] = base;
+    a.info[4 * b + 1] = splits;
+    a.info[4 * b + 2] = rb;
+    a.info[4 * b + 3] = l;
+    base += a.Hkv * rb * splits;
+  }
+  if (t == 255) {
+    a.info[4 * a.B + 0] = chunk;
+    a.info[4 * a.B + 1] = min(s_scan[255], a.items_max);
+  }
+  __syncthreads();
+  for (int b = 0; b < a.B; ++b) {
+    const int ib = a.info[4 * b + 0], splits = a.info[4 * b + 1], rb = a.info[4 * b + 2];
+    const int cnt = a.Hkv * rb * splits;
+    for (int i = t; i < cnt; i += 256) {
+      if (ib + i >= a.items_max) break;
+      const int split = i % splits;
+      const int u = i / splits;
+      a.desc[ib + i] = make_int4(b, u / rb, u % rb, split);
+    }
+  }
+}
+
+struct ItemCtx {
+  int b, kvh, rowb, split, splits, l_b, n_b, keys_b, k_beg, k_end, rows_b;
+};
+
+__device__ __forceinline__ bool load_item(const AttnArgs& a, ItemCtx& c) {
+  const int item = blockIdx.x;
+  if (item >= a.info[4 * a.B + 1]) return false;
+  const int4 d = a.desc[item];
+  c.b = d.x;
+  c.kvh = d.y;
+  c.rowb = d.z;
+  c.split = d.w;
+  const int chunk = a.info[4 * a.B];
+  c.splits = a.info[4 * c.b + 1];
+  c.l_b = a.info[4 * c.b + 3];
+  c.n_b = clampi(a.n_nodes[c.b], 0, a.N_max);
+  c.keys_b = c.l_b + c.n_b;
+  c.k_beg = c.split * chunk;
+  c.k_end = min(c.keys_b, c.k_beg + chunk);
+  c.rows_b = c.n_b * a.G;
+  return true;
+}
+
+// element offset of key `key` (virtual index) of request b, or -1 past the end
+__device__ __forceinline__ long key_row(const AttnArgs& a, const ItemCtx& c, int key, bool* tree) {
+  if (key < c.l_b) {
+    *tree = false;
+    return (static_cast<long>(c.b) * a.L_cap + key) * a.stride;
+  }
+  *tree = true;
+  return (static_cast<long>(c.b) * a.N_max + (key - c.l_b)) * a.stride;
+}
+
+// --------------------------------------------------------------- MFMA path
+template <int DQK, int DV, int RG, int KT, bool PREFETCH>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int RB = 64 * RG;        // 4 waves x RG groups of 16 rows
+  constexpr int KSTR = DQK + 8;      // bf16 per K-tile row (padding vs bank conflicts)
+  constexpr int VSTR = KT / 2 + 2;   // dwords per transposed value row
+  constexpr int NC = DQK / 32;       // k-steps of the score product
+  constexpr int NKB = KT / 16;       // 16-key blocks per tile
+  constexpr int NDB = DV / 16;       // 16-wide value blocks
+  constexpr int NST = KT / 32;       // 32-key steps of the value product
+  constexpr int KCH = DQK / 8;       // 16-byte chunks per key row
+  constexpr int VCH = DV / 8;        // 16-byte chunks per value row
+  constexpr int KLD = KT * KCH / 256;         // K chunks per thread
+  constexpr int VLD = (KT / 2) * VCH / 256;   // value key-pair tasks per thread
+  static_assert(KT * KCH % 256 == 0 && (KT / 2) * VCH % 256 == 0, "tile split");
+  __shared__ __align__(16) uint16_t sK[KT * KSTR];
+  __shared__ __align__(16) uint32_t sV[DV * VSTR];
+
+  ItemCtx c;
+  if (!load_item(a, c)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
+  const uint16_t* kt = static_cast<const uint16_t*>(a.kt);
+  const uint16_t* vt = static_cast<const uint16_t*>(a.vt);
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const float scale = a.scale_log2;
+
+  bf16x8 qf[RG][NC];
+  uint32_t anc[RG][4];
+  bool act[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int r_first = c.rowb * RB + wave * RG * 16 + rg * 16;
+    act[rg] = r_first < c.rows_b;
+    const int r = r_first + lr;
+    const bool rv = r < c.rows_b;
+    const int node = rv ? r / a.G : 0;
+    const int h = c.kvh * a.G + (rv ? r % a.G : 0);
+    const uint16_t* src = qp + ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * DQK;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      if (rv) qf[rg][k] = *reinterpret_cast<const bf16x8*>(src + 32 * k + 8 * lq);
+      else qf[rg][k] = bf16x8{};
+    }
+    const unsigned* ab = a.anc + (static_cast<size_t>(c.b) * a.N_max + node) * a.W;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) anc[rg][w] = (rv && w < a.W) ? ab[w] : 0u;
+  }
+
+  float m_run[RG], l_run[RG];
+  f32x4 o[RG][NDB];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    m_run[rg] = -INFINITY;
+    l_run[rg] = 0.f;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) o[rg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint4 rk[KLD];
+  uint4 rv0[VLD], rv1[VLD];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int ci = tid + 256 * i;
+      const int key = ci / KCH, ch = ci % KCH;
+      const int kk = t0 + key;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kk < c.k_end) {
+        bool tr;
+        const long off = key_row(a, c, kk, &tr) + static_cast<long>(c.kvh) * DQK + 8 * ch;
+        v = *reinterpret_cast<const uint4*>((tr ? kt : kc) + off);
+      }
+      rk[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int vi = tid + 256 * i;
+      const int p = vi / VCH, ch = vi % VCH;
+      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+      const int k0 = t0 + 2 * p;
+      if (k0 < c.k_end) {
+        bool tr;
+        const long off = key_row(a, c, k0, &tr) + static_cast<long>(c.kvh) * DV + 8 * ch;
+        x0 = *reinterpret_cast<const uint4*>((tr ? vt : vc) + off);
+      }
+      if (k0 + 1 < c.k_end) {
+        bool tr;
+        const long off = key_row(a, c, k0 + 1, &tr) + static_cast<long>(c.kvh) * DV + 8 * ch;
+        x1 = *reinterpret_cast<const uint4*>((tr ? vt : vc) + off);
+      }
+      rv0[i] = x0;
+      rv1[i] = x1;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int ci = tid + 256 * i;
+      const int key = ci / KCH, ch = ci % KCH;
+      *reinterpret_cast<uint4*>(&sK[key * KSTR + 8 * ch]) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int vi = tid + 256 * i;
+      const int p = vi / VCH, ch = vi % VCH;
+      const uint32_t w0[4] = {rv0[i].x, rv0[i].y, rv0[i].z, rv0[i].w};
+      const uint32_t w1[4] = {rv1[i].x, rv1[i].y, rv1[i].z, rv1[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sV[(8 * ch + 2 * j) * VSTR + p] = (w0[j] & 0xFFFFu) | (w1[j] << 16);
+        sV[(8 * ch + 2 * j + 1) * VSTR + p] = (w0[j] >> 16) | (w1[j] & 0xFFFF0000u);
+      }
+    }
+  };
+
+  if (PREFETCH && c.k_beg < c.k_end) fetch(c.k_beg);
+  for (int t0 = c.k_beg; t0 < c.k_end; t0 += KT) {
+    __syncthreads();  // the previous tile is no longer read
+    if (!PREFETCH) fetch(t0);
+    stash();
+    __syncthreads();
+    if (PREFETCH && t0 + KT < c.k_end) fetch(t0 + KT);
+
+    // scores, transposed: lane holds S^T[key = kb*16 + 4*lq + i][row = lr]
+    f32x4 s[RG][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + lr) * KSTR + 32 * k + 8 * lq]);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          if (act[rg]) s[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][k], s[rg][kb], 0, 0, 0);
+      }
+    }
+
+    const bool full = (t0 + KT <= c.k_end) && (t0 + KT <= c.l_b);
+    bf16x8 pf[RG][NST];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      if (!act[rg]) continue;
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = t0 + kb * 16 + 4 * lq + i;
+            const bool ok = key < c.k_end && (key < c.l_b || anc_bit(anc[rg], key - c.l_b));
+            if (!ok) s[rg][kb][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[rg][kb][0], s[rg][kb][1]), fmaxf(s[rg][kb][2], s[rg][kb][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m_run[rg], mx * scale);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(m_run[rg] - muse);
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(fmaf(s[rg][kb][i], scale, -muse));
+          lsum += p;
+          pf[rg][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
+        }
+      }
+      l_run[rg] = l_run[rg] * alpha + lsum;
+      m_run[rg] = mnew;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[rg][d] *= alpha;
+      }
+    }
+
+    // values: O^T[dv][row] += V^T[dv][keys] * P^T[keys][row]
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const uint32_t* vrow = &sV[(d * 16 + lr) * VSTR + 16 * st];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 2 * lq);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8 + 2 * lq);
+        union {
+          uint4 u;
+          bf16x8 v;
+        } vf;
+        vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          if (act[rg]) o[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rg][st], o[rg][d], 0, 0, 0);
+      }
+    }
+  }
+
+  // lane holds O^T[dv = d*16 + 4*lq + i][row = lr]
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    if (!act[rg]) continue;
+    float lt = l_run[rg];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int r_loc = wave * RG * 16 + rg * 16 + lr;
+    const int r = c.rowb * RB + r_loc;
+    if (r >= c.rows_b) continue;
+    if (c.splits == 1) {
+      const int node = r / a.G, h = c.kvh * a.G + r % a.G;
+      const size_t orow = (static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h;
+      uint16_t* op = static_cast<uint16_t*>(a.out) + orow * DV;
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        union {
+          uint2 u;
+          __bf16 h4[4];
+        } pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(o[rg][d][i] * inv);
+        *reinterpret_cast<uint2*>(op + d * 16 + 4 * lq) = pk.u;
+      }
+      if (lq == 0 && a.lse) a.lse[orow] = (m_run[rg] + log2f(lt)) * kLn2;
+    } else {
+      const size_t prow = static_cast<size_t>(blockIdx.x) * RB + r_loc;
+      float* pa = a.part_acc + prow * DV;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+        *reinterpret_cast<float4*>(pa + d * 16 + 4 * lq) =
+            make_float4(o[rg][d][0], o[rg][d][1], o[rg][d][2], o[rg][d][3]);
+      if (lq == 0) {
+        a.part_ml[prow * 2 + 0] = m_run[rg];
+        a.part_ml[prow * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- VALU path
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p);
+template <>
+__device__ __forceinline__ float ld_elem<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T>
+__device__ __forceinline__ void st_elem(T* p, float v);
+template <>
+__device__ __forceinline__ void st_elem<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void st_elem<uint16_t>(uint16_t* p, float v) {
+  __bf16 h = static_cast<__bf16>(v);
+  *p = *reinterpret_cast<uint16_t*>(&h);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+  constexpr int R = kValuRows, K = kValuKeys, DM = kValuMaxD;
+  __shared__ float sQ[R * DM];
+  __shared__ float sK[K * (DM + 1)];
+  __shared__ float sV[K * DM];
+  __shared__ float sP[R * (K + 1)];
+  __shared__ uint32_t sA[R][4];
+
+  ItemCtx c;
+  if (!load_item(a, c)) return;
+  const int DQ = a.d_qk, DVv = a.d_v, KS = DQ + 1;
+  const int tid = threadIdx.x;
+  const int row = tid / K, col = tid % K;
+  const T* qp = static_cast<const T*>(a.q);
+  const T* kc = static_cast<const T*>(a.kc);
+  const T* vc = static_cast<const T*>(a.vc);
+  const T* kt = static_cast<const T*>(a.kt);
+  const T* vt = static_cast<const T*>(a.vt);
+
+  for (int e = tid; e < R * DQ; e += 256) {
+    const int r = e / DQ, x = e % DQ;
+    const int rg = c.rowb * R + r;
+    float v = 0.f;
+    if (rg < c.rows_b) {
+      const int node = rg / a.G, h = c.kvh * a.G + rg % a.G;
+      v = ld_elem<T>(qp + ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * DQ + x);
+    }
+    sQ[r * DQ + x] = v;
+  }
+  if (tid < R * 4) {
+    const int r = tid / 4, w = tid % 4;
+    const int rg = c.rowb * R + r;
+    uint32_t v = 0;
+    if (rg < c.rows_b && w < a.W)
+      v = a.anc[(static_cast<size_t>(c.b) * a.N_max + rg / a.G) * a.W + w];
+    sA[r][w] = v;
+  }
+  const bool row_ok = c.rowb * R + row < c.rows_b;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[(DM + K - 1) / K];
+#pragma unroll
+  for (int j = 0; j < (DM + K - 1) / K; ++j) acc[j] = 0.f;
+
+  for (int t0 = c.k_beg; t0 < c.k_end; t0 += K) {
+    __syncthreads();
+    for (int e = tid; e < K * DQ; e += 256) {
+      const int key = e / DQ, x = e % DQ, kk = t0 + key;
+      float v = 0.f;
+      if (kk < c.k_end) {
+        bool tr;
+        const long off = key_row(a, c, kk, &tr) + static_cast<long>(c.kvh) * DQ + x;
+        v = ld_elem<T>((tr ? kt : kc) + off);
+      }
+      sK[key * KS + x] = v;
+    }
+    for (int e = tid; e < K * DVv; e += 256) {
+      const int key = e / DVv, x = e % DVv, kk = t0 + key;
+      float v = 0.f;
+      if (kk < c.k_end) {
+        bool tr;
+        const long off = key_row(a, c, kk, &tr) + static_cast<long>(c.kvh) * DVv + x;
+        v = ld_elem<T>((tr ? vt : vc) + off);
+      }
+      sV[key * DVv + x] = v;
+    }
+    __syncthreads();
+    float s = 0.f;
+    for (int x = 0; x < DQ; ++x) s = fmaf(sQ[row * DQ + x], sK[col * KS + x], s);
+    const int key = t0 + col;
+    const bool ok = row_ok && key < c.k_end && (key < c.l_b || anc_bit(sA[row], key - c.l_b));
+    s = ok ? s * a.scale_log2 : -INFINITY;
+    float mx = s;
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, K));
+    const float mnew = fmaxf(m_run, mx);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2f(m_run - muse);
+    const float p = exp2f(s - muse);
+    float ps = p;
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) ps += __shfl_xor(ps, m, K);
+    l_run = l_run * alpha + ps;
+    m_run = mnew;
+    sP[row * (K + 1) + col] = p;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < (DM + K - 1) / K; ++j) {
+      const int dv = col + K * j;
+      if (dv < DVv) {
+        float v = acc[j] * alpha;
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) v = fmaf(sP[row * (K + 1) + kk], sV[kk * DVv + dv], v);
+        acc[j] = v;
+      }
+    }
+  }
+
+  if (!row_ok) return;
+  const int r_loc = row;
+  const int rg = c.rowb * R + r_loc;
+  if (c.splits == 1) {
+    const int node = rg / a.G, h = c.kvh * a.G + rg % a.G;
+    const size_t orow = (static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h;
+    T* op = static_cast<T*>(a.out) + orow * DVv;
+    const float inv = 1.0f / l_run;
+#pragma unroll
+    for (int j = 0; j < (DM + K - 1) / K; ++j) {
+      const int dv = col + K * j;
+      if (dv < DVv) st_elem<T>(op + dv, acc[j] * inv);
+    }
+    if (col == 0 && a.lse) a.lse[orow] = (m_run + log2f(l_run)) * kLn2;
+  } else {
+    const size_t prow = static_cast<size_t>(blockIdx.x) * R + r_loc;
+#pragma unroll
+    for (int j = 0; j < (DM + K - 1) / K; ++j) {
+      const int dv = col + K * j;
+      if (dv < DVv) a.part_acc[prow * DVv + dv] = acc[j];
+    }
+    if (col == 0) {
+      a.part_ml[prow * 2 + 0] = m_run;
+      a.part_ml[prow * 2 + 1] = l_run;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- combine
+template <typename T>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long row = static_cast<long>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<long>(a.B) * a.N_max * a.Hq) return;
+  const int h = static_cast<int>(row % a.Hq);
+  const long bi = row / a.Hq;
+  const int i = static_cast<int>(bi % a.N_max);
+  const int b = static_cast<int>(bi / a.N_max);
+  const int n_b = clampi(a.n_nodes[b], 0, a.N_max);
+  if (i >= n_b) return;
+  const int splits = a.info[4 * b + 1];
+  if (splits <= 1) return;  // written by the item itself
+  const int rbs = a.info[4 * b + 2];
+  const int kvh = h / a.G;
+  const int r = i * a.G + h % a.G;
+  const int rowb = r / a.RB, r_loc = r % a.RB;
+  const long item0 = a.info[4 * b] + static_cast<long>(kvh * rbs + rowb) * splits;
+  if (item0 + splits > a.items_max) return;
+  auto ml = [&](int s, int f) { return a.part_ml[((item0 + s) * a.RB + r_loc) * 2 + f]; };
+  float M = -INFINITY;
+  for (int s = lane; s < splits; s += 64) M = fmaxf(M, ml(s, 0));
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+  float L = 0.f;
+  for (int s = lane; s < splits; s += 64) {
+    const float ms = ml(s, 0);
+    L += ms == -INFINITY ? 0.f : exp2f(ms - M) * ml(s, 1);
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) L += __shfl_xor(L, m);
+  const float inv = 1.0f / L;
+  const size_t orow = (static_cast<size_t>(b) * a.N_max + i) * a.Hq + h;
+  T* op = static_cast<T*>(a.out) + orow * a.d_v;
+  for (int dv = lane; dv < a.d_v; dv += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float ms = ml(s, 0);
+      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      acc = fmaf(w, a.part_acc[((item0 + s) * a.RB + r_loc) * a.d_v + dv], acc);
+    }
+    st_elem<T>(op + dv, acc * inv);
+  }
+  if (lane == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * kLn2;
+}
+
+}  // namespace
+
+AttnPlan attn_plan(const AttnShape& sh, bool aligned) {
+  AttnPlan p;
+  const bool bf = sh.dtype == TSV_BF16;
+  if (bf && aligned && sh.d_qk == 128 && sh.d_v == 128) {
+    p.path = kPathMfmaGqa;
+    p.RB = 128;
+    p.KT = 64;
+    p.min_chunk = 512;
+    p.target_items = 512;
+  } else if (bf && aligned && sh.d_qk == 576 && sh.d_v == 512) {
+    p.path = kPathMfmaLatent;
+    p.RB = 64;
+    p.KT = 32;
+    p.min_chunk = 256;
+    p.target_items = 1024;
+  } else {
+    p.path = kPathValu;
+    p.RB = kValuRows;
+    p.KT = kValuKeys;
+    p.min_chunk = 256;
+    p.target_items = 1024;
+  }
+  const int G = sh.Hq / sh.Hkv;
+  const long units = static_cast<long>(sh.B) * sh.Hkv * ((static_cast<long>(sh.N_max) * G + p.RB - 1) / p.RB);
+  const long items = p.target_items + units;
+  p.items_max = static_cast<int>(items);
+  size_t off = 0;
+  p.off_info = off;
+  off = align_up(off + (4 * static_cast<size_t>(sh.B) + 2) * sizeof(int));
+  p.off_desc = off;
+  off = align_up(off + static_cast<size_t>(items) * sizeof(int4));
+  p.off_ml = off;
+  off = align_up(off + static_cast<size_t>(items) * p.RB * 2 * sizeof(float));
+  p.off_acc = off;
+  off = align_up(off + static_cast<size_t>(items) * p.RB * sh.d_v * sizeof(float));
+  p.bytes = off;
+  return p;
+}
+
+hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype, hipStream_t s) {
+  attn_plan_kernel<<<dim3(1), dim3(256), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid(a.items_max), block(256);
+  if (path == kPathMfmaGqa) {
+    attn_mfma_kernel<128, 128, 2, 64, true><<<grid, block, 0, s>>>(a);
+  } else if (path == kPathMfmaLatent) {
+    attn_mfma_kernel<576, 512, 1, 32, false><<<grid, block, 0, s>>>(a);
+  } else if (dtype == TSV_F32) {
+    attn_valu_kernel<float><<<grid, block, 0, s>>>(a);
+  } else {
+    attn_valu_kernel<uint16_t><<<grid, block, 0, s>>>(a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long rows = static_cast<long>(a.B) * a.N_max * a.Hq;
+  dim3 g2(static_cast<unsigned>((rows + 3) / 4));
+  if (dtype == TSV_F32)
+    attn_combine_kernel<float><<<g2, block, 0, s>>>(a);
+  else
+    attn_combine_kernel<uint16_t><<<g2, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace tsv

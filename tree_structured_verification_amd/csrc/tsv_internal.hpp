@@ -1,0 +1,106 @@
+// Host-side interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tsv.h"
+
+namespace tsv {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Waves a streaming scan aims to keep in flight (about 16 per CU on a
+// 256-CU part); fixed so that results never depend on the device.
+constexpr int kScanWaves = 4096;
+
+// ---- build_tree --------------------------------------------------------
+struct TopkPlan {
+  int rows, V, k, slots, nseg, seg_len;
+  bool vec;
+};
+TopkPlan topk_plan(int rows, int V, int k);
+size_t topk_ws_bytes(const TopkPlan& p);  // segment lists only
+hipError_t launch_topk(const float* x, const TopkPlan& p, uint64_t* seg_keys,
+                       int* out_idx, float* out_p, hipStream_t s);
+
+struct TreeArgs {
+  const int* tk_idx;
+  const float* tk_p;
+  int B, gamma, k, N_max, cap, adaptive;
+  tsv_cost cost;
+  const int* prefix_len;
+  int* n_nodes;
+  int* parent;
+  int* token;
+  int* depth;
+  float* score;
+  unsigned* anc_bits;
+};
+hipError_t launch_best_first(const TreeArgs& a, hipStream_t s);
+
+// ---- accept_walk -------------------------------------------------------
+struct ArgmaxPlan {
+  int rows, V, nseg, seg_len;
+  bool vec;
+};
+ArgmaxPlan argmax_plan(int rows, int V, int dtype);
+hipError_t launch_accept_walk(const void* logits, int dtype, int B, int N_max,
+                              int V, int gamma, const int* n_nodes,
+                              const int* parent, const int* token,
+                              int* accept_len, int* accept_nodes,
+                              int* out_tokens, uint64_t* seg_best,
+                              const ArgmaxPlan& p, hipStream_t s);
+
+// ---- commit_path -------------------------------------------------------
+hipError_t launch_commit(void* k_cache, void* v_cache, int* prefix_len,
+                         const void* k_tree, const void* v_tree,
+                         size_t row_bytes, const int* accept_len,
+                         const int* accept_nodes, int B, int N_max, int L_cap,
+                         size_t k_bytes, size_t v_bytes, int gamma,
+                         int* status, hipStream_t s);
+
+// ---- tree_verify_attn --------------------------------------------------
+enum AttnPath { kPathValu = 0, kPathMfmaGqa = 1, kPathMfmaLatent = 2 };
+
+struct AttnShape {
+  int B, N_max, L_cap, Hq, Hkv, d_qk, d_v, dtype;
+};
+struct AttnPlan {
+  AttnPath path;
+  int RB;            // query rows (node x head) per work item
+  int KT;            // keys per tile
+  int min_chunk;     // smallest split of the key range
+  int target_items;  // work items aimed for
+  int items_max;     // bound on work items for any prefix lengths / node counts
+  size_t off_info, off_desc, off_ml, off_acc, bytes;
+};
+// `aligned` says whether pointers and strides allow 16-byte vector access.
+AttnPlan attn_plan(const AttnShape& sh, bool aligned);
+
+struct AttnArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const void* kt;
+  const void* vt;
+  long stride;
+  const int* prefix_len;
+  const int* n_nodes;
+  const unsigned* anc;
+  int B, N_max, L_cap, Hq, Hkv, G, d_qk, d_v, W;
+  float scale_log2;
+  void* out;
+  float* lse;
+  int* info;        // [B][4] item_base, splits, rowblocks, prefix; then chunk, total
+  int4* desc;       // [items_max] request, kv head, row block, split
+  float* part_ml;   // [items_max][RB][2]
+  float* part_acc;  // [items_max][RB][d_v]
+  int RB, KT, items_max, target_items, min_chunk;
+};
+hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype,
+                            hipStream_t s);
+
+}  // namespace tsv
