@@ -101,7 +101,11 @@ def test_sibling_isolation_and_determinism():
     scale = 0.088
     o1, l1, _, _ = _run(q, kc, vc, kt, vt, pl, trees, Hkv, d, scale)
     o2, l2, _, _ = _run(q, kc, vc, kt, vt, pl, trees, Hkv, d, scale)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    for b in range(B):      # rows past n_b are never written
+        n = trees[b].n
+        assert torch.equal(bits(o1[b, :n]), bits(o2[b, :n]))
+        assert torch.equal(bits(l1[b, :n]), bits(l2[b, :n]))
     for b in range(B):
         for i in range(trees[b].n):
             anc = {j for j in range(N_max) if trees[b].anc_bits[i, j // 32] >> (j % 32) & 1}
@@ -112,7 +116,8 @@ def test_sibling_isolation_and_determinism():
             kt2[b, others] = (kt2[b, others].float() * -3.0 + 1.0).to(kt.dtype)
             vt2[b, others] = (vt2[b, others].float() + 5.0).to(vt.dtype)
             o3, l3, _, _ = _run(q, kc, vc, kt2, vt2, pl, trees, Hkv, d, scale)
-            assert torch.equal(o3[b, i], o1[b, i]) and torch.equal(l3[b, i], l1[b, i])
+            assert torch.equal(bits(o3[b, i]), bits(o1[b, i]))
+            assert torch.equal(bits(l3[b, i]), bits(l1[b, i]))
             if i == 0 and b == 0:
                 # and an ancestor perturbation does change it
                 kt3 = kt.clone()

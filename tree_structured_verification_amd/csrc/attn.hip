@@ -36,9 +36,19 @@ constexpr int kValuRows = 16;
 constexpr int kValuKeys = 16;
 constexpr int kValuMaxD = 576;
 
-__device__ __forceinline__ bool anc_bit(const uint32_t* w, int j) {
-  const uint32_t word = (j < 32) ? w[0] : (j < 64) ? w[1] : (j < 96) ? w[2] : w[3];
-  return (word >> (j & 31)) & 1u;
+// Whether virtual key `key` is visible to a row whose node has ancestor words
+// w[0..3]: prefix keys always, scratch keys iff their bit is set, nothing at or
+// past k_end.  Written without short-circuit operators so that it compiles to
+// selects rather than nested EXEC-masked branches.
+__device__ __forceinline__ bool key_visible(const uint32_t* w, int key, int l_b, int k_end) {
+  int j = key - l_b;
+  j = j < 0 ? 0 : (j > 127 ? 127 : j);
+  const uint32_t lo = (j < 32) ? w[0] : w[1];
+  const uint32_t hi = (j < 96) ? w[2] : w[3];
+  const uint32_t word = (j < 64) ? lo : hi;
+  const int bit = static_cast<int>((word >> (j & 31)) & 1u);
+  const int vis = static_cast<int>(key < l_b) | bit;
+  return (static_cast<int>(key < k_end) & vis) != 0;
 }
 
 // ---------------------------------------------------------------- planner
@@ -172,7 +182,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 
   ItemCtx c;
   if (!load_item(a, c)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform by construction; readfirstlane lets the compiler branch on
+  // it with scalar branches instead of EXEC-masked regions around the MFMAs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const int r_first = c.rowb * RB + wave * RG * 16 + rg * 16;
-    act[rg] = r_first < c.rows_b;
+    act[rg] = __builtin_amdgcn_readfirstlane(r_first < c.rows_b ? 1 : 0) != 0;
     const int r = r_first + lr;
     const bool rv = r < c.rows_b;
     const int node = rv ? r / a.G : 0;
@@ -304,8 +317,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = t0 + kb * 16 + 4 * lq + i;
-            const bool ok = key < c.k_end && (key < c.l_b || anc_bit(anc[rg], key - c.l_b));
-            if (!ok) s[rg][kb][i] = -INFINITY;
+            const bool ok = key_visible(anc[rg], key, c.l_b, c.k_end);
+            s[rg][kb][i] = ok ? s[rg][kb][i] : -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -485,7 +498,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     float s = 0.f;
     for (int x = 0; x < DQ; ++x) s = fmaf(sQ[row * DQ + x], sK[col * KS + x], s);
     const int key = t0 + col;
-    const bool ok = row_ok && key < c.k_end && (key < c.l_b || anc_bit(sA[row], key - c.l_b));
+    const bool ok = row_ok && key_visible(sA[row], key, c.l_b, c.k_end);
     s = ok ? s * a.scale_log2 : -INFINITY;
     float mx = s;
 #pragma unroll
