@@ -88,7 +88,7 @@ typedef struct {
  *               <= N_max.
  *   cost        HOST pointer or NULL (fixed budget)
  *   prefix_len  int32 [B], read only when cost != NULL (l in C_v)
- *   N_max       1 <= N_max <= 128; gamma <= 64; gamma * top_k <= 8192
+ *   N_max       1 <= N_max <= 128; gamma <= 64; gamma * top_k <= 4096
  * Outputs (device, written for every b and every i < N_max)
  *   n_nodes     int32 [B]
  *   parent      int32 [B][N_max]  parent node index, -1 = child of the root
@@ -141,7 +141,7 @@ int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
  *   out       [B][N_max][Hq][d_v]  rows i >= n_b are left untouched
  *   lse       fp32 [B][N_max][Hq] or NULL
  * Requirements: Hq % Hkv == 0; kv_row_stride >= Hkv*max(d_qk, d_v);
- * 1 <= d_qk, d_v <= 576.  Accumulation is fp32.
+ * 1 <= d_qk, d_v <= 576; B <= 4096.  Accumulation is fp32.
  */
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const void* k_tree, const void* v_tree, long kv_row_stride,

@@ -15,6 +15,7 @@ constexpr int kMaxGamma = 64;
 constexpr int kMaxTopk = 128;
 constexpr int kMaxTopkTable = 4096;  // gamma * top_k staged in LDS by the tree kernel
 constexpr int kMaxHeadDim = 576;
+constexpr int kMaxAttnBatch = 4096;   // request table of the attention planner lives in LDS
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -52,6 +53,7 @@ bool build_sizes_ok(int B, int gamma, int V, int top_k, int N_max) {
 
 bool attn_sizes_ok(int B, int N_max, int L_cap, int Hq, int Hkv, int d_qk, int d_v) {
   if (B < 1 || N_max < 1 || N_max > kMaxNodes || L_cap < 0 || Hq < 1 || Hkv < 1) return false;
+  if (B > kMaxAttnBatch) return false;
   if (Hq % Hkv != 0) return false;
   if (d_qk < 1 || d_v < 1 || d_qk > kMaxHeadDim || d_v > kMaxHeadDim) return false;
   if (static_cast<long long>(B) * N_max * Hq > (1LL << 30)) return false;

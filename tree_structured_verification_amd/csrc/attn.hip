@@ -35,6 +35,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kValuRows = 16;
 constexpr int kValuKeys = 16;
 constexpr int kValuMaxD = 576;
+constexpr float kLazy = 8.0f;  // lazy-rescale threshold, log2 units
 
 // Whether virtual key `key` is visible to a row whose node has ancestor words
 // w[0..3]: prefix keys always, scratch keys iff their bit is set, nothing at or
@@ -52,30 +53,41 @@ __device__ __forceinline__ bool key_visible(const uint32_t* w, int key, int l_b,
 }
 
 // ---------------------------------------------------------------- planner
-__global__ __launch_bounds__(256) void attn_plan_kernel(AttnArgs a) {
-  __shared__ long long s_red[256];
-  __shared__ int s_scan[256];
+// One workgroup of 1024 threads: per-request work, the split size, an
+// exclusive scan of the item counts (request table kept in LDS), then every
+// thread writes descriptors for its share of items, locating each item's
+// request by binary search over the scanned bases.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxB = 4096;
+
+__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
+  __shared__ int s_base[kPlanMaxB + 1];
+  __shared__ int s_splits[kPlanMaxB];
+  __shared__ int s_rb[kPlanMaxB];
+  __shared__ long long s_red[kPlanThreads / 64];
+  __shared__ int s_scan[kPlanThreads];
   __shared__ int s_chunk;
-  const int t = threadIdx.x;
-  const int per = (a.B + 255) / 256;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int per = (a.B + kPlanThreads - 1) / kPlanThreads;   // requests per thread (<= 4)
   const int b0 = min(a.B, t * per), b1 = min(a.B, b0 + per);
+
   long long w = 0;
   for (int b = b0; b < b1; ++b) {
     const int n = clampi(a.n_nodes[b], 0, a.N_max);
     const int l = clampi(a.prefix_len[b], 0, a.L_cap);
-    if (n > 0) {
-      const int rb = (n * a.G + a.RB - 1) / a.RB;
-      w += static_cast<long long>(a.Hkv) * rb * (l + n);
-    }
+    const int rb = n > 0 ? (n * a.G + a.RB - 1) / a.RB : 0;
+    s_rb[b] = rb;
+    s_splits[b] = l;   // prefix length parked here until the split size is known
+    w += static_cast<long long>(a.Hkv) * rb * (l + n);
   }
-  s_red[t] = w;
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) w += __shfl_xor(w, m);
+  if (lane == 0) s_red[wave] = w;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) s_red[t] += s_red[t + s];
-    __syncthreads();
-  }
   if (t == 0) {
-    long long c = (s_red[0] + a.target_items - 1) / a.target_items;
+    long long W = 0;
+    for (int i = 0; i < kPlanThreads / 64; ++i) W += s_red[i];
+    long long c = (W + a.target_items - 1) / a.target_items;
     if (c < a.min_chunk) c = a.min_chunk;
     c = (c + a.KT - 1) / a.KT * a.KT;
     if (c > (1LL << 30)) c = 1LL << 30;
@@ -86,15 +98,17 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(AttnArgs a) {
   int items = 0;
   for (int b = b0; b < b1; ++b) {
     const int n = clampi(a.n_nodes[b], 0, a.N_max);
-    const int l = clampi(a.prefix_len[b], 0, a.L_cap);
-    if (n > 0) {
-      const int rb = (n * a.G + a.RB - 1) / a.RB;
-      items += a.Hkv * rb * ((l + n + chunk - 1) / chunk);
-    }
+    const int l = s_splits[b];
+    const int splits = n > 0 ? (l + n + chunk - 1) / chunk : 0;
+    a.info[4 * b + 1] = splits;
+    a.info[4 * b + 2] = s_rb[b];
+    a.info[4 * b + 3] = l;
+    s_splits[b] = splits;
+    items += a.Hkv * s_rb[b] * splits;
   }
   s_scan[t] = items;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
     const int v = t >= off ? s_scan[t - off] : 0;
     __syncthreads();
     s_scan[t] += v;
@@ -102,30 +116,28 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(AttnArgs a) {
   }
   int base = s_scan[t] - items;
   for (int b = b0; b < b1; ++b) {
-    const int n = clampi(a.n_nodes[b], 0, a.N_max);
-    const int l = clampi(a.prefix_len[b], 0, a.L_cap);
-    const int rb = n > 0 ? (n * a.G + a.RB - 1) / a.RB : 0;
-    const int splits = n > 0 ? (l + n + chunk - 1) / chunk : 0;
+    s_base[b] = base;
     a.info[4 * b + 0] = base;
-    a.info[4 * b + 1] = splits;
-    a.info[4 * b + 2] = rb;
-    a.info[4 * b + 3] = l;
-    base += a.Hkv * rb * splits;
+    base += a.Hkv * s_rb[b] * s_splits[b];
   }
-  if (t == 255) {
+  const int total = min(s_scan[kPlanThreads - 1], a.items_max);
+  if (t == 0) {
+    s_base[a.B] = s_scan[kPlanThreads - 1];
     a.info[4 * a.B + 0] = chunk;
-    a.info[4 * a.B + 1] = min(s_scan[255], a.items_max);
+    a.info[4 * a.B + 1] = total;
   }
   __syncthreads();
-  for (int b = 0; b < a.B; ++b) {
-    const int ib = a.info[4 * b + 0], splits = a.info[4 * b + 1], rb = a.info[4 * b + 2];
-    const int cnt = a.Hkv * rb * splits;
-    for (int i = t; i < cnt; i += 256) {
-      if (ib + i >= a.items_max) break;
-      const int split = i % splits;
-      const int u = i / splits;
-      a.desc[ib + i] = make_int4(b, u / rb, u % rb, split);
+  for (int it = t; it < total; it += kPlanThreads) {
+    int lo = 0, hi = a.B - 1;  // last request with s_base[b] <= it
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_base[mid] <= it) lo = mid;
+      else hi = mid - 1;
     }
+    const int b = lo, i = it - s_base[b];
+    const int splits = s_splits[b], rb = s_rb[b];
+    const int split = i % splits, u = i / splits;
+    a.desc[it] = make_int4(b, u / rb, u % rb, split);
   }
 }
 
@@ -409,6 +421,335 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------ grouped-query MFMA path
+// Grouped-query heads of width 128 (the common bf16 case): 128 query rows per
+// work item (4 waves x 2 groups of 16 rows), keys streamed in tiles of KT.
+//
+// Memory pipeline: K and V tiles go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging) into a ring of STAGES
+// buffers, so STAGES-1 tiles are in flight while one is computed; waits are
+// explicit vmcnt counts and bare barriers (a workgroup fence would drain
+// every outstanding load).  Rows are stored unpadded (256 B) with 16-byte
+// chunk c of row r at slot c ^ swz(r); the swizzle is applied through the
+// global source address of each lane, since the LDS destination of these
+// loads is fixed by the lane id.  swz() makes both the K reads (16 rows, one
+// chunk) and the transposed V reads (8 rows x 2 chunks per half-wave)
+// bank-conflict free.
+//
+// The value operand of O^T = V^T P^T needs, per lane, four consecutive keys
+// of one value column: ds_read_b64_tr_b16 returns exactly that from V in its
+// natural [key][dv] layout when source lane r of a 16-lane group points at
+// V[key0 + r/4][dv0 + 4*(r%4)]: lane i then holds V[key0 + k][dv0 + i].
+
+__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with vmcnt = n (n <= 63), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+  asm volatile("" ::: "memory");
+}
+
+template <int LPT, int S>
+__device__ __forceinline__ void wait_tile(int later) {
+  // `later` tiles were issued after the one now needed (0 <= later <= S-2)
+  if (S >= 4 && later >= 2) wait_vmcnt<LPT * 2 * (S >= 4)>();
+  else if (S >= 3 && later >= 1) wait_vmcnt<LPT * (S >= 3)>();
+  else wait_vmcnt<0>();
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define TSV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define TSV_LDS4(p) ((__attribute__((address_space(3))) s16x4*)(p))
+
+// One thread's share of loading a K and V tile of KT keys (virtual key
+// indices t0 .. t0+KT-1 of one request) into an LDS stage: KT/8
+// wave-instructions, each filling 4 consecutive 256-byte rows.  Keys at or
+// past k_end re-read row k_end-1 (finite data; masked by the caller).
+// Fast path of the loader for a tile that lies entirely inside the prefix:
+// the per-thread byte offsets within a tile (off[n]) are fixed, only the
+// tile base moves.
+template <int KT>
+__device__ __forceinline__ void gqa_issue_prefix_tile(char* stage, int wave, const char* kbase,
+                                                      const char* vbase, const uint32_t* off) {
+#pragma unroll
+  for (int n = 0; n < KT / 8; ++n) {
+    const int g = n * 4 + wave;
+    const int region = g / (KT / 4);
+    const int rq = g % (KT / 4);
+    const char* src = (region == 0 ? kbase : vbase) + off[n];
+    const uint32_t dst = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>(TSV_LDS(stage + region * KT * 256 + rq * 1024)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(dst), "v"(src)
+                 : "memory", "m0");
+  }
+}
+
+template <int KT>
+__device__ __forceinline__ void gqa_issue_tile(char* stage, int t0, int wave, int lane,
+                                               int k_end, int l_b, const char* kc_b,
+                                               const char* vc_b, const char* kt_b,
+                                               const char* vt_b, long rstride) {
+#pragma unroll
+  for (int n = 0; n < KT / 8; ++n) {
+    const int g = n * 4 + wave;                  // wave-uniform
+    const int region = g / (KT / 4);             // 0 = K, 1 = V
+    const int rq = g % (KT / 4);
+    const int row = rq * 4 + (lane >> 4);
+    const int chunk = (lane & 15) ^ swz(row);
+    int key = t0 + row;
+    key = key < k_end ? key : k_end - 1;
+    const bool tr = key >= l_b;
+    const long roff = (tr ? key - l_b : key) * rstride + chunk * 16;
+    const char* src = (region == 0 ? (tr ? kt_b : kc_b) : (tr ? vt_b : vc_b)) + roff;
+    // Issued as inline asm on purpose: the compiler does not track these
+    // LDS writes, so it adds no conservative vmcnt(0) before every LDS read
+    // of the tile being computed.  Ordering is explicit: each tile is waited
+    // for with wait_tile() (vmcnt counts these loads in issue order) and a
+    // barrier before any wave reads it.
+    const uint32_t dst = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>(TSV_LDS(stage + region * KT * 256 + rq * 1024)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(dst), "v"(src)
+                 : "memory", "m0");
+  }
+}
+
+template <int KT, int STAGES>
+__global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnArgs a) {
+  constexpr int D = 128, RG = 2, RB = 128;
+  constexpr int ROWB = 256;                    // bytes per key row
+  constexpr int STAGE = 2 * KT * ROWB;         // K tile then V tile
+  constexpr int LPT = KT / 8;                  // 16-byte loads per thread per tile
+  constexpr int NKB = KT / 16, NST = KT / 32, NC = D / 32, NDB = D / 16;
+  __shared__ __align__(1024) char smem[STAGES * STAGE];
+
+  ItemCtx c;
+  if (!load_item(a, c)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  const char* kc = static_cast<const char*>(a.kc);
+  const char* vc = static_cast<const char*>(a.vc);
+  const char* kt = static_cast<const char*>(a.kt);
+  const char* vt = static_cast<const char*>(a.vt);
+  const long rstride = a.stride * 2;           // bytes per cache row
+  const long head_off = static_cast<long>(c.kvh) * D * 2;
+  const float scale = a.scale_log2;
+  // per-request bases (the head offset folded in); keys index rows from here
+  const char* kc_b = kc + static_cast<long>(c.b) * a.L_cap * rstride + head_off;
+  const char* vc_b = vc + static_cast<long>(c.b) * a.L_cap * rstride + head_off;
+  const char* kt_b = kt + static_cast<long>(c.b) * a.N_max * rstride + head_off;
+  const char* vt_b = vt + static_cast<long>(c.b) * a.N_max * rstride + head_off;
+  const int k_end = c.k_end, l_b = c.l_b;
+  uint32_t toff[KT / 8];  // byte offset of this thread's n-th load within a prefix tile
+#pragma unroll
+  for (int n = 0; n < KT / 8; ++n) {
+    const int g = n * 4 + wave;
+    const int row = (g % (KT / 4)) * 4 + (lane >> 4);
+    toff[n] = static_cast<uint32_t>(row * rstride + (((lane & 15) ^ swz(row)) << 4));
+  }
+  auto load_tile = [&](int tt0, int stage) {
+    char* dst = smem + stage * STAGE;
+    if (tt0 + KT <= k_end && tt0 + KT <= l_b)
+      gqa_issue_prefix_tile<KT>(dst, wave, kc_b + tt0 * rstride, vc_b + tt0 * rstride, toff);
+    else
+      gqa_issue_tile<KT>(dst, tt0, wave, lane, k_end, l_b, kc_b, vc_b, kt_b, vt_b, rstride);
+  };
+
+  bf16x8 qf[RG][NC];
+  uint32_t anc[RG][4];
+  bool act[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int r_first = c.rowb * RB + wave * RG * 16 + rg * 16;
+    act[rg] = __builtin_amdgcn_readfirstlane(r_first < c.rows_b ? 1 : 0) != 0;
+    const int r = r_first + lr;
+    const bool rv = r < c.rows_b;
+    const int node = rv ? r / a.G : 0;
+    const int h = c.kvh * a.G + (rv ? r % a.G : 0);
+    const uint16_t* src = qp + ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * D;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      if (rv) qf[rg][k] = *reinterpret_cast<const bf16x8*>(src + 32 * k + 8 * lq);
+      else qf[rg][k] = bf16x8{};
+    }
+    const unsigned* ab = a.anc + (static_cast<size_t>(c.b) * a.N_max + node) * a.W;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) anc[rg][w] = (rv && w < a.W) ? ab[w] : 0u;
+  }
+
+  float m_run[RG], l_run[RG];
+  f32x4 o[RG][NDB];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    m_run[rg] = -INFINITY;
+    l_run[rg] = 0.f;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) o[rg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int ntiles = (c.k_end - c.k_beg + KT - 1) / KT;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < ntiles) load_tile(c.k_beg + s * KT, s);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = c.k_beg + t * KT;
+    const int later = min(STAGES - 2, ntiles - 1 - t);
+    wait_tile<LPT, STAGES>(later);
+    lds_barrier();  // tile t visible to all waves; stage of tile t-1 free
+    if (t + STAGES - 1 < ntiles) load_tile(t0 + (STAGES - 1) * KT, (t + STAGES - 1) % STAGES);
+    const char* kb_base = smem + (t % STAGES) * STAGE;
+    const char* vb_base = kb_base + KT * ROWB;
+
+    // scores, transposed: lane holds S^T[key = kb*16 + 4*lq + i][row = lr]
+    f32x4 s[RG][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = kb * 16 + lr;
+      const char* rp = kb_base + row * ROWB;
+      const int sw = swz(row);
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp + (((4 * k + lq) ^ sw) << 4));
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)  // idle row groups hold zero queries
+          s[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][k], s[rg][kb], 0, 0, 0);
+      }
+    }
+
+    const bool full = (t0 + KT <= c.k_end) && (t0 + KT <= c.l_b);
+    bf16x8 pf[RG][NST];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      if (!act[rg]) {
+#pragma unroll
+        for (int st = 0; st < NST; ++st) pf[rg][st] = bf16x8{};
+        continue;
+      }
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = key_visible(anc[rg], t0 + kb * 16 + 4 * lq + i, c.l_b, c.k_end);
+            s[rg][kb][i] = ok ? s[rg][kb][i] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[rg][kb][0], s[rg][kb][1]), fmaxf(s[rg][kb][2], s[rg][kb][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescaling: a row's reference max moves only when the tile max
+      // exceeds it by more than kLazy (log2 units), so p <= 2^kLazy and the
+      // accumulators are rescaled rarely; the final normalisation is exact.
+      const float mt = mx * scale;
+      if (__ballot(mt > m_run[rg] + kLazy)) {
+        const float mnew = mt > m_run[rg] + kLazy ? mt : m_run[rg];
+        const float alpha = m_run[rg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - mnew);
+        l_run[rg] *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[rg][d] *= alpha;
+        m_run[rg] = mnew;
+      }
+      const float muse = m_run[rg] == -INFINITY ? 0.f : m_run[rg];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[rg][kb][i], scale, -muse));
+          lsum += p;
+          pf[rg][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
+        }
+      }
+      l_run[rg] += lsum;
+    }
+
+    // values: O^T[dv][row] += V^T[dv][keys] * P^T[keys][row]
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const int chunk = 2 * d + ((lr & 3) >> 1);
+        const int boff = (lr & 1) << 3;
+        const int row0 = 32 * st + 4 * lq + (lr >> 2);
+        const int row1 = row0 + 16;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TSV_LDS4(vb_base + row0 * ROWB + ((chunk ^ swz(row0)) << 4) + boff));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TSV_LDS4(vb_base + row1 * ROWB + ((chunk ^ swz(row1)) << 4) + boff));
+        union {
+          s16x4 h[2];
+          bf16x8 v;
+        } vf;
+        vf.h[0] = lo;
+        vf.h[1] = hi;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          o[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rg][st], o[rg][d], 0, 0, 0);
+      }
+    }
+  }
+
+  // lane holds O^T[dv = d*16 + 4*lq + i][row = lr]
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    if (!act[rg]) continue;
+    float lt = l_run[rg];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int r_loc = wave * RG * 16 + rg * 16 + lr;
+    const int r = c.rowb * RB + r_loc;
+    if (r >= c.rows_b) continue;
+    if (c.splits == 1) {
+      const int node = r / a.G, h = c.kvh * a.G + r % a.G;
+      const size_t orow = (static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h;
+      uint16_t* op = static_cast<uint16_t*>(a.out) + orow * D;
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        union {
+          uint2 u;
+          __bf16 h4[4];
+        } pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(o[rg][d][i] * inv);
+        *reinterpret_cast<uint2*>(op + d * 16 + 4 * lq) = pk.u;
+      }
+      if (lq == 0 && a.lse) a.lse[orow] = (m_run[rg] + log2f(lt)) * kLn2;
+    } else {
+      const size_t prow = static_cast<size_t>(blockIdx.x) * RB + r_loc;
+      float* pa = a.part_acc + prow * D;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+        *reinterpret_cast<float4*>(pa + d * 16 + 4 * lq) =
+            make_float4(o[rg][d][0], o[rg][d][1], o[rg][d][2], o[rg][d][3]);
+      if (lq == 0) {
+        a.part_ml[prow * 2 + 0] = m_run[rg];
+        a.part_ml[prow * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------- VALU path
 template <typename T>
 __device__ __forceinline__ float ld_elem(const T* p);
@@ -554,6 +895,94 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   }
 }
 
+// --------------------------------------------------- combine (MFMA paths)
+// One wavefront per (request, node, head) row whose unit was split: lanes
+// read the splits' (max, sum) pairs once, then cooperate over splits and
+// 16-byte chunks of the fp32 accumulators so every load is independent.
+template <int DV>
+__global__ __launch_bounds__(256) void attn_combine_vec_kernel(AttnArgs a) {
+  constexpr int NCH = DV / 4;                   // float4 chunks per row
+  constexpr int GROUPS = NCH >= 64 ? 1 : 64 / NCH;
+  constexpr int CPL = NCH >= 64 ? NCH / 64 : 1;  // chunks per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long row = static_cast<long>(blockIdx.x) * 4 + wave;
+  if (row >= static_cast<long>(a.B) * a.N_max * a.Hq) return;
+  const int h = static_cast<int>(row % a.Hq);
+  const long bi = row / a.Hq;
+  const int i = static_cast<int>(bi % a.N_max);
+  const int b = static_cast<int>(bi / a.N_max);
+  const int n_b = clampi(a.n_nodes[b], 0, a.N_max);
+  if (i >= n_b) return;
+  const int splits = a.info[4 * b + 1];
+  if (splits <= 1) return;
+  const int rbs = a.info[4 * b + 2];
+  const int kvh = h / a.G;
+  const int r = i * a.G + h % a.G;
+  const int rowb = r / a.RB, r_loc = r % a.RB;
+  const long item0 = a.info[4 * b] + static_cast<long>(kvh * rbs + rowb) * splits;
+  if (item0 + splits > a.items_max) return;
+  const float* ml = a.part_ml + (item0 * a.RB + r_loc) * 2;
+  const long mstride = static_cast<long>(a.RB) * 2;
+  float M = -INFINITY;
+  for (int s2 = lane; s2 < splits; s2 += 64) M = fmaxf(M, ml[s2 * mstride]);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+  float L = 0.f;
+  for (int s2 = lane; s2 < splits; s2 += 64) {
+    const float ms = ml[s2 * mstride];
+    L += ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[s2 * mstride + 1];
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) L += __shfl_xor(L, m);
+  const int grp = lane / (64 / GROUPS);
+  const int cl = lane % (64 / GROUPS);
+  float4 acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* pa = a.part_acc + (item0 * a.RB + r_loc) * DV;
+  const long astride = static_cast<long>(a.RB) * DV;
+#pragma unroll 4
+  for (int s2 = grp; s2 < splits; s2 += GROUPS) {
+    const float ms = ml[s2 * mstride];
+    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float4 v = *reinterpret_cast<const float4*>(pa + s2 * astride + 4 * (cl + 64 * c));
+      acc[c].x = fmaf(w, v.x, acc[c].x);
+      acc[c].y = fmaf(w, v.y, acc[c].y);
+      acc[c].z = fmaf(w, v.z, acc[c].z);
+      acc[c].w = fmaf(w, v.w, acc[c].w);
+    }
+  }
+  if (GROUPS == 2) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      acc[c].x += __shfl_xor(acc[c].x, 32);
+      acc[c].y += __shfl_xor(acc[c].y, 32);
+      acc[c].z += __shfl_xor(acc[c].z, 32);
+      acc[c].w += __shfl_xor(acc[c].w, 32);
+    }
+  }
+  const float inv = 1.0f / L;
+  const size_t orow = (static_cast<size_t>(b) * a.N_max + i) * a.Hq + h;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + orow * DV;
+  if (grp == 0) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      union {
+        uint2 u;
+        __bf16 h4[4];
+      } pk;
+      pk.h4[0] = static_cast<__bf16>(acc[c].x * inv);
+      pk.h4[1] = static_cast<__bf16>(acc[c].y * inv);
+      pk.h4[2] = static_cast<__bf16>(acc[c].z * inv);
+      pk.h4[3] = static_cast<__bf16>(acc[c].w * inv);
+      *reinterpret_cast<uint2*>(op + 4 * (cl + 64 * c)) = pk.u;
+    }
+  }
+  if (lane == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * kLn2;
+}
+
 // ----------------------------------------------------------------- combine
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
@@ -643,12 +1072,12 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype, hipStream_t s) {
-  attn_plan_kernel<<<dim3(1), dim3(256), 0, s>>>(a);
+  attn_plan_kernel<<<dim3(1), dim3(kPlanThreads), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(a.items_max), block(256);
   if (path == kPathMfmaGqa) {
-    attn_mfma_kernel<128, 128, 2, 64, true><<<grid, block, 0, s>>>(a);
+    attn_gqa_kernel<64, 2><<<grid, block, 0, s>>>(a);
   } else if (path == kPathMfmaLatent) {
     attn_mfma_kernel<576, 512, 1, 32, false><<<grid, block, 0, s>>>(a);
   } else if (dtype == TSV_F32) {
@@ -660,7 +1089,11 @@ hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype, hipStre
   if (e != hipSuccess) return e;
   const long rows = static_cast<long>(a.B) * a.N_max * a.Hq;
   dim3 g2(static_cast<unsigned>((rows + 3) / 4));
-  if (dtype == TSV_F32)
+  if (path == kPathMfmaGqa)
+    attn_combine_vec_kernel<128><<<g2, block, 0, s>>>(a);
+  else if (path == kPathMfmaLatent)
+    attn_combine_vec_kernel<512><<<g2, block, 0, s>>>(a);
+  else if (dtype == TSV_F32)
     attn_combine_kernel<float><<<g2, block, 0, s>>>(a);
   else
     attn_combine_kernel<uint16_t><<<g2, block, 0, s>>>(a);
