@@ -157,24 +157,64 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(
   WaveSelect<SLOTS> sel;
   sel.init(k, queue[wave], lane);
 
-  if (VEC) {
-    for (int base = beg; base < end; base += 1024) {
-      float4 v[4];
+  // Warm-up on the first 1024 elements: seed the list with every lane's best
+  // (and, for lists of 128, second best) element in one sort, then offer
+  // only the rest.  Without the seed the threshold admits everything until k
+  // keys are seen, and each 64 admissions cost a full sort and merge.
+  {
+    float v[16];
+    int e0[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 16; ++u) {
+      // element order per lane is increasing in index, as in the main loop
+      const int e = VEC ? beg + (u >> 2) * 256 + lane * 4 + (u & 3) : beg + u * 64 + lane;
+      e0[u] = e;
+      v[u] = e < end ? p[e] : -INFINITY;
+    }
+    uint64_t k1 = 0, k2 = 0;
+    int u1 = -1, u2 = -1;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint64_t kk = e0[u] < end ? sel_key(v[u], e0[u]) : 0;
+      if (kk > k1) { k2 = k1; u2 = u1; k1 = kk; u1 = u; }
+      else if (kk > k2) { k2 = kk; u2 = u; }
+    }
+    sel.list.v[0] = sort64_desc(k1, lane);
+    if (SLOTS > 1) sel.list.merge(sort64_desc(k2, lane));
+    sel.tau = sel.list.at(k - 1);
+    if (sel.tau != 0) {
+      const uint32_t o = static_cast<uint32_t>(sel.tau >> 32);
+      sel.tau_v = __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool seeded = (u == u1) || (SLOTS > 1 && u == u2);
+      const bool ok = e0[u] < end && !seeded && v[u] >= sel.tau_v;
+      if (__ballot(ok) == 0) continue;
+      sel.offer(ok ? sel_key(v[u], e0[u]) : 0);
+    }
+  }
+
+  if (VEC) {
+    for (int base = beg + 1024; base < end; base += 2048) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
         int e = base + u * 256 + lane * 4;
         if (e < end) v[u] = *reinterpret_cast<const float4*>(p + e);
         else v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       }
       float m = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
         m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
       if (__ballot(m >= sel.tau_v) == 0) continue;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         int e = base + u * 256 + lane * 4;
         bool ok = e < end;
+        if (__ballot(ok && fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)) >= sel.tau_v) == 0)
+          continue;
         sel.offer(ok ? sel_key(v[u].x, e) : 0);
         sel.offer(ok ? sel_key(v[u].y, e + 1) : 0);
         sel.offer(ok ? sel_key(v[u].z, e + 2) : 0);
@@ -182,7 +222,7 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(
       }
     }
   } else {
-    for (int base = beg; base < end; base += 1024) {
+    for (int base = beg + 1024; base < end; base += 1024) {
       float v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -206,35 +246,51 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(
   for (int s = 0; s < SLOTS; ++s) out[s * 64 + lane] = sel.list.v[s];
 }
 
-template <int SLOTS>
+// One workgroup per row: the first k keys of every segment list (only they
+// can reach the row's top k) are sorted descending in LDS with a bitonic
+// network; the first k are the row's top-k.
+constexpr int kMergeCap = 4096;  // nseg * k, enforced by topk_plan
+
 __global__ __launch_bounds__(256) void topk_merge_kernel(
-    const float* __restrict__ x, int rows, int V, int k, int nseg,
+    const float* __restrict__ x, int rows, int V, int k, int nseg, int ks,
     const uint64_t* __restrict__ seg_keys, int* __restrict__ out_idx,
     float* __restrict__ out_p) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= rows) return;
-  WaveList<SLOTS> list;
-  list.clear(lane);
-  const uint64_t* src = seg_keys + static_cast<size_t>(row) * nseg * (64 * SLOTS);
-  for (int seg = 0; seg < nseg; ++seg) {
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      // a 64-slot slice of a descending list is itself descending
-      list.merge(src[(seg * SLOTS + s) * 64 + lane]);
+  __shared__ uint64_t keys[kMergeCap];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int n = nseg * k;
+  int P = 1;
+  while (P < n) P <<= 1;
+  const uint64_t* src = seg_keys + static_cast<size_t>(row) * nseg * ks;
+  for (int i = t; i < P; i += 256) {
+    uint64_t v = 0;
+    if (i < n) v = src[(i / k) * ks + (i % k)];
+    keys[i] = v;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = t; i < P / 2; i += 256) {
+        const int lo = 2 * i - (i & (stride - 1));   // lower index of the pair
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t a = keys[lo], b = keys[hi];
+        if ((a < b) == desc) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
     }
   }
-#pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    int pos = s * 64 + lane;
-    if (pos < k) {
-      // every row holds V >= k elements, so the first k slots are filled;
-      // the guard keeps an impossible empty slot inside the row
-      uint32_t idx = list.v[s] ? sel_key_index(list.v[s]) : 0u;
-      out_idx[static_cast<size_t>(row) * k + pos] = static_cast<int>(idx);
-      // re-read the element so the stored probability keeps its exact bits
-      out_p[static_cast<size_t>(row) * k + pos] = x[static_cast<size_t>(row) * V + idx];
-    }
+  for (int pos = t; pos < k; pos += 256) {
+    const uint64_t key = keys[pos];
+    // every row holds V >= k elements, so the first k slots are filled;
+    // the guard keeps an impossible empty slot inside the row
+    const uint32_t idx = key ? sel_key_index(key) : 0u;
+    out_idx[static_cast<size_t>(row) * k + pos] = static_cast<int>(idx);
+    // re-read the element so the stored probability keeps its exact bits
+    out_p[static_cast<size_t>(row) * k + pos] = x[static_cast<size_t>(row) * V + idx];
   }
 }
 
@@ -248,11 +304,12 @@ TopkPlan topk_plan(int rows, int V, int k) {
   p.slots = k <= 64 ? 1 : 2;
   p.vec = (V % 4) == 0;
   int want = (kScanWaves + rows - 1) / rows;
-  int most = V / 2048 > 1 ? V / 2048 : 1;  // segments of at least ~2k elements
+  int most = V / 4096 > 1 ? V / 4096 : 1;  // segments of at least ~4k elements
+  if (most > kMergeCap / k) most = kMergeCap / k;
   int nseg = want < most ? want : most;
   if (nseg < 1) nseg = 1;
   int len = (V + nseg - 1) / nseg;
-  len = (len + 1023) / 1024 * 1024;
+  len = (len + 1023) / 2048 * 2048 + 1024;  // one warm-up block of 1024, then steps of 2048
   p.seg_len = len;
   p.nseg = (V + len - 1) / len;
   return p;
@@ -279,11 +336,8 @@ hipError_t launch_topk(const float* x, const TopkPlan& p, uint64_t* seg_keys,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2((p.rows + 3) / 4);
-  if (p.slots == 1)
-    topk_merge_kernel<1><<<g2, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, seg_keys, out_idx, out_p);
-  else
-    topk_merge_kernel<2><<<g2, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, seg_keys, out_idx, out_p);
+  topk_merge_kernel<<<dim3(p.rows), block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, 64 * p.slots,
+                                                   seg_keys, out_idx, out_p);
   return hipGetLastError();
 }
 

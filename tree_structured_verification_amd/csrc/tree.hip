@@ -42,7 +42,7 @@ __device__ __forceinline__ double round_cost(const tsv_cost& c, int n, double l)
 __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   __shared__ float s_p[kMaxTopkTable];
   __shared__ int s_i[kMaxTopkTable];
-  __shared__ int n_par[128], n_tok[128], n_dep[128];
+  __shared__ int n_par[128], n_dep[128], n_rank[128];
   __shared__ float n_sc[128];
 
   const int b = blockIdx.x;
@@ -55,20 +55,35 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   }
   __syncthreads();
 
-  uint64_t fr[kFrontierSlots];
+  // Frontier slot = 64-bit order key split in (hi = ordered score bits,
+  // lo = depth/parent/rank fields, 0 = empty) plus the entry's exact score
+  // and its parent's score, so a pop reads everything from the winner lane.
+  uint32_t fhi[kFrontierSlots], flo[kFrontierSlots];
+  float fsc[kFrontierSlots], fps[kFrontierSlots];
 #pragma unroll
-  for (int s = 0; s < kFrontierSlots; ++s) fr[s] = 0;
+  for (int s = 0; s < kFrontierSlots; ++s) {
+    fhi[s] = 0;
+    flo[s] = 0;
+    fsc[s] = 0.f;
+    fps[s] = 0.f;
+  }
   int cnt = 0;
-  auto push = [&](uint64_t key) {
+  auto push = [&](float score, float parent_score, int depth, int parent, int rank) {
+    const uint64_t key = frontier_key(score, depth, parent, rank);
     const int L = cnt & 63, S = cnt >> 6;
 #pragma unroll
     for (int s = 0; s < kFrontierSlots; ++s)
-      if (s == S && lane == L) fr[s] = key;
+      if (s == S && lane == L) {
+        fhi[s] = static_cast<uint32_t>(key >> 32);
+        flo[s] = static_cast<uint32_t>(key);
+        fsc[s] = score;
+        fps[s] = parent_score;
+      }
     ++cnt;
   };
 
   // the root's best child: score 1 * q, depth 1, rank 0
-  push(frontier_key(__fmul_rn(1.0f, s_p[0]), 1, -1, 0));
+  push(__fmul_rn(1.0f, s_p[0]), 1.0f, 1, -1, 0);
 
   const double l = a.adaptive ? static_cast<double>(a.prefix_len[b]) : 0.0;
   double phi = 0.0;
@@ -76,16 +91,40 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 
   int m = 0;
   while (m < a.cap) {
-    uint64_t best = 0;
+    // best slot of this lane (hi, then lo)
+    uint32_t bh = 0, bl = 0;
+    int bs = 0;
 #pragma unroll
-    for (int s = 0; s < kFrontierSlots; ++s) best = umax64(best, fr[s]);
-    best = wave_max_u64(best);
-    if (best == 0) break;  // every candidate taken
-    const int rank = 127 - static_cast<int>(best & 127);
-    const int par = 255 - static_cast<int>((best >> 7) & 255) - 1;
-    const int dep = 63 - static_cast<int>((best >> 15) & 63) + 1;
-    const float ps = par < 0 ? 1.0f : n_sc[par];
-    const float sc = __fmul_rn(ps, s_p[(dep - 1) * a.k + rank]);
+    for (int s = 0; s < kFrontierSlots; ++s) {
+      const bool better = fhi[s] > bh || (fhi[s] == bh && flo[s] > bl);
+      bh = better ? fhi[s] : bh;
+      bl = better ? flo[s] : bl;
+      bs = better ? s : bs;
+    }
+    const uint32_t wh = wave_max_u32(bh);
+    if (wh == 0) break;  // every candidate taken
+    uint64_t cand = __ballot(bh == wh);
+    uint32_t wl;
+    if (__popcll(cand) == 1) {
+      wl = __builtin_amdgcn_readlane(bl, __ffsll(static_cast<long long>(cand)) - 1);
+    } else {  // equal scores: settle by depth, parent position, rank
+      wl = wave_max_u32(bh == wh ? bl : 0u);
+      cand = __ballot(bh == wh && bl == wl);
+    }
+    const int wlane = __ffsll(static_cast<long long>(cand)) - 1;
+    const int wslot = __builtin_amdgcn_readlane(bs, wlane);
+    const int rank = 127 - static_cast<int>(wl & 127);
+    const int par = 255 - static_cast<int>((wl >> 7) & 255) - 1;
+    const int dep = 63 - static_cast<int>((wl >> 15) & 63) + 1;
+    float sc_l = 0.f, ps_l = 0.f;
+#pragma unroll
+    for (int s = 0; s < kFrontierSlots; ++s)
+      if (s == wslot) {
+        sc_l = fsc[s];
+        ps_l = fps[s];
+      }
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_l), wlane));
+    const float ps = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps_l), wlane));
     if (a.adaptive) {
       const double phi2 = __dadd_rn(phi, static_cast<double>(sc));
       const double th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, m + 1, l));
@@ -95,19 +134,21 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     }
     if (lane == 0) {
       n_par[m] = par;
-      n_tok[m] = s_i[(dep - 1) * a.k + rank];
       n_dep[m] = dep;
+      n_rank[m] = rank;
       n_sc[m] = sc;
     }
 #pragma unroll
     for (int s = 0; s < kFrontierSlots; ++s)
-      if (fr[s] == best) fr[s] = 0;
-    if (rank + 1 < a.k)
-      push(frontier_key(__fmul_rn(ps, s_p[(dep - 1) * a.k + rank + 1]), dep, par, rank + 1));
-    if (dep < a.gamma)
-      push(frontier_key(__fmul_rn(sc, s_p[dep * a.k]), dep + 1, m, 0));
+      if (lane == wlane && s == wslot) {
+        fhi[s] = 0;
+        flo[s] = 0;
+      }
+    const float q_sib = rank + 1 < a.k ? s_p[(dep - 1) * a.k + rank + 1] : 0.f;
+    const float q_kid = dep < a.gamma ? s_p[dep * a.k] : 0.f;
+    if (rank + 1 < a.k) push(__fmul_rn(ps, q_sib), ps, dep, par, rank + 1);
+    if (dep < a.gamma) push(__fmul_rn(sc, q_kid), sc, dep + 1, m, 0);
     ++m;
-    wave_lds_sync();  // n_sc[m-1] is read by every lane in later pops
   }
   const int n = m;
   __syncthreads();
@@ -117,7 +158,7 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   for (int i = lane; i < a.N_max; i += 64) {
     const bool v = i < n;
     a.parent[nb + i] = v ? n_par[i] : -1;
-    a.token[nb + i] = v ? n_tok[i] : -1;
+    a.token[nb + i] = v ? s_i[(n_dep[i] - 1) * a.k + n_rank[i]] : -1;
     a.depth[nb + i] = v ? n_dep[i] : -1;
     a.score[nb + i] = v ? n_sc[i] : 0.0f;
     uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;

@@ -60,6 +60,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
+// Wave-wide max of an unsigned 32-bit value with DPP (pairs, quads, 8- and
+// 16-lane mirrors) and four readlanes; returns the max in every lane.
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v),
+                                                           CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax32(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = umax32(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = umax32(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = umax32(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return umax32(umax32(r0, r1), umax32(r2, r3));
+}
+
 // Orders LDS traffic of one wavefront around a point where lanes exchange
 // data through LDS.
 __device__ __forceinline__ void wave_lds_sync() {

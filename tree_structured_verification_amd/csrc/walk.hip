@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void argmax_segment_kernel(
   if (VEC) {
     constexpr int N = Vec16<T>::N;
     constexpr int STEP = 64 * N;
-    for (int base = beg; base < end; base += 4 * STEP) {
-      float v[4][N];
+    for (int base = beg; base < end; base += 8 * STEP) {
+      float v[8][N];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         int e = base + u * STEP + lane * N;
         if (e < end) Vec16<T>::load(p + e, v[u]);
         else {
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void argmax_segment_kernel(
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         int e = base + u * STEP + lane * N;
 #pragma unroll
         for (int c = 0; c < N; ++c) {
