@@ -32,7 +32,11 @@
  *   - Floating-point inputs must be finite (marginals also non-negative);
  *     results for NaN inputs are unspecified but memory-safe.
  *   - `ws` is device scratch of at least tsv_workspace_size(...) bytes, owned
- *     by the caller, 256-byte aligned; its contents on entry do not matter.
+ *     by the caller, 256-byte aligned.  For build_tree and accept_walk its
+ *     contents on entry do not matter.  tree_verify_attn keeps arrival
+ *     counters in it: that workspace must be all zero before its first use
+ *     (e.g. one hipMemset at allocation), every call leaves the counters at
+ *     zero again, and it must not be shared with the other entry points.
  *     Two calls that run concurrently need distinct workspaces.
  *
  * Notation: B requests; gamma drafter positions (= maximum tree depth);
@@ -142,6 +146,11 @@ int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
  *   lse       fp32 [B][N_max][Hq] or NULL
  * Requirements: Hq % Hkv == 0; kv_row_stride >= Hkv*max(d_qk, d_v);
  * 1 <= d_qk, d_v <= 576; B <= 4096.  Accumulation is fp32.
+ * Workspace: zero before the first call, see the conventions above.  The key
+ * range of a (request, KV head, row block) may be split over several
+ * workgroups whose partial results the last of them combines, so the exact
+ * rounding of `out` depends on the split sizes (which depend on B, N_max,
+ * L_cap and the head shape, never on the data).
  */
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const void* k_tree, const void* v_tree, long kv_row_stride,

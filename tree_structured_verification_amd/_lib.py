@@ -115,7 +115,9 @@ def workspace_size(which: int, B=1, gamma=1, V=1, top_k=1, N_max=1, L_cap=0, Hq=
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """Zero-filled device workspace (tree_verify_attn needs zeros on first use
+    and leaves them in place; the other entry points accept any contents)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def _cost_struct(cost):

@@ -212,6 +212,11 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
   a.items_max = P.items_max;
   a.target_items = P.target_items;
   a.min_chunk = P.min_chunk;
+  a.counters = reinterpret_cast<int*>(w + P.off_cnt);
+  a.chunk = P.chunk;
+  a.S = P.S;
+  a.units = P.units;
+  a.rbs = P.rbs;
   return launch_status(launch_attention(a, P.path, dtype, static_cast<hipStream_t>(stream)));
 }
 

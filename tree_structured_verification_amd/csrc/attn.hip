@@ -423,18 +423,17 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
 
 // ------------------------------------------------ grouped-query MFMA path
 // Grouped-query heads of width 128 (the common bf16 case): 128 query rows per
-// work item (4 waves x 2 groups of 16 rows), keys streamed in tiles of KT.
+// work item (4 waves x 2 groups of 16 rows), keys streamed in tiles of 32.
 //
 // Memory pipeline: K and V tiles go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no register staging) into a ring of STAGES
-// buffers, so STAGES-1 tiles are in flight while one is computed; waits are
-// explicit vmcnt counts and bare barriers (a workgroup fence would drain
+// global_load_lds_dwordx4 (no register staging) into a ring of slots; waits
+// are explicit vmcnt counts and bare barriers (a workgroup fence would drain
 // every outstanding load).  Rows are stored unpadded (256 B) with 16-byte
 // chunk c of row r at slot c ^ swz(r); the swizzle is applied through the
 // global source address of each lane, since the LDS destination of these
-// loads is fixed by the lane id.  swz() makes both the K reads (16 rows, one
-// chunk) and the transposed V reads (8 rows x 2 chunks per half-wave)
-// bank-conflict free.
+// loads is fixed by the lane id.  swz() spreads both the K reads (16 rows,
+// one chunk) and the transposed V reads (8 rows x 2 chunks per half-wave)
+// over the LDS banks.
 //
 // The value operand of O^T = V^T P^T needs, per lane, four consecutive keys
 // of one value column: ds_read_b64_tr_b16 returns exactly that from V in its
@@ -458,13 +457,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-template <int LPT, int S>
-__device__ __forceinline__ void wait_tile(int later) {
-  // `later` tiles were issued after the one now needed (0 <= later <= S-2)
-  if (S >= 4 && later >= 2) wait_vmcnt<LPT * 2 * (S >= 4)>();
-  else if (S >= 3 && later >= 1) wait_vmcnt<LPT * (S >= 3)>();
-  else wait_vmcnt<0>();
-}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define TSV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -474,27 +466,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // indices t0 .. t0+KT-1 of one request) into an LDS stage: KT/8
 // wave-instructions, each filling 4 consecutive 256-byte rows.  Keys at or
 // past k_end re-read row k_end-1 (finite data; masked by the caller).
-// Fast path of the loader for a tile that lies entirely inside the prefix:
-// the per-thread byte offsets within a tile (off[n]) are fixed, only the
-// tile base moves.
-template <int KT>
-__device__ __forceinline__ void gqa_issue_prefix_tile(char* stage, int wave, const char* kbase,
-                                                      const char* vbase, const uint32_t* off) {
-#pragma unroll
-  for (int n = 0; n < KT / 8; ++n) {
-    const int g = n * 4 + wave;
-    const int region = g / (KT / 4);
-    const int rq = g % (KT / 4);
-    const char* src = (region == 0 ? kbase : vbase) + off[n];
-    const uint32_t dst = static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>(TSV_LDS(stage + region * KT * 256 + rq * 1024)));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(dst), "v"(src)
-                 : "memory", "m0");
-  }
-}
-
 template <int KT>
 __device__ __forceinline__ void gqa_issue_tile(char* stage, int t0, int wave, int lane,
                                                int k_end, int l_b, const char* kc_b,
@@ -515,8 +486,8 @@ __device__ __forceinline__ void gqa_issue_tile(char* stage, int t0, int wave, in
     // Issued as inline asm on purpose: the compiler does not track these
     // LDS writes, so it adds no conservative vmcnt(0) before every LDS read
     // of the tile being computed.  Ordering is explicit: each tile is waited
-    // for with wait_tile() (vmcnt counts these loads in issue order) and a
-    // barrier before any wave reads it.
+    // for with an explicit vmcnt count (these loads complete in issue order)
+    // and a barrier before any wave reads it.
     const uint32_t dst = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>(TSV_LDS(stage + region * KT * 256 + rq * 1024)));
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -526,58 +497,171 @@ __device__ __forceinline__ void gqa_issue_tile(char* stage, int t0, int wave, in
   }
 }
 
-template <int KT, int STAGES>
-__global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnArgs a) {
-  constexpr int D = 128, RG = 2, RB = 128;
-  constexpr int ROWB = 256;                    // bytes per key row
-  constexpr int STAGE = 2 * KT * ROWB;         // K tile then V tile
-  constexpr int LPT = KT / 8;                  // 16-byte loads per thread per tile
-  constexpr int NKB = KT / 16, NST = KT / 32, NC = D / 32, NDB = D / 16;
-  __shared__ __align__(1024) char smem[STAGES * STAGE];
+// ------------------------------------ grouped-query MFMA path, pipelined
+// Same work item and LDS layout as above, restructured so that matrix and
+// vector work of one wavefront overlap: tiles of 32 keys go through a ring of
+// NSLOT slots (NSLOT-2 tiles in flight), and iteration t issues
+//   phase 1: the score MFMAs of tile t+1  |  exp / convert / sum of tile t
+//   phase 2: the value MFMAs of tile t    |  mask and row max of tile t+1
+// followed by the (rare) lazy rescale for tile t+1.  Both phases are single
+// basic blocks of independent MFMA and VALU instructions, so the sequencer
+// co-issues them.  Row max / sum across the four 16-lane groups use the
+// permlane swaps (VALU) rather than LDS permutes.
+
+// max of v over the lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float quad_group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// LDS-DMA of one 1 KiB block: 64 lanes x 16 bytes from sbase + voff (sbase
+// is wave-uniform; readfirstlane puts it in scalar registers for the
+// instruction's saddr operand).  m0 is written here and used by nothing the
+// compiler emits in these kernels, so clobbering it is safe.
+__device__ __forceinline__ void dma_1k(uint32_t lds_dst, const char* sbase, uint32_t voff) {
+  // readfirstlane returns int: both halves go through uint32_t so that the
+  // low half is zero-extended, never sign-extended, into the 64-bit address
+  const uint64_t p = reinterpret_cast<uintptr_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32))));
+  const uint64_t sp = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_dst)), "v"(voff), "s"(sp)
+               : "memory", "m0");
+}
+
+// Relaxed atomics at agent scope: coherent across the XCDs without ordering
+// anything else (no cache-wide write-back or invalidation).
+__device__ __forceinline__ void st_coherent2(uint64_t* p, float x, float y) {
+  const uint64_t v = (static_cast<uint64_t>(__float_as_uint(y)) << 32) | __float_as_uint(x);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_coherent2(const uint64_t* p) {
+  const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+template <int LPT, int L>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (L == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= L) wait_vmcnt<LPT * L>();
+    else wait_later<LPT, L - 1>(later);
+  }
+}
+
+// Work item of the one-kernel grouped-query path.  Workgroup ids are dealt to
+// the XCDs round robin (id % 8); consecutive ids on one XCD take the S splits
+// of one unit, so a unit's splits run side by side and share that XCD's L2,
+// where the last one to finish reads the others' partials.
+__device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& unit) {
+  const int id = static_cast<int>(blockIdx.x);
+  const int slot = id >> 3;
+  unit = (slot / a.S) * 8 + (id & 7);
+  const int split = slot % a.S;
+  if (unit >= a.units) return false;
+  const int per_b = a.Hkv * a.rbs;
+  c.b = unit / per_b;
+  const int rem = unit - c.b * per_b;
+  c.kvh = rem / a.rbs;
+  c.rowb = rem - c.kvh * a.rbs;
+  c.n_b = clampi(a.n_nodes[c.b], 0, a.N_max);
+  c.l_b = clampi(a.prefix_len[c.b], 0, a.L_cap);
+  c.rows_b = c.n_b * a.G;
+  if (c.rowb * 128 >= c.rows_b) return false;
+  c.keys_b = c.l_b + c.n_b;
+  // the unit's keys in S nearly equal chunks (a multiple of 32 keys, at least
+  // a.chunk keys), so that the splits stay busy however short the prefix
+  int chunk = (c.keys_b + a.S - 1) / a.S;
+  chunk = (chunk + 31) / 32 * 32;
+  chunk = chunk > a.chunk ? chunk : a.chunk;
+  c.splits = (c.keys_b + chunk - 1) / chunk;  // <= S
+  if (split >= c.splits) return false;
+  c.split = split;
+  c.k_beg = split * chunk;
+  c.k_end = min(c.keys_b, c.k_beg + chunk);
+  return true;
+}
+
+template <int NSLOT>
+__global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
+  constexpr int KT = 32, D = 128, RG = 2, RB = 128;
+  constexpr int ROWB = 256;               // bytes per key row of one head
+  constexpr int TILEB = KT * ROWB;        // K (or V) part of a tile
+  constexpr int SLOT = 2 * TILEB;
+  constexpr int LPT = KT / 8;             // 1 KiB DMA blocks per thread per tile
+  constexpr int NKB = KT / 16, NC = D / 32, NDB = D / 16;
+  static_assert(NSLOT == 4, "the unrolled steps assume a ring of four tiles");
+  __shared__ __align__(1024) char smem[NSLOT * SLOT];
+  __shared__ int s_last;
 
   ItemCtx c;
-  if (!load_item(a, c)) return;
+  int unit;
+  if (!fused_item(a, c, unit)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-  const char* kc = static_cast<const char*>(a.kc);
-  const char* vc = static_cast<const char*>(a.vc);
-  const char* kt = static_cast<const char*>(a.kt);
-  const char* vt = static_cast<const char*>(a.vt);
-  const long rstride = a.stride * 2;           // bytes per cache row
+  const long rstride = a.stride * 2;
   const long head_off = static_cast<long>(c.kvh) * D * 2;
   const float scale = a.scale_log2;
-  // per-request bases (the head offset folded in); keys index rows from here
-  const char* kc_b = kc + static_cast<long>(c.b) * a.L_cap * rstride + head_off;
-  const char* vc_b = vc + static_cast<long>(c.b) * a.L_cap * rstride + head_off;
-  const char* kt_b = kt + static_cast<long>(c.b) * a.N_max * rstride + head_off;
-  const char* vt_b = vt + static_cast<long>(c.b) * a.N_max * rstride + head_off;
-  const int k_end = c.k_end, l_b = c.l_b;
-  uint32_t toff[KT / 8];  // byte offset of this thread's n-th load within a prefix tile
+  const char* kc_b = static_cast<const char*>(a.kc) + static_cast<long>(c.b) * a.L_cap * rstride + head_off;
+  const char* vc_b = static_cast<const char*>(a.vc) + static_cast<long>(c.b) * a.L_cap * rstride + head_off;
+  const char* kt_b = static_cast<const char*>(a.kt) + static_cast<long>(c.b) * a.N_max * rstride + head_off;
+  const char* vt_b = static_cast<const char*>(a.vt) + static_cast<long>(c.b) * a.N_max * rstride + head_off;
+  const int k_beg = c.k_beg, k_end = c.k_end, l_b = c.l_b;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TSV_LDS(smem)));
+
+  // this thread's two 1 KiB blocks of a tile's K part (the V part mirrors
+  // them); tiles are issued in order, so the source pointers just advance
+  uint32_t toff[2], tdst[2];
 #pragma unroll
-  for (int n = 0; n < KT / 8; ++n) {
-    const int g = n * 4 + wave;
-    const int row = (g % (KT / 4)) * 4 + (lane >> 4);
+  for (int n = 0; n < 2; ++n) {
+    const int rq = n * 4 + wave;                 // 4-row group, 0..7
+    const int row = rq * 4 + (lane >> 4);
     toff[n] = static_cast<uint32_t>(row * rstride + (((lane & 15) ^ swz(row)) << 4));
+    tdst[n] = lds0 + static_cast<uint32_t>(rq * 1024);
   }
-  auto load_tile = [&](int tt0, int stage) {
-    char* dst = smem + stage * STAGE;
-    if (tt0 + KT <= k_end && tt0 + KT <= l_b)
-      gqa_issue_prefix_tile<KT>(dst, wave, kc_b + tt0 * rstride, vc_b + tt0 * rstride, toff);
-    else
-      gqa_issue_tile<KT>(dst, tt0, wave, lane, k_end, l_b, kc_b, vc_b, kt_b, vt_b, rstride);
+  const long tile_bytes = static_cast<long>(KT) * rstride;
+  const char* kp = kc_b + static_cast<long>(k_beg) * rstride;
+  const char* vp = vc_b + static_cast<long>(k_beg) * rstride;
+  int tn = k_beg;  // first key of the next tile to issue
+  auto issue = [&](auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    if (tn + KT <= k_end && tn + KT <= l_b) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n) dma_1k(tdst[n] + SL * SLOT, kp, toff[n]);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) dma_1k(tdst[n] + SL * SLOT + TILEB, vp, toff[n]);
+    } else {
+      gqa_issue_tile<KT>(smem + SL * SLOT, tn, wave, lane, k_end, l_b, kc_b, vc_b, kt_b, vt_b, rstride);
+    }
+    kp += tile_bytes;
+    vp += tile_bytes;
+    tn += KT;
   };
+
+  // the key stream starts before anything else is loaded
+  const int ntiles = (k_end - k_beg + KT - 1) / KT;
+  issue(IC<0>{});
+  if (1 < ntiles) issue(IC<1>{});
+  if (2 < ntiles) issue(IC<2>{});
 
   bf16x8 qf[RG][NC];
   uint32_t anc[RG][4];
-  bool act[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const int r_first = c.rowb * RB + wave * RG * 16 + rg * 16;
-    act[rg] = __builtin_amdgcn_readfirstlane(r_first < c.rows_b ? 1 : 0) != 0;
-    const int r = r_first + lr;
-    const bool rv = r < c.rows_b;
+    const int r = c.rowb * RB + wave * RG * 16 + rg * 16 + lr;
+    const bool rv = r < c.rows_b;   // idle rows compute on zero queries, never written
     const int node = rv ? r / a.G : 0;
     const int h = c.kvh * a.G + (rv ? r % a.G : 0);
     const uint16_t* src = qp + ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * D;
@@ -591,163 +675,330 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_kernel(AttnArgs a) {
     for (int w = 0; w < 4; ++w) anc[rg][w] = (rv && w < a.W) ? ab[w] : 0u;
   }
 
-  float m_run[RG], l_run[RG];
-  f32x4 o[RG][NDB];
+  // m_run: reference max per row (log2 units); muse: m_run, or 0 while no key
+  // was seen; lacc: row sums of the weights (every element holds the sum)
+  float m_run[RG], muse[RG];
+  f32x4 o[RG][NDB], lacc[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     m_run[rg] = -INFINITY;
-    l_run[rg] = 0.f;
+    muse[rg] = 0.f;
+    lacc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < NDB; ++d) o[rg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  const int ntiles = (c.k_end - c.k_beg + KT - 1) / KT;
+  bf16x8 ones;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntiles) load_tile(c.k_beg + s * KT, s);
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = c.k_beg + t * KT;
-    const int later = min(STAGES - 2, ntiles - 1 - t);
-    wait_tile<LPT, STAGES>(later);
-    lds_barrier();  // tile t visible to all waves; stage of tile t-1 free
-    if (t + STAGES - 1 < ntiles) load_tile(t0 + (STAGES - 1) * KT, (t + STAGES - 1) % STAGES);
-    const char* kb_base = smem + (t % STAGES) * STAGE;
-    const char* vb_base = kb_base + KT * ROWB;
-
-    // scores, transposed: lane holds S^T[key = kb*16 + 4*lq + i][row = lr]
-    f32x4 s[RG][NKB];
+  // per-lane LDS byte offsets inside a slot; the slot base and the second
+  // 16-row half are immediates (swz is the same for rows r and r + 16)
+  uint32_t koff[NC], voff[NDB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+  for (int k = 0; k < NC; ++k) koff[k] = lr * ROWB + (((4 * k + lq) ^ swz(lr)) << 4);
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    const int row0 = 4 * lq + (lr >> 2);
+    const int chunk = 2 * d + ((lr & 3) >> 1);
+    voff[d] = TILEB + row0 * ROWB + ((chunk ^ swz(row0)) << 4) + ((lr & 1) << 3);
+  }
+
+  // S^T of a tile: lane holds S^T[key = kb*16 + 4*lq + i][row = lr]
+  auto scores = [&](f32x4 (&s)[RG][NKB], int j) {
+    const char* kb_base = smem + (j % NSLOT) * SLOT;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = kb * 16 + lr;
-      const char* rp = kb_base + row * ROWB;
-      const int sw = swz(row);
 #pragma unroll
-      for (int k = 0; k < NC; ++k) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp + (((4 * k + lq) ^ sw) << 4));
+    for (int k = 0; k < NC; ++k) {
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)  // idle row groups hold zero queries
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 16 + lr;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb_base + row * ROWB + (((4 * k + lq) ^ swz(row)) << 4));
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
           s[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][k], s[rg][kb], 0, 0, 0);
       }
     }
-
-    const bool full = (t0 + KT <= c.k_end) && (t0 + KT <= c.l_b);
-    bf16x8 pf[RG][NST];
+  };
+  // masks of a tile that reaches into the scratch rows or past the chunk end
+  auto mask = [&](f32x4 (&s)[RG][NKB], int j) {
+    const int t0 = k_beg + j * KT;
+    if (t0 + KT <= k_end && t0 + KT <= l_b) return;
+    // keeps the compiler from computing the masks for every tile and
+    // selecting afterwards; only the last tiles of an item take this path
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      if (!act[rg]) {
-#pragma unroll
-        for (int st = 0; st < NST; ++st) pf[rg][st] = bf16x8{};
-        continue;
-      }
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = key_visible(anc[rg], t0 + kb * 16 + 4 * lq + i, c.l_b, c.k_end);
-            s[rg][kb][i] = ok ? s[rg][kb][i] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[rg][kb][0], s[rg][kb][1]), fmaxf(s[rg][kb][2], s[rg][kb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy rescaling: a row's reference max moves only when the tile max
-      // exceeds it by more than kLazy (log2 units), so p <= 2^kLazy and the
-      // accumulators are rescaled rarely; the final normalisation is exact.
-      const float mt = mx * scale;
-      if (__ballot(mt > m_run[rg] + kLazy)) {
-        const float mnew = mt > m_run[rg] + kLazy ? mt : m_run[rg];
-        const float alpha = m_run[rg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - mnew);
-        l_run[rg] *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) o[rg][d] *= alpha;
-        m_run[rg] = mnew;
-      }
-      const float muse = m_run[rg] == -INFINITY ? 0.f : m_run[rg];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[rg][kb][i], scale, -muse));
-          lsum += p;
-          pf[rg][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
+          const bool ok = key_visible(anc[rg], t0 + kb * 16 + 4 * lq + i, l_b, k_end);
+          s[rg][kb][i] = ok ? s[rg][kb][i] : -INFINITY;
         }
-      }
-      l_run[rg] += lsum;
+  };
+  // Turns the scores of a tile into exponents x = s*scale - m (log2 units)
+  // and applies lazy rescaling: the reference max m of a row moves only when
+  // the tile holds a score above m + kLazy, so p = 2^x <= 2^kLazy.  The test
+  // uses each lane's own maximum (fma results, so max needs no NaN quieting);
+  // only a tile that moves some row's max takes the cross-lane path.
+  auto exponents = [&](f32x4 (&s)[RG][NKB]) {
+    bool need = false;
+    float lmax[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[rg][kb][i] = fmaf(s[rg][kb][i], scale, -muse[rg]);
+      float mx = fmaxf(fmaxf(s[rg][0][0], s[rg][0][1]), fmaxf(s[rg][0][2], s[rg][0][3]));
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[rg][kb][0], s[rg][kb][1]), fmaxf(s[rg][kb][2], s[rg][kb][3])));
+      lmax[rg] = mx;
+      need |= mx > (m_run[rg] == -INFINITY ? -INFINITY : kLazy);
     }
+    if (__ballot(need)) {
+      asm volatile("" ::: "memory");  // a real branch: taken for few tiles
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const float mt = quad_group_max(lmax[rg]) + muse[rg];   // the row's scaled max
+        const bool up = m_run[rg] == -INFINITY ? mt > -INFINITY : mt > m_run[rg] + kLazy;
+        if (!up) continue;  // uniform over the row's four lanes
+        const float alpha = m_run[rg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - mt);
+        lacc[rg] *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[rg][d] *= alpha;
+        const float delta = muse[rg] - mt;
+        m_run[rg] = mt;
+        muse[rg] = mt;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[rg][kb] += delta;
+      }
+    }
+  };
+  auto probs = [&](const f32x4 (&x)[RG][NKB], bf16x8 (&pf)[RG]) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pf[rg][kb * 4 + i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[rg][kb][i]));
+  };
+  // O^T[dv][row] += V^T[dv][keys] P^T[keys][row]; the key order inside the
+  // 32-key step (16*(e/4) + 4*lq + e%4 for element e) matches the scores'
+  auto values = [&](const bf16x8 (&pf)[RG], int j) {
+    const char* vb_base = smem + (j % NSLOT) * SLOT + TILEB;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int chunk = 2 * d + ((lr & 3) >> 1);
+      const int boff = (lr & 1) << 3;
+      const int row0 = 4 * lq + (lr >> 2);
+      const int row1 = row0 + 16;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          TSV_LDS4(vb_base + row0 * ROWB + ((chunk ^ swz(row0)) << 4) + boff));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          TSV_LDS4(vb_base + row1 * ROWB + ((chunk ^ swz(row1)) << 4) + boff));
+      union {
+        s16x4 h[2];
+        bf16x8 v;
+      } vf;
+      vf.h[0] = lo;
+      vf.h[1] = hi;
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        o[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rg], o[rg][d], 0, 0, 0);
+    }
+    // row sums of the same bf16 weights: every output row of ones * P^T
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      lacc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rg], lacc[rg], 0, 0, 0);
+  };
 
-    // values: O^T[dv][row] += V^T[dv][keys] * P^T[keys][row]
+  f32x4 sc[RG][NKB], sn[RG][NKB];
+  bf16x8 pf[RG];
+  wait_later<LPT, NSLOT - 2>(min(NSLOT - 2, ntiles - 1));
+  lds_barrier();
+  scores(sc, 0);
+  mask(sc, 0);
+  exponents(sc);
+
+  // One step of the pipeline for tile t (t % NSLOT == J, a compile-time
+  // slot, so every LDS address below is a register plus an immediate).
+  auto step = [&](auto j_c, int t) {
+    constexpr int J = decltype(j_c)::value;
+    constexpr int SN = (J + 1) % NSLOT;  // slot of tile t+1
+    // tile t+1 resident; every wave is done with tile t-1, whose slot is refilled
+    wait_later<LPT, NSLOT - 3>(min(NSLOT - 3, ntiles - 2 - t));
+    lds_barrier();
+    if (t + NSLOT - 1 < ntiles) issue(IC<(J + NSLOT - 1) % NSLOT>{});
+    // The offsets are redefined here so that offset + slot constant is not
+    // hoisted out of the loop (one register per slot and read); inside the
+    // block the constant folds into the instruction's offset field.
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
+    for (int k = 0; k < NC; ++k) asm volatile("" : "+v"(koff[k]));
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const int chunk = 2 * d + ((lr & 3) >> 1);
-        const int boff = (lr & 1) << 3;
-        const int row0 = 32 * st + 4 * lq + (lr >> 2);
-        const int row1 = row0 + 16;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TSV_LDS4(vb_base + row0 * ROWB + ((chunk ^ swz(row0)) << 4) + boff));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TSV_LDS4(vb_base + row1 * ROWB + ((chunk ^ swz(row1)) << 4) + boff));
-        union {
-          s16x4 h[2];
-          bf16x8 v;
-        } vf;
-        vf.h[0] = lo;
-        vf.h[1] = hi;
+    for (int d = 0; d < NDB; ++d) asm volatile("" : "+v"(voff[d]));
+    // one basic block: scores of tile t+1, weights and values of tile t
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) sn[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + SN * SLOT + kb * 16 * ROWB + koff[k]);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
-          o[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rg][st], o[rg][d], 0, 0, 0);
+          sn[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][k], sn[rg][kb], 0, 0, 0);
       }
+    probs(sc, pf);
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      union {
+        s16x4 h[2];
+        bf16x8 v;
+      } vf;
+      vf.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(smem + J * SLOT + voff[d]));
+      vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(smem + J * SLOT + 16 * ROWB + voff[d]));
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        o[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rg], o[rg][d], 0, 0, 0);
     }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      lacc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rg], lacc[rg], 0, 0, 0);
+    mask(sn, t + 1);
+    exponents(sn);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sc[rg][kb] = sn[rg][kb];
+  };
+
+  // four steps per trip, leaving after whichever step reaches the last tile
+  for (int t = 0; t + 1 < ntiles;) {
+    step(IC<0>{}, t);
+    if (++t + 1 >= ntiles) break;
+    step(IC<1>{}, t);
+    if (++t + 1 >= ntiles) break;
+    step(IC<2>{}, t);
+    if (++t + 1 >= ntiles) break;
+    step(IC<3>{}, t);
+    ++t;
+  }
+  probs(sc, pf);
+  values(pf, ntiles - 1);
+
+  // lane holds O^T[dv = d*16 + 4*lq + i][row = lr]; lacc[rg] holds the row sum
+  auto write_row = [&](int rg, const f32x4 (&acc)[NDB], float m, float l) {
+    const int r = c.rowb * RB + wave * RG * 16 + rg * 16 + lr;
+    if (r >= c.rows_b) return;
+    const int node = r / a.G, h = c.kvh * a.G + r % a.G;
+    const size_t orow = (static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + orow * D;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      union {
+        uint2 u;
+        __bf16 h4[4];
+      } pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(acc[d][i] * inv);
+      *reinterpret_cast<uint2*>(op + d * 16 + 4 * lq) = pk.u;
+    }
+    if (lq == 0 && a.lse) a.lse[orow] = (m + log2f(l)) * kLn2;
+  };
+
+  if (c.splits == 1) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) write_row(rg, o[rg], m_run[rg], lacc[rg][0]);
+    return;
   }
 
-  // lane holds O^T[dv = d*16 + 4*lq + i][row = lr]
+  // Split-K.  Each split publishes its rows (max, sum, accumulator) with
+  // device-coherent stores (relaxed atomics at agent scope: written through
+  // to the level shared by all XCDs), waits until they are complete, and then
+  // counts itself in.  The split that counts last reads the others' rows with
+  // device-coherent loads, issued only after it has seen the count, combines
+  // them and resets the counter for the next call.  Agent-scope fences would
+  // do the same by writing back and invalidating whole L2 caches, which costs
+  // far more than these few hundred coherent accesses.
+  // Layout private to this kernel, in lane order so that every store and
+  // load instruction covers 512 contiguous bytes: per (unit, split), per
+  // (wave, row group): accumulators [d][pair][lane] as float2, and the row
+  // (max, sum) pairs [lr] as float2.
+  const size_t item = static_cast<size_t>(unit) * a.S + c.split;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    if (!act[rg]) continue;
-    float lt = l_run[rg];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const int r_loc = wave * RG * 16 + rg * 16 + lr;
-    const int r = c.rowb * RB + r_loc;
-    if (r >= c.rows_b) continue;
-    if (c.splits == 1) {
-      const int node = r / a.G, h = c.kvh * a.G + r % a.G;
-      const size_t orow = (static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h;
-      uint16_t* op = static_cast<uint16_t*>(a.out) + orow * D;
-      const float inv = 1.0f / lt;
+    const int wr = wave * RG + rg;
+    uint64_t* pa = reinterpret_cast<uint64_t*>(a.part_acc + item * RB * D) + static_cast<size_t>(wr) * NDB * 2 * 64;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        union {
-          uint2 u;
-          __bf16 h4[4];
-        } pk;
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(o[rg][d][i] * inv);
-        *reinterpret_cast<uint2*>(op + d * 16 + 4 * lq) = pk.u;
+      for (int ip = 0; ip < 2; ++ip)
+        st_coherent2(pa + (d * 2 + ip) * 64 + lane, o[rg][d][2 * ip], o[rg][d][2 * ip + 1]);
+    if (lq == 0)
+      st_coherent2(reinterpret_cast<uint64_t*>(a.part_ml + item * RB * 2) + wr * 16 + lr, m_run[rg], lacc[rg][0]);
+  }
+  wait_vmcnt<0>();  // this thread's rows are complete at device scope
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             c.splits - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int wr = wave * RG + rg;
+    auto ml_of = [&](int s2) {
+      return ld_coherent2(reinterpret_cast<const uint64_t*>(a.part_ml + (static_cast<size_t>(unit) * a.S + s2) * RB * 2) +
+                          wr * 16 + lr);
+    };
+    float M = m_run[rg];
+    for (int s2 = 0; s2 < c.splits; ++s2) {
+      if (s2 == c.split) continue;
+      M = fmaxf(M, ml_of(s2).x);
+    }
+    // summed in split order whichever split arrived last, so that the bits
+    // do not depend on the arrival order
+    float L = 0.f;
+    f32x4 acc[NDB];
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < c.splits; ++s2) {
+      if (s2 == c.split) {
+        const float w = m_run[rg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - M);
+        L = fmaf(w, lacc[rg][0], L);
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[d][i] = fmaf(w, o[rg][d][i], acc[d][i]);
+        continue;
       }
-      if (lq == 0 && a.lse) a.lse[orow] = (m_run[rg] + log2f(lt)) * kLn2;
-    } else {
-      const size_t prow = static_cast<size_t>(blockIdx.x) * RB + r_loc;
-      float* pa = a.part_acc + prow * D;
+      const float2 ml = ml_of(s2);
+      const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+      L = fmaf(w, ml.y, L);
+      const uint64_t* pa = reinterpret_cast<const uint64_t*>(a.part_acc + (static_cast<size_t>(unit) * a.S + s2) * RB * D) +
+                           static_cast<size_t>(wr) * NDB * 2 * 64;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
-        *reinterpret_cast<float4*>(pa + d * 16 + 4 * lq) =
-            make_float4(o[rg][d][0], o[rg][d][1], o[rg][d][2], o[rg][d][3]);
-      if (lq == 0) {
-        a.part_ml[prow * 2 + 0] = m_run[rg];
-        a.part_ml[prow * 2 + 1] = lt;
-      }
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {
+          const float2 v = ld_coherent2(pa + (d * 2 + ip) * 64 + lane);
+          acc[d][2 * ip] = fmaf(w, v.x, acc[d][2 * ip]);
+          acc[d][2 * ip + 1] = fmaf(w, v.y, acc[d][2 * ip + 1]);
+        }
     }
+    write_row(rg, acc, M, L);
   }
+  if (tid == 0) a.counters[unit] = 0;
 }
 
 // --------------------------------------------------------------- VALU path
@@ -1035,12 +1286,39 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 AttnPlan attn_plan(const AttnShape& sh, bool aligned) {
   AttnPlan p;
   const bool bf = sh.dtype == TSV_BF16;
+  p.chunk = p.S = p.units = p.rbs = 0;
+  p.off_cnt = 0;
   if (bf && aligned && sh.d_qk == 128 && sh.d_v == 128) {
+    // One kernel: the key range of every unit (request, KV head, block of
+    // 128 rows) is cut into splits of `chunk` keys, sized from the capacity
+    // so that about two workgroups per compute unit exist; the launch has S
+    // slots per unit and a unit uses ceil(keys / chunk) of them.
     p.path = kPathMfmaGqa;
     p.RB = 128;
-    p.KT = 64;
-    p.min_chunk = 512;
+    p.KT = 32;
+    p.min_chunk = 256;
     p.target_items = 512;
+    const int G = sh.Hq / sh.Hkv;
+    p.rbs = (sh.N_max * G + p.RB - 1) / p.RB;
+    p.units = sh.B * sh.Hkv * p.rbs;
+    const int units_pad = (p.units + 7) / 8 * 8;
+    const long long keys_max = static_cast<long long>(sh.L_cap) + sh.N_max;
+    long long c = (static_cast<long long>(p.units) * keys_max + p.target_items - 1) / p.target_items;
+    if (c < p.min_chunk) c = p.min_chunk;
+    c = (c + p.KT - 1) / p.KT * p.KT;
+    p.S = static_cast<int>((keys_max + c - 1) / c);
+    p.chunk = p.min_chunk;  // the device cuts each unit's actual keys into S chunks of at least this
+    p.items_max = units_pad * p.S;
+    size_t off = 0;
+    p.off_cnt = off;
+    off = align_up(off + static_cast<size_t>(units_pad) * sizeof(int));
+    p.off_info = p.off_desc = off;
+    p.off_ml = off;
+    off = align_up(off + static_cast<size_t>(p.items_max) * p.RB * 2 * sizeof(float));
+    p.off_acc = off;
+    off = align_up(off + static_cast<size_t>(p.items_max) * p.RB * sh.d_v * sizeof(float));
+    p.bytes = off;
+    return p;
   } else if (bf && aligned && sh.d_qk == 576 && sh.d_v == 512) {
     p.path = kPathMfmaLatent;
     p.RB = 64;
@@ -1072,13 +1350,15 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype, hipStream_t s) {
+  if (path == kPathMfmaGqa) {
+    attn_gqa_pipe_kernel<4><<<dim3(a.items_max), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+  }
   attn_plan_kernel<<<dim3(1), dim3(kPlanThreads), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(a.items_max), block(256);
-  if (path == kPathMfmaGqa) {
-    attn_gqa_kernel<64, 2><<<grid, block, 0, s>>>(a);
-  } else if (path == kPathMfmaLatent) {
+  if (path == kPathMfmaLatent) {
     attn_mfma_kernel<576, 512, 1, 32, false><<<grid, block, 0, s>>>(a);
   } else if (dtype == TSV_F32) {
     attn_valu_kernel<float><<<grid, block, 0, s>>>(a);
@@ -1089,9 +1369,7 @@ hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype, hipStre
   if (e != hipSuccess) return e;
   const long rows = static_cast<long>(a.B) * a.N_max * a.Hq;
   dim3 g2(static_cast<unsigned>((rows + 3) / 4));
-  if (path == kPathMfmaGqa)
-    attn_combine_vec_kernel<128><<<g2, block, 0, s>>>(a);
-  else if (path == kPathMfmaLatent)
+  if (path == kPathMfmaLatent)
     attn_combine_vec_kernel<512><<<g2, block, 0, s>>>(a);
   else if (dtype == TSV_F32)
     attn_combine_kernel<float><<<g2, block, 0, s>>>(a);

@@ -75,6 +75,12 @@ struct AttnPlan {
   int min_chunk;     // smallest split of the key range
   int target_items;  // work items aimed for
   int items_max;     // bound on work items for any prefix lengths / node counts
+  // grouped-query path (one kernel, split-K combined by the last split):
+  int chunk;         // smallest split, in keys
+  int S;             // splits per unit at most
+  int units;         // request x KV head x row block
+  int rbs;           // row blocks per (request, KV head)
+  size_t off_cnt;    // arrival counters, one int per unit (zero between calls)
   size_t off_info, off_desc, off_ml, off_acc, bytes;
 };
 // `aligned` says whether pointers and strides allow 16-byte vector access.
@@ -99,6 +105,8 @@ struct AttnArgs {
   float* part_ml;   // [items_max][RB][2]
   float* part_acc;  // [items_max][RB][d_v]
   int RB, KT, items_max, target_items, min_chunk;
+  int* counters;    // [units] arrival counters (grouped-query path)
+  int chunk, S, units, rbs;
 };
 hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype,
                             hipStream_t s);
