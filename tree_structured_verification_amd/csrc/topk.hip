@@ -5,19 +5,21 @@
 // probable tokens of each position.  Order: probability descending, then
 // token id ascending.
 //
-// Design (HBM-bound scan, rows of ~10^5 probabilities):
-//   * each wavefront owns one contiguous segment of one row and keeps the
-//     best KS = 64 or 128 keys of that segment as a sorted list spread over
-//     its 64 lanes (one or two slots per lane);
-//   * a running threshold (the k-th best key so far) filters the stream: a
-//     lane tests the max of 16 loaded values against it, so after a short
-//     warm-up almost every 1 KiB load costs one compare and one ballot;
+// Design (HBM-bound scan, rows of ~10^5 probabilities), one workgroup per
+// row and one wavefront per contiguous segment of it:
+//   * a wavefront keeps the best KS = 64 or 128 keys of its segment as a
+//     sorted list spread over its 64 lanes (one or two slots per lane);
+//   * it filters the stream with the larger of its own k-th best value and
+//     the row's floor, the largest k-th best any wavefront of the row has
+//     published (an LDS atomic max): k elements of the row are at least that
+//     value, so nothing below it can reach the row's top k;
 //   * survivors are appended to a per-wave 64-entry LDS queue; a full queue
 //     is bitonic-sorted across lanes and merged into the list (elementwise
-//     max against the reversed queue, then a bitonic merge);
-//   * a second kernel merges the per-segment lists of a row the same way.
+//     max against the reversed queue, then a bitonic merge), with lane
+//     exchanges done by DPP and permlane swaps;
+//   * the first k keys of every list are finally sorted together in LDS.
 // Keys are unique (value, then lower index), so the result does not depend
-// on the segmentation or on the order elements are seen.
+// on the segmentation, on timing, or on the order elements are seen.
 
 #include "tsv_device.hpp"
 #include "tsv_internal.hpp"
@@ -25,18 +27,30 @@
 namespace tsv {
 namespace {
 
-__device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t y = shfl_xor_u64(x, j);
-      bool lower = (lane & j) == 0;
-      bool desc = (lane & k) == 0;
-      x = (lower == desc) ? umax64(x, y) : umin64(x, y);
-    }
-  }
+// One compare-exchange stage of a bitonic network over the 64 lanes: lanes
+// l and l ^ J swap so that the block of K lanes holding l ends up descending
+// (or ascending, for every other block when K < 64).
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t x, int lane) {
+  const uint64_t y = xor_lane_u64<J>(x);
+  const bool lower = (lane & J) == 0;
+  const bool desc = (lane & K) == 0;
+  return (lower == desc) ? umax64(x, y) : umin64(x, y);
+}
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_pass(uint64_t x, int lane) {
+  x = bitonic_stage<K, J>(x, lane);
+  if constexpr (J > 1) x = bitonic_pass<K, J / 2>(x, lane);
   return x;
+}
+// Sorts one key per lane, descending over lanes 0..63.
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
+  x = bitonic_pass<2, 1>(x, lane);
+  x = bitonic_pass<4, 2>(x, lane);
+  x = bitonic_pass<8, 4>(x, lane);
+  x = bitonic_pass<16, 8>(x, lane);
+  x = bitonic_pass<32, 16>(x, lane);
+  return bitonic_pass<64, 32>(x, lane);
 }
 
 template <int SLOTS>
@@ -53,7 +67,7 @@ struct WaveList {
   // Merge 64 keys sorted descending across lanes (one per lane) into the
   // descending list, keeping the best 64*SLOTS.
   __device__ void merge(uint64_t q) {
-    uint64_t qr = shfl_u64(q, 63 - lane);  // ascending
+    uint64_t qr = reverse_lanes_u64(q);  // ascending
     if (SLOTS == 1) {
       v[0] = umax64(v[0], qr);
     } else {
@@ -63,14 +77,16 @@ struct WaveList {
       v[SLOTS - 1] = umin64(a, b);
     }
 #pragma unroll
-    for (int j = 32; j > 0; j >>= 1) {
-      bool lower = (lane & j) == 0;
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        uint64_t o = shfl_xor_u64(v[s], j);
-        v[s] = lower ? umax64(v[s], o) : umin64(v[s], o);
-      }
-    }
+    for (int s = 0; s < SLOTS; ++s) v[s] = half_cleaner<32>(v[s]);
+  }
+
+  // Bitonic merge stages lane ^ J, ..., lane ^ 1 (descending result).
+  template <int J>
+  __device__ uint64_t half_cleaner(uint64_t x) const {
+    const uint64_t o = xor_lane_u64<J>(x);
+    x = (lane & J) == 0 ? umax64(x, o) : umin64(x, o);
+    if constexpr (J > 1) x = half_cleaner<J / 2>(x);
+    return x;
   }
 
   // Key at list position p (uniform p).
@@ -89,14 +105,16 @@ struct WaveSelect {
   int qcount;         // wave-uniform
   int k;
   uint64_t* queue;    // this wave's 64 LDS slots
+  uint32_t* floor_ord;  // the row's floor (ordered bits of a value, 0 = none), LDS
 
-  __device__ void init(int kk, uint64_t* q, int lane) {
+  __device__ void init(int kk, uint64_t* q, uint32_t* fl, int lane) {
     list.clear(lane);
     tau = 0;
     tau_v = -INFINITY;
     qcount = 0;
     k = kk;
     queue = q;
+    floor_ord = fl;
   }
 
   __device__ void flush() {
@@ -106,12 +124,24 @@ struct WaveSelect {
     x = sort64_desc(x, list.lane);
     list.merge(x);
     qcount = 0;
+    set_tau();
+  }
+
+  // tau = the list's k-th key; its value joins the row's floor
+  __device__ void set_tau() {
     tau = list.at(k - 1);
     if (tau != 0) {
-      uint32_t o = static_cast<uint32_t>(tau >> 32);
-      uint32_t bits = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-      tau_v = __uint_as_float(bits);
+      const uint32_t o = static_cast<uint32_t>(tau >> 32);
+      tau_v = __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+      if (list.lane == 0) atomicMax(floor_ord, o);
     }
+  }
+
+  // filter value: the larger of the own k-th best and the row's floor
+  __device__ float threshold() const {
+    const uint32_t o = __hip_atomic_load(floor_ord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const float f = o == 0 ? -INFINITY : __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+    return fmaxf(tau_v, f);
   }
 
   // Every lane offers one key (0 = nothing).
@@ -141,21 +171,27 @@ struct WaveSelect {
   }
 };
 
+constexpr int kMergeCap = 4096;  // segments * k, enforced by topk_plan
+constexpr int kMaxSegments = 16;
+
+// One workgroup per row, wavefront w scanning segment w.
 template <int SLOTS, bool VEC>
-__global__ __launch_bounds__(256) void topk_segment_kernel(
+__global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
     const float* __restrict__ x, int rows, int V, int k, int nseg, int seg_len,
-    uint64_t* __restrict__ seg_keys) {
-  __shared__ uint64_t queue[4][64];
+    int* __restrict__ out_idx, float* __restrict__ out_p) {
+  __shared__ uint64_t queue[kMaxSegments][64];
+  __shared__ uint64_t keys[kMergeCap];
+  __shared__ uint32_t floor_ord;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int task = blockIdx.x * 4 + wave;
-  if (task >= rows * nseg) return;  // whole wave leaves; no block barriers below
-  const int row = task / nseg, seg = task - row * nseg;
-  const int beg = seg * seg_len;
+  const int row = blockIdx.x;
+  if (threadIdx.x == 0) floor_ord = 0;
+  __syncthreads();
+  const int beg = wave * seg_len;
   const int end = min(V, beg + seg_len);
   const float* p = x + static_cast<size_t>(row) * V;
 
   WaveSelect<SLOTS> sel;
-  sel.init(k, queue[wave], lane);
+  sel.init(k, queue[wave], &floor_ord, lane);
 
   // Warm-up on the first 1024 elements: seed the list with every lane's best
   // (and, for lists of 128, second best) element in one sort, then offer
@@ -181,45 +217,60 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(
     }
     sel.list.v[0] = sort64_desc(k1, lane);
     if (SLOTS > 1) sel.list.merge(sort64_desc(k2, lane));
-    sel.tau = sel.list.at(k - 1);
-    if (sel.tau != 0) {
-      const uint32_t o = static_cast<uint32_t>(sel.tau >> 32);
-      sel.tau_v = __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-    }
+    sel.set_tau();
+    const float thr = sel.threshold();
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const bool seeded = (u == u1) || (SLOTS > 1 && u == u2);
-      const bool ok = e0[u] < end && !seeded && v[u] >= sel.tau_v;
+      const bool ok = e0[u] < end && !seeded && v[u] >= thr;
       if (__ballot(ok) == 0) continue;
       sel.offer(ok ? sel_key(v[u], e0[u]) : 0);
     }
   }
 
   if (VEC) {
-    for (int base = beg + 1024; base < end; base += 2048) {
-      float4 v[8];
+    // blocks of 8 float4 per lane (2048 elements); a group past the end
+    // re-reads the slice's last group and is ignored, so loads are
+    // unconditional; two blocks alternate so that one is in flight while the
+    // other is scanned
+    auto load_block = [&](float4 (&raw)[8], int base) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        int e = base + u * 256 + lane * 4;
-        if (e < end) v[u] = *reinterpret_cast<const float4*>(p + e);
-        else v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        const int e = min(base + u * 256 + lane * 4, end - 4);
+        raw[u] = *reinterpret_cast<const float4*>(p + e);
       }
-      float m = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
-      if (__ballot(m >= sel.tau_v) == 0) continue;
+    };
+    auto process = [&](const float4 (&v)[8], int base) {
+      float m4[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        int e = base + u * 256 + lane * 4;
-        bool ok = e < end;
-        if (__ballot(ok && fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)) >= sel.tau_v) == 0)
-          continue;
+        const int e = base + u * 256 + lane * 4;
+        const float m = vmax3(vmax3(v[u].x, v[u].y, v[u].z), v[u].w, v[u].w);
+        m4[u] = e < end ? m : -INFINITY;
+      }
+      const float m = vmax3(vmax3(m4[0], m4[1], m4[2]), vmax3(m4[3], m4[4], m4[5]), vmax3(m4[6], m4[7], m4[7]));
+      const float thr = sel.threshold();
+      if (__ballot(m >= thr) == 0) return;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = base + u * 256 + lane * 4;
+        const bool ok = e < end;
+        if (__ballot(ok && m4[u] >= thr) == 0) continue;
         sel.offer(ok ? sel_key(v[u].x, e) : 0);
         sel.offer(ok ? sel_key(v[u].y, e + 1) : 0);
         sel.offer(ok ? sel_key(v[u].z, e + 2) : 0);
         sel.offer(ok ? sel_key(v[u].w, e + 3) : 0);
       }
+    };
+    float4 b0[8], b1[8];
+    const int first = beg + 1024;
+    if (first < end) load_block(b0, first);
+    for (int base = first; base < end; base += 4096) {
+      if (base + 2048 < end) load_block(b1, base + 2048);
+      process(b0, base);
+      if (base + 2048 >= end) break;
+      if (base + 4096 < end) load_block(b0, base + 4096);
+      process(b1, base + 2048);
     }
   } else {
     for (int base = beg + 1024; base < end; base += 1024) {
@@ -232,7 +283,7 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(
       float m = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 16; ++u) m = fmaxf(m, v[u]);
-      if (__ballot(m >= sel.tau_v) == 0) continue;
+      if (__ballot(m >= sel.threshold()) == 0) continue;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         int e = base + u * 64 + lane;
@@ -241,36 +292,21 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(
     }
   }
   sel.finish();
-  uint64_t* out = seg_keys + static_cast<size_t>(task) * (64 * SLOTS);
+
+  // the first k keys of each list (only they can reach the row's top k),
+  // then one bitonic sort of all of them in LDS
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) out[s * 64 + lane] = sel.list.v[s];
-}
-
-// One workgroup per row: the first k keys of every segment list (only they
-// can reach the row's top k) are sorted descending in LDS with a bitonic
-// network; the first k are the row's top-k.
-constexpr int kMergeCap = 4096;  // nseg * k, enforced by topk_plan
-
-__global__ __launch_bounds__(256) void topk_merge_kernel(
-    const float* __restrict__ x, int rows, int V, int k, int nseg, int ks,
-    const uint64_t* __restrict__ seg_keys, int* __restrict__ out_idx,
-    float* __restrict__ out_p) {
-  __shared__ uint64_t keys[kMergeCap];
-  const int row = blockIdx.x;
-  const int t = threadIdx.x;
+  for (int s2 = 0; s2 < SLOTS; ++s2)
+    if (s2 * 64 + lane < k) keys[wave * k + s2 * 64 + lane] = sel.list.v[s2];
   const int n = nseg * k;
   int P = 1;
   while (P < n) P <<= 1;
-  const uint64_t* src = seg_keys + static_cast<size_t>(row) * nseg * ks;
-  for (int i = t; i < P; i += 256) {
-    uint64_t v = 0;
-    if (i < n) v = src[(i / k) * ks + (i % k)];
-    keys[i] = v;
-  }
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int i = n + t; i < P; i += nt) keys[i] = 0;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < P / 2; i += 256) {
+      for (int i = t; i < P / 2; i += nt) {
         const int lo = 2 * i - (i & (stride - 1));   // lower index of the pair
         const int hi = lo + stride;
         const bool desc = (lo & size) == 0;
@@ -283,14 +319,14 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(
       __syncthreads();
     }
   }
-  for (int pos = t; pos < k; pos += 256) {
+  for (int pos = t; pos < k; pos += nt) {
     const uint64_t key = keys[pos];
     // every row holds V >= k elements, so the first k slots are filled;
     // the guard keeps an impossible empty slot inside the row
     const uint32_t idx = key ? sel_key_index(key) : 0u;
     out_idx[static_cast<size_t>(row) * k + pos] = static_cast<int>(idx);
     // re-read the element so the stored probability keeps its exact bits
-    out_p[static_cast<size_t>(row) * k + pos] = x[static_cast<size_t>(row) * V + idx];
+    out_p[static_cast<size_t>(row) * k + pos] = p[idx];
   }
 }
 
@@ -303,10 +339,12 @@ TopkPlan topk_plan(int rows, int V, int k) {
   p.k = k;
   p.slots = k <= 64 ? 1 : 2;
   p.vec = (V % 4) == 0;
-  int want = (kScanWaves + rows - 1) / rows;
-  int most = V / 4096 > 1 ? V / 4096 : 1;  // segments of at least ~4k elements
+  // segments of at least ~8k elements, at most kMaxSegments per row, and
+  // segments * k within the merge buffer
+  int most = kMaxSegments;
   if (most > kMergeCap / k) most = kMergeCap / k;
-  int nseg = want < most ? want : most;
+  int nseg = (V + 8191) / 8192;
+  if (nseg > most) nseg = most;
   if (nseg < 1) nseg = 1;
   int len = (V + nseg - 1) / nseg;
   len = (len + 1023) / 2048 * 2048 + 1024;  // one warm-up block of 1024, then steps of 2048
@@ -315,29 +353,22 @@ TopkPlan topk_plan(int rows, int V, int k) {
   return p;
 }
 
-size_t topk_ws_bytes(const TopkPlan& p) {
-  return static_cast<size_t>(p.rows) * p.nseg * 64 * p.slots * sizeof(uint64_t);
-}
+size_t topk_ws_bytes(const TopkPlan&) { return 0; }
 
-hipError_t launch_topk(const float* x, const TopkPlan& p, uint64_t* seg_keys,
-                       int* out_idx, float* out_p, hipStream_t s) {
-  int tasks = p.rows * p.nseg;
-  dim3 grid((tasks + 3) / 4), block(256);
+hipError_t launch_topk(const float* x, const TopkPlan& p, uint64_t*, int* out_idx, float* out_p,
+                       hipStream_t s) {
+  dim3 grid(p.rows), block(64 * p.nseg);
   if (p.slots == 1) {
     if (p.vec)
-      topk_segment_kernel<1, true><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, seg_keys);
+      topk_row_kernel<1, true><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
     else
-      topk_segment_kernel<1, false><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, seg_keys);
+      topk_row_kernel<1, false><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
   } else {
     if (p.vec)
-      topk_segment_kernel<2, true><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, seg_keys);
+      topk_row_kernel<2, true><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
     else
-      topk_segment_kernel<2, false><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, seg_keys);
+      topk_row_kernel<2, false><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  topk_merge_kernel<<<dim3(p.rows), block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, 64 * p.slots,
-                                                   seg_keys, out_idx, out_p);
   return hipGetLastError();
 }
 

@@ -21,7 +21,6 @@
 namespace tsv {
 namespace {
 
-constexpr int kFrontierSlots = 5;  // 64 * 5 >= 1 + 2 * 128 entries
 constexpr int kMaxTopkTable = 4096;
 
 __device__ __forceinline__ uint64_t frontier_key(float score, int depth, int parent, int rank) {
@@ -39,6 +38,9 @@ __device__ __forceinline__ double round_cost(const tsv_cost& c, int n, double l)
   return __dadd_rn(c.c_d, v);
 }
 
+// SLOTS frontier entries per lane; the frontier never holds more than
+// 1 + 2 * cap entries, so 64 * SLOTS > 2 * cap suffices.
+template <int SLOTS>
 __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   __shared__ float s_p[kMaxTopkTable];
   __shared__ int s_i[kMaxTopkTable];
@@ -49,19 +51,35 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   const int lane = threadIdx.x;
   const int gk = a.gamma * a.k;
   const size_t tbase = static_cast<size_t>(b) * gk;
-  for (int e = lane; e < gk; e += 64) {
-    s_p[e] = a.tk_p[tbase + e];
-    s_i[e] = a.tk_idx[tbase + e];
+  // the table in batches of 8 loads per lane, all in flight together
+  for (int e0 = 0; e0 < gk; e0 += 8 * 64) {
+    float p[8];
+    int ix[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * 64 + lane;
+      p[u] = e < gk ? a.tk_p[tbase + e] : 0.f;
+      ix[u] = e < gk ? a.tk_idx[tbase + e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * 64 + lane;
+      if (e < gk) {
+        s_p[e] = p[u];
+        s_i[e] = ix[u];
+      }
+    }
   }
   __syncthreads();
 
   // Frontier slot = 64-bit order key split in (hi = ordered score bits,
   // lo = depth/parent/rank fields, 0 = empty) plus the entry's exact score
   // and its parent's score, so a pop reads everything from the winner lane.
-  uint32_t fhi[kFrontierSlots], flo[kFrontierSlots];
-  float fsc[kFrontierSlots], fps[kFrontierSlots];
+  // Updates are selects (no lane-dependent branches).
+  uint32_t fhi[SLOTS], flo[SLOTS];
+  float fsc[SLOTS], fps[SLOTS];
 #pragma unroll
-  for (int s = 0; s < kFrontierSlots; ++s) {
+  for (int s = 0; s < SLOTS; ++s) {
     fhi[s] = 0;
     flo[s] = 0;
     fsc[s] = 0.f;
@@ -70,15 +88,17 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   int cnt = 0;
   auto push = [&](float score, float parent_score, int depth, int parent, int rank) {
     const uint64_t key = frontier_key(score, depth, parent, rank);
-    const int L = cnt & 63, S = cnt >> 6;
+    const uint32_t kh = static_cast<uint32_t>(key >> 32), kl = static_cast<uint32_t>(key);
+    const bool mine = lane == (cnt & 63);
+    const int S = cnt >> 6;
 #pragma unroll
-    for (int s = 0; s < kFrontierSlots; ++s)
-      if (s == S && lane == L) {
-        fhi[s] = static_cast<uint32_t>(key >> 32);
-        flo[s] = static_cast<uint32_t>(key);
-        fsc[s] = score;
-        fps[s] = parent_score;
-      }
+    for (int s = 0; s < SLOTS; ++s) {
+      const bool w = mine && s == S;
+      fhi[s] = w ? kh : fhi[s];
+      flo[s] = w ? kl : flo[s];
+      fsc[s] = w ? score : fsc[s];
+      fps[s] = w ? parent_score : fps[s];
+    }
     ++cnt;
   };
 
@@ -92,14 +112,17 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   int m = 0;
   while (m < a.cap) {
     // best slot of this lane (hi, then lo)
-    uint32_t bh = 0, bl = 0;
+    uint32_t bh = fhi[0], bl = flo[0];
     int bs = 0;
+    float bsc = fsc[0], bps = fps[0];
 #pragma unroll
-    for (int s = 0; s < kFrontierSlots; ++s) {
+    for (int s = 1; s < SLOTS; ++s) {
       const bool better = fhi[s] > bh || (fhi[s] == bh && flo[s] > bl);
       bh = better ? fhi[s] : bh;
       bl = better ? flo[s] : bl;
       bs = better ? s : bs;
+      bsc = better ? fsc[s] : bsc;
+      bps = better ? fps[s] : bps;
     }
     const uint32_t wh = wave_max_u32(bh);
     if (wh == 0) break;  // every candidate taken
@@ -116,15 +139,8 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     const int rank = 127 - static_cast<int>(wl & 127);
     const int par = 255 - static_cast<int>((wl >> 7) & 255) - 1;
     const int dep = 63 - static_cast<int>((wl >> 15) & 63) + 1;
-    float sc_l = 0.f, ps_l = 0.f;
-#pragma unroll
-    for (int s = 0; s < kFrontierSlots; ++s)
-      if (s == wslot) {
-        sc_l = fsc[s];
-        ps_l = fps[s];
-      }
-    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_l), wlane));
-    const float ps = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps_l), wlane));
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsc), wlane));
+    const float ps = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bps), wlane));
     if (a.adaptive) {
       const double phi2 = __dadd_rn(phi, static_cast<double>(sc));
       const double th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, m + 1, l));
@@ -139,11 +155,11 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       n_sc[m] = sc;
     }
 #pragma unroll
-    for (int s = 0; s < kFrontierSlots; ++s)
-      if (lane == wlane && s == wslot) {
-        fhi[s] = 0;
-        flo[s] = 0;
-      }
+    for (int s = 0; s < SLOTS; ++s) {
+      const bool w = lane == wlane && s == wslot;
+      fhi[s] = w ? 0u : fhi[s];
+      flo[s] = w ? 0u : flo[s];
+    }
     const float q_sib = rank + 1 < a.k ? s_p[(dep - 1) * a.k + rank + 1] : 0.f;
     const float q_kid = dep < a.gamma ? s_p[dep * a.k] : 0.f;
     if (rank + 1 < a.k) push(__fmul_rn(ps, q_sib), ps, dep, par, rank + 1);
@@ -186,7 +202,16 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 }  // namespace
 
 hipError_t launch_best_first(const TreeArgs& a, hipStream_t s) {
-  best_first_kernel<<<dim3(a.B), dim3(64), 0, s>>>(a);
+  // frontier entries: at most 1 + 2 * cap (each pop adds two, removes one)
+  const int need = 1 + 2 * a.cap;
+  if (need <= 64)
+    best_first_kernel<1><<<dim3(a.B), dim3(64), 0, s>>>(a);
+  else if (need <= 128)
+    best_first_kernel<2><<<dim3(a.B), dim3(64), 0, s>>>(a);
+  else if (need <= 192)
+    best_first_kernel<3><<<dim3(a.B), dim3(64), 0, s>>>(a);
+  else
+    best_first_kernel<5><<<dim3(a.B), dim3(64), 0, s>>>(a);
   return hipGetLastError();
 }
 

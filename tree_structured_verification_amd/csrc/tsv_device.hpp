@@ -49,14 +49,6 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
   uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
-}
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
@@ -76,6 +68,72 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
   const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
   return umax32(umax32(r0, r1), umax32(r2, r3));
+}
+
+// Value of lane (lane ^ J), J in {1, 2, 4, 8, 16, 32}, with VALU lane
+// operations only (DPP within 16-lane rows, permlane swaps across rows); the
+// whole wavefront must be active.
+//   row_ror:N gives lane i the value of lane (i - N) mod 16 of its row;
+//   permlane16/32_swap return (value of the lower lane of the pair, value of
+//   the upper lane) in every lane of the pair.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v) {
+  if constexpr (J == 1) {
+    return dpp_u32<0xB1>(v);   // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return dpp_u32<0x4E>(v);   // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    // Two writes with complementary bank masks (bank = lanes 4b..4b+3 of a
+    // row): banks 0 and 2 take lane i + 4 (row_ror:12), banks 1 and 3 take
+    // lane i - 4 (row_ror:4).  No lane-dependent select, which the compiler
+    // may turn into EXEC-masked branches around the DPP moves (a DPP move
+    // then reads inactive lanes and returns its old value).
+    const int t = __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x12C, 0xF, 0x5, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, static_cast<int>(v), 0x124, 0xF, 0xA, false));
+  } else if constexpr (J == 8) {
+    return dpp_u32<0x128>(v);  // row_ror:8
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() & 32) ? r[0] : r[1];
+  }
+}
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
+  const uint32_t lo = xor_lane_u32<J>(static_cast<uint32_t>(v));
+  const uint32_t hi = xor_lane_u32<J>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+// Value of lane 63 - lane: mirror inside the row (lane ^ 15), then lane ^ 16
+// and lane ^ 32.
+__device__ __forceinline__ uint64_t reverse_lanes_u64(uint64_t v) {
+  uint32_t lo = dpp_u32<0x140>(static_cast<uint32_t>(v));   // row_mirror
+  uint32_t hi = dpp_u32<0x140>(static_cast<uint32_t>(v >> 32));
+  lo = xor_lane_u32<32>(xor_lane_u32<16>(lo));
+  hi = xor_lane_u32<32>(xor_lane_u32<16>(hi));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// max(a, b, c) of finite floats in one instruction.  Written as asm because
+// the compiler quiets signalling NaNs of loaded values before fmaxf (one
+// extra instruction per value); inputs here are finite by contract.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Wave-wide maximum of a 64-bit key (every lane gets it).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, xor_lane_u64<32>(v));
+  v = umax64(v, xor_lane_u64<16>(v));
+  v = umax64(v, xor_lane_u64<8>(v));
+  v = umax64(v, xor_lane_u64<4>(v));
+  v = umax64(v, xor_lane_u64<2>(v));
+  return umax64(v, xor_lane_u64<1>(v));
 }
 
 // Orders LDS traffic of one wavefront around a point where lanes exchange

@@ -17,24 +17,23 @@ namespace tsv {
 namespace {
 
 template <typename T>
-struct Vec16;  // 16 bytes of T
+struct Vec16;  // 16 bytes of T, widened to fp32
 template <>
 struct Vec16<float> {
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* out) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  __device__ static void widen(const uint4& v, float* out) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
   }
   __device__ static float one(const float* p) { return *p; }
 };
 template <>
 struct Vec16<uint16_t> {
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* out) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  __device__ static void widen(const uint4& v, float* out) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {  // exact widening of the two halves
       out[2 * i] = __uint_as_float(w[i] << 16);
       out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
@@ -42,6 +41,12 @@ struct Vec16<uint16_t> {
   __device__ static float one(const uint16_t* p) { return bf16_to_f32(*p); }
 };
 
+// One wavefront per (verified row, segment): the first maximum of the slice.
+// Vector path: a lane visits its 16-byte groups in increasing index order and
+// keeps only its running maximum and the first group where that maximum rose
+// (strict comparison, so ties stay with the earlier group); the first element
+// of that group equal to the maximum is found once at the end.  Ties across
+// lanes are settled by the key (lower index).
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void argmax_segment_kernel(
     const T* __restrict__ logits, int B, int N_max, int V, int nseg, int seg_len,
@@ -58,34 +63,53 @@ __global__ __launch_bounds__(256) void argmax_segment_kernel(
   const int end = min(V, beg + seg_len);
   const T* p = logits + static_cast<size_t>(row) * V;
 
-  // each lane visits its elements in increasing index order and keeps the
-  // first maximum; ties across lanes are settled by the key (lower index)
   float bv = -INFINITY;
   int bi = -1;
   if (VEC) {
     constexpr int N = Vec16<T>::N;
     constexpr int STEP = 64 * N;
-    for (int base = beg; base < end; base += 8 * STEP) {
-      float v[8][N];
+    constexpr int BLK = 8 * STEP;  // elements per block of 8 loads per lane
+    int bg = -1;  // first element of the group holding this lane's maximum
+    // groups lie wholly inside or outside [beg, end) (V and the segment
+    // bounds are multiples of N); a group past the end re-reads the last
+    // group of the slice and is then ignored, so every load is in bounds and
+    // unconditional
+    auto load_block = [&](uint4 (&raw)[8], int base) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        int e = base + u * STEP + lane * N;
-        if (e < end) Vec16<T>::load(p + e, v[u]);
-        else {
-#pragma unroll
-          for (int c = 0; c < N; ++c) v[u][c] = -INFINITY;
-        }
+        const int e = min(base + u * STEP + lane * N, end - N);
+        raw[u] = *reinterpret_cast<const uint4*>(p + e);
       }
+    };
+    auto process = [&](const uint4 (&raw)[8], int base) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        int e = base + u * STEP + lane * N;
+        float v[N];
+        Vec16<T>::widen(raw[u], v);
+        float m = vmax3(v[0], v[1], v[2]);
 #pragma unroll
-        for (int c = 0; c < N; ++c) {
-          bool better = (e + c < end) && (v[u][c] > bv || bi < 0);
-          bv = better ? v[u][c] : bv;
-          bi = better ? e + c : bi;
-        }
+        for (int c = 3; c < N; c += 2) m = vmax3(m, v[c], v[c + 1 < N ? c + 1 : c]);
+        const int e = base + u * STEP + lane * N;
+        const bool up = e < end && m > bv;
+        bv = up ? m : bv;
+        bg = up ? e : bg;
       }
+    };
+    // two register blocks in turn: one in flight while the other is scanned
+    uint4 b0[8], b1[8];
+    load_block(b0, beg);
+    for (int base = beg; base < end; base += 2 * BLK) {
+      if (base + BLK < end) load_block(b1, base + BLK);
+      process(b0, base);
+      if (base + BLK >= end) break;
+      if (base + 2 * BLK < end) load_block(b0, base + 2 * BLK);
+      process(b1, base + BLK);
+    }
+    if (bg >= 0) {
+      float w[N];
+      Vec16<T>::widen(*reinterpret_cast<const uint4*>(p + bg), w);
+#pragma unroll
+      for (int c = N - 1; c >= 0; --c) bi = (w[c] == bv) ? bg + c : bi;
     }
   } else {
     for (int e = beg + lane; e < end; e += 64) {
