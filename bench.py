@@ -15,8 +15,15 @@ every step does identical work.
 Reported: verified tree tokens/s = sum_b n_b * K / wall time of K steps
 (bracketed by device synchronisation), the attention entry point's achieved
 HBM bandwidth on its algorithmic bytes (HIP events around each call on the
-launch stream), and the CPU oracle timed on the same workload on this
-host's cores.
+launch stream; the entry point is a single kernel), the HBM bytes one such
+launch actually moves (from the committed counter summary, when it was taken
+on the current kernel source), and the CPU oracle timed on the same
+workload on this host's cores.
+
+    python bench.py --attention-only --copy-calibration 256 --steps 10 --warmup 2
+
+runs only the attention calls (after three 256 MiB device copies of known
+traffic), for the FETCH_SIZE / WRITE_SIZE counter runs.
 """
 
 import argparse
@@ -40,6 +47,31 @@ from workloads import attention_inputs, config, marginals, target_logits  # noqa
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = 2
 ROTATE = 3
+ATTN_SOURCE = os.path.join(ROOT, "tree_structured_verification_amd", "csrc", "attn.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tree_verify_attn_gqa_bf16_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on another version of the kernel
+    source (the summary records the source's SHA-256)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for ln in text.splitlines():
+        if ":" in ln and ln.strip().startswith("- "):
+            k, v = ln.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    digest = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if fields.get("attn_source_sha256") != digest:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def attention_bytes(cfg, prefix, n):
@@ -62,6 +94,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the workload the CPU oracle runs")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="run only the tree_verify_attn calls of the steps (for counter runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB three times between device buffers, so that "
+                         "byte counters can be scaled by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -69,6 +106,13 @@ def main():
         sys.exit(2)
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        nb = args.copy_calibration << 20
+        bufs = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(6)]
+        for i in range(3):
+            bufs[2 * i + 1].copy_(bufs[2 * i])
+        torch.cuda.synchronize()
+        del bufs
     cfg = config(WORKLOAD)
     print(f"[bench] generating workload {cfg.name} on {torch.cuda.get_device_name(dev)}",
           file=sys.stderr, flush=True)
@@ -150,6 +194,14 @@ def main():
         e[4].record(stream)
         return rc
 
+    if args.attention_only:
+        for s in range(W + K):
+            if L.tree_verify_attn(*all_args[s][1]) != 0:
+                raise RuntimeError("tree_verify_attn failed")
+        torch.cuda.synchronize()
+        print(json.dumps({"attention_only_calls": W + K}), flush=True)
+        return
+
     print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
     for s in range(W):
         if run(s) != 0:
@@ -203,7 +255,7 @@ def main():
                       "commit_path": round(float(np.mean(t_commit)), 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "tree_verify_attn",
+                     "traffic": measured_traffic(), "kernel": "tree_verify_attn",
                      "algorithmic_bytes": attn_bytes},
     }
 

@@ -129,6 +129,36 @@ def test_sibling_isolation_and_determinism():
 SAMPLES = {2: 48, 3: 12, 4: 40, 5: 8}
 
 
+def test_workspace_reuse_and_counter_reset():
+    """Split-K arrival counters live in the workspace: repeated calls on one
+    workspace give the same bits, and every call leaves the counters zero
+    (the workspace contract of tree_verify_attn)."""
+    rng = np.random.default_rng(11)
+    B, N_max, Hq, Hkv, d = 3, 32, 16, 4, 128
+    prefix = [6000, 2500, 700]
+    q, kc, vc, kt, vt, pl = _inputs(rng, B, N_max, 6016, Hq, Hkv, d, d, torch.bfloat16, prefix)
+    trees = _random_trees(rng, B, N_max, [32, 9, 20])
+    n = torch.tensor([t.n for t in trees], dtype=torch.int32, device=DEV)
+    anc = torch.from_numpy(np.stack([t.anc_bits for t in trees]).view(np.int32)).to(DEV)
+    nbytes = tsv.workspace_size(1, B, 1, 1, 1, N_max, 6016, Hq, Hkv, d, d, tsv.TSV_BF16)
+    ws = tsv.workspace(nbytes, DEV)
+    outs = []
+    for _ in range(3):
+        o, l = tsv.tree_verify_attn(q, kc, vc, kt, vt, pl, n, anc, Hkv, d, 0.09, ws=ws)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).clone(), l.view(torch.int32).clone()))
+        # the counters (one int per unit (request, KV head, block of 128 rows),
+        # padded to a multiple of 8, at the start of the workspace) are zero again
+        units = B * Hkv * ((N_max * (Hq // Hkv) + 127) // 128)
+        assert int(ws[:4 * ((units + 7) // 8 * 8)].count_nonzero()) == 0
+    for o, l in outs[1:]:   # rows past n_b are never written
+        for b, t in enumerate(trees):
+            assert torch.equal(o[b, :t.n], outs[0][0][b, :t.n])
+            assert torch.equal(l[b, :t.n], outs[0][1][b, :t.n])
+    check_attention(outs[0][0].view(torch.bfloat16), outs[0][1].view(torch.float32), q, kc, vc, kt, vt,
+                    prefix, trees, 0.09, TOL[torch.bfloat16], False, d)
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_workload(cid):
     """Full-size inputs, trees built by the oracle; every node checked for

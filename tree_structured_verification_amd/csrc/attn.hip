@@ -922,13 +922,16 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
   }
 
   // Split-K.  Each split publishes its rows (max, sum, accumulator) with
-  // device-coherent stores (relaxed atomics at agent scope: written through
-  // to the level shared by all XCDs), waits until they are complete, and then
-  // counts itself in.  The split that counts last reads the others' rows with
-  // device-coherent loads, issued only after it has seen the count, combines
-  // them and resets the counter for the next call.  Agent-scope fences would
-  // do the same by writing back and invalidating whole L2 caches, which costs
-  // far more than these few hundred coherent accesses.
+  // agent-scope atomic stores, which are written through the L2 to the level
+  // shared by all XCDs and acknowledged from there; once every thread has
+  // seen its acknowledgements (vmcnt 0) one thread counts the split in with
+  // an agent-scope atomic add.  The split that counts last acquires at agent
+  // scope (dropping stale cached lines), reads the others' rows with
+  // agent-scope atomic loads, combines them and resets the counter for the
+  // next call.  A release fence is left out on purpose: what it adds to the
+  // acknowledgement wait is a write-back of every dirty line of the L2, and
+  // the published rows never are dirty there; issued by every workgroup it
+  // costs more than the rest of the combine.
   // Layout private to this kernel, in lane order so that every store and
   // load instruction covers 512 contiguous bytes: per (unit, split), per
   // (wave, row group): accumulators [d][pair][lane] as float2, and the row
@@ -946,13 +949,14 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
     if (lq == 0)
       st_coherent2(reinterpret_cast<uint64_t*>(a.part_ml + item * RB * 2) + wr * 16 + lr, m_run[rg], lacc[rg][0]);
   }
-  wait_vmcnt<0>();  // this thread's rows are complete at device scope
+  wait_vmcnt<0>();  // this thread's row stores acknowledged at device scope
   __syncthreads();
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(a.counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              c.splits - 1;
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // no stale cached copy of the rows
 
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {

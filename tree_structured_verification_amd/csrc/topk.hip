@@ -27,6 +27,28 @@
 namespace tsv {
 namespace {
 
+// Inverse of ord_f32 for a non-zero ordered value.
+__device__ __forceinline__ float ord_value(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Sorts one value per lane descending within each row of 16 lanes.
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic16_pass(uint32_t x, int lane) {
+  const uint32_t y = xor_lane_u32<J>(x);
+  const bool lower = (lane & J) == 0;
+  const bool desc = (lane & K) == 0 || K == 16;
+  x = (lower == desc) ? umax32(x, y) : (x < y ? x : y);
+  if constexpr (J > 1) x = bitonic16_pass<K, J / 2>(x, lane);
+  return x;
+}
+__device__ __forceinline__ uint32_t sort16_desc_u32(uint32_t x, int lane) {
+  x = bitonic16_pass<2, 1>(x, lane);
+  x = bitonic16_pass<4, 2>(x, lane);
+  x = bitonic16_pass<8, 4>(x, lane);
+  return bitonic16_pass<16, 8>(x, lane);
+}
+
 // One compare-exchange stage of a bitonic network over the 64 lanes: lanes
 // l and l ^ J swap so that the block of K lanes holding l ends up descending
 // (or ascending, for every other block when K < 64).
@@ -105,16 +127,22 @@ struct WaveSelect {
   int qcount;         // wave-uniform
   int k;
   uint64_t* queue;    // this wave's 64 LDS slots
-  uint32_t* floor_ord;  // the row's floor (ordered bits of a value, 0 = none), LDS
+  uint32_t* pub;      // per segment: ordered bits of its m-th best value (LDS)
+  int wave, nseg, m, r;
 
-  __device__ void init(int kk, uint64_t* q, uint32_t* fl, int lane) {
+  __device__ void init(int kk, uint64_t* q, uint32_t* published, int w, int ns, int lane) {
     list.clear(lane);
     tau = 0;
     tau_v = -INFINITY;
     qcount = 0;
     k = kk;
     queue = q;
-    floor_ord = fl;
+    pub = published;
+    wave = w;
+    nseg = ns;
+    const int r0 = min(4, min(ns, kk));
+    m = (kk + r0 - 1) / r0;
+    r = (kk + m - 1) / m;  // <= r0 <= nseg
   }
 
   __device__ void flush() {
@@ -127,21 +155,25 @@ struct WaveSelect {
     set_tau();
   }
 
-  // tau = the list's k-th key; its value joins the row's floor
+  // tau = the list's k-th key; the value of its m-th key is published for
+  // the row's floor (values only grow, so an old one stays a valid bound)
   __device__ void set_tau() {
     tau = list.at(k - 1);
-    if (tau != 0) {
-      const uint32_t o = static_cast<uint32_t>(tau >> 32);
-      tau_v = __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-      if (list.lane == 0) atomicMax(floor_ord, o);
-    }
+    if (tau != 0) tau_v = ord_value(static_cast<uint32_t>(tau >> 32));
+    const uint32_t om = static_cast<uint32_t>(list.at(m - 1) >> 32);
+    if (list.lane == 0 && om != 0) pub[wave] = om;
   }
 
-  // filter value: the larger of the own k-th best and the row's floor
+  // Filter value: the larger of the own k-th best and the row's floor, the
+  // r-th largest published value: r segments each hold m >= k/r elements at
+  // or above it, so k elements of the row are, and nothing below it can
+  // reach the row's top k.  The published values are sorted across the
+  // first 16 lanes (0 = not yet published, so too few gives no floor).
   __device__ float threshold() const {
-    const uint32_t o = __hip_atomic_load(floor_ord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const float f = o == 0 ? -INFINITY : __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-    return fmaxf(tau_v, f);
+    uint32_t o = list.lane < nseg ? __hip_atomic_load(pub + list.lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
+    o = sort16_desc_u32(o, list.lane);
+    o = __builtin_amdgcn_readlane(o, r - 1);
+    return o == 0 ? tau_v : fmaxf(tau_v, ord_value(o));
   }
 
   // Every lane offers one key (0 = nothing).
@@ -181,17 +213,17 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
     int* __restrict__ out_idx, float* __restrict__ out_p) {
   __shared__ uint64_t queue[kMaxSegments][64];
   __shared__ uint64_t keys[kMergeCap];
-  __shared__ uint32_t floor_ord;
+  __shared__ uint32_t published[kMaxSegments];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x;
-  if (threadIdx.x == 0) floor_ord = 0;
+  if (threadIdx.x < kMaxSegments) published[threadIdx.x] = 0;
   __syncthreads();
   const int beg = wave * seg_len;
   const int end = min(V, beg + seg_len);
   const float* p = x + static_cast<size_t>(row) * V;
 
   WaveSelect<SLOTS> sel;
-  sel.init(k, queue[wave], &floor_ord, lane);
+  sel.init(k, queue[wave], published, wave, nseg, lane);
 
   // Warm-up on the first 1024 elements: seed the list with every lane's best
   // (and, for lists of 128, second best) element in one sort, then offer
