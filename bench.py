@@ -195,6 +195,8 @@ def main():
         return rc
 
     if args.attention_only:
+        if L.build_tree(*all_args[0][0]) != 0:   # the trees the attention reads
+            raise RuntimeError("build_tree failed")
         for s in range(W + K):
             if L.tree_verify_attn(*all_args[s][1]) != 0:
                 raise RuntimeError("tree_verify_attn failed")
