@@ -600,9 +600,11 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
   constexpr int SLOT = 2 * TILEB;
   constexpr int LPT = KT / 8;             // 1 KiB DMA blocks per thread per tile
   constexpr int NKB = KT / 16, NC = D / 32, NDB = D / 16;
-  static_assert(NSLOT == 4, "the unrolled steps assume a ring of four tiles");
+  static_assert(NSLOT == 4 || NSLOT == 5, "the unrolled steps assume a ring of four or five tiles");
   __shared__ __align__(1024) char smem[NSLOT * SLOT];
-  __shared__ int s_last;
+  // after the key loop the ring is free; its first word carries the
+  // last-split flag (two workgroups of five slots fill the CU's LDS)
+  int& s_last = *reinterpret_cast<int*>(smem);
 
   ItemCtx c;
   int unit;
@@ -655,6 +657,8 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
   issue(IC<0>{});
   if (1 < ntiles) issue(IC<1>{});
   if (2 < ntiles) issue(IC<2>{});
+  if constexpr (NSLOT == 5)
+    if (3 < ntiles) issue(IC<3>{});
 
   bf16x8 qf[RG][NC];
   uint32_t anc[RG][4];
@@ -880,7 +884,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
       for (int kb = 0; kb < NKB; ++kb) sc[rg][kb] = sn[rg][kb];
   };
 
-  // four steps per trip, leaving after whichever step reaches the last tile
+  // NSLOT steps per trip, leaving after whichever step reaches the last tile
   for (int t = 0; t + 1 < ntiles;) {
     step(IC<0>{}, t);
     if (++t + 1 >= ntiles) break;
@@ -889,6 +893,10 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
     step(IC<2>{}, t);
     if (++t + 1 >= ntiles) break;
     step(IC<3>{}, t);
+    if constexpr (NSLOT == 5) {
+      if (++t + 1 >= ntiles) break;
+      step(IC<4>{}, t);
+    }
     ++t;
   }
   probs(sc, pf);
@@ -1355,7 +1363,7 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned) {
 
 hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype, hipStream_t s) {
   if (path == kPathMfmaGqa) {
-    attn_gqa_pipe_kernel<4><<<dim3(a.items_max), dim3(256), 0, s>>>(a);
+    attn_gqa_pipe_kernel<5><<<dim3(a.items_max), dim3(256), 0, s>>>(a);
     return hipGetLastError();
   }
   attn_plan_kernel<<<dim3(1), dim3(kPlanThreads), 0, s>>>(a);
