@@ -59,6 +59,33 @@ def test_walk_small(dtype, V):
     _check_walk(g, np32(logits), trees, gamma)
 
 
+def test_walk_workspace_reuse():
+    """Calls on one workspace, with changing trees and logits, each match the
+    oracle (no state survives in the workspace)."""
+    B, gamma, k, N_max, V = 6, 5, 3, 20, 3001
+    ws = tsv.workspace(tsv.workspace_size(2, B, gamma, V, 1, N_max, dtype=tsv.TSV_BF16), DEV)
+    for call in range(3):
+        rng = np.random.default_rng(100 + call)
+        marg = rng.dirichlet(np.ones(10) * 0.5, size=(B, gamma)).astype(np.float32)
+        marg = np.concatenate([marg, np.zeros((B, gamma, V - 10), np.float32)], -1)
+        budgets = [int(x) for x in rng.integers(0, N_max + 1, size=B)]
+        trees = []
+        for b in range(B):
+            idx, p = oracle.topk_per_position(marg[b:b + 1], k)
+            trees.append(oracle.select_tree(idx[0], p[0], budgets[b], N_max))
+        lg = rng.normal(0, 1, size=(B, 1 + N_max, V)).astype(np.float32)
+        for b, t in enumerate(trees):
+            for r in range(1 + t.n):
+                kids = [j for j in range(t.n) if t.parent[j] == r - 1]
+                if kids and rng.random() < 0.8:
+                    lg[b, r, t.token[kids[rng.integers(len(kids))]]] = 9.0
+        st = _dev_tree(stack_trees(trees, N_max))
+        logits = torch.from_numpy(lg).to(torch.bfloat16).to(DEV)
+        g = tsv.accept_walk(logits, st["n_nodes"], st["parent"], st["token"], gamma, ws=ws)
+        torch.cuda.synchronize()
+        _check_walk(g, np32(logits), trees, gamma)
+
+
 def test_walk_dspark_cycle_chain():
     """Chain E F G under root D; the target agrees on E and F and prefers G*
     after F: two tokens accepted, then the correction."""
