@@ -35,6 +35,11 @@ def command(out: str = LIB, extra=()):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-fno-fast-math",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix instructions start in the VGPR form; the register allocator
+        # then moves the large accumulators into AGPRs.  Without it, a kernel
+        # allowed more than 256 registers puts every accumulator in AGPRs
+        # (the latent attention kernel's score tiles then no longer fit)
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-result",
         "-I", INCLUDE, "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],

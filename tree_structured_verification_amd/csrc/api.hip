@@ -61,8 +61,12 @@ bool attn_sizes_ok(int B, int N_max, int L_cap, int Hq, int Hkv, int d_qk, int d
 }
 
 size_t attn_bytes_any(const AttnShape& sh) {
-  size_t a = attn_plan(sh, true).bytes, b = attn_plan(sh, false).bytes;
-  return a > b ? a : b;
+  size_t m = 0;
+  for (int mode = 0; mode < 4; ++mode) {
+    const size_t x = attn_plan(sh, (mode & 1) != 0, (mode & 2) != 0).bytes;
+    m = x > m ? x : m;
+  }
+  return m;
 }
 
 size_t walk_bytes(int B, int N_max, int V, int dtype) {
@@ -178,7 +182,9 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                    aligned_to(k_tree, 16) && aligned_to(v_tree, 16) && aligned_to(out, 16) &&
                    (kv_row_stride * es) % 16 == 0;
   AttnShape sh{B, N_max, L_cap, Hq, Hkv, d_qk, d_v, dtype};
-  const AttnPlan P = attn_plan(sh, vec);
+  // a latent cache: one KV head whose value is the start of the key row
+  const bool shared = Hkv == 1 && v_cache == k_cache && v_tree == k_tree;
+  const AttnPlan P = attn_plan(sh, vec, shared);
   if (!ws || ws_bytes < P.bytes || !aligned_to(ws, kAlign)) return TSV_EWORKSPACE;
   char* w = static_cast<char*>(ws);
   AttnArgs a;

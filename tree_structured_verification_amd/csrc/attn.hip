@@ -174,253 +174,6 @@ __device__ __forceinline__ long key_row(const AttnArgs& a, const ItemCtx& c, int
   return (static_cast<long>(c.b) * a.N_max + (key - c.l_b)) * a.stride;
 }
 
-// --------------------------------------------------------------- MFMA path
-template <int DQK, int DV, int RG, int KT, bool PREFETCH>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int RB = 64 * RG;        // 4 waves x RG groups of 16 rows
-  constexpr int KSTR = DQK + 8;      // bf16 per K-tile row (padding vs bank conflicts)
-  constexpr int VSTR = KT / 2 + 2;   // dwords per transposed value row
-  constexpr int NC = DQK / 32;       // k-steps of the score product
-  constexpr int NKB = KT / 16;       // 16-key blocks per tile
-  constexpr int NDB = DV / 16;       // 16-wide value blocks
-  constexpr int NST = KT / 32;       // 32-key steps of the value product
-  constexpr int KCH = DQK / 8;       // 16-byte chunks per key row
-  constexpr int VCH = DV / 8;        // 16-byte chunks per value row
-  constexpr int KLD = KT * KCH / 256;         // K chunks per thread
-  constexpr int VLD = (KT / 2) * VCH / 256;   // value key-pair tasks per thread
-  static_assert(KT * KCH % 256 == 0 && (KT / 2) * VCH % 256 == 0, "tile split");
-  __shared__ __align__(16) uint16_t sK[KT * KSTR];
-  __shared__ __align__(16) uint32_t sV[DV * VSTR];
-
-  ItemCtx c;
-  if (!load_item(a, c)) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  // wave-uniform by construction; readfirstlane lets the compiler branch on
-  // it with scalar branches instead of EXEC-masked regions around the MFMAs
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, lq = lane >> 4;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
-  const uint16_t* kt = static_cast<const uint16_t*>(a.kt);
-  const uint16_t* vt = static_cast<const uint16_t*>(a.vt);
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-  const float scale = a.scale_log2;
-
-  bf16x8 qf[RG][NC];
-  uint32_t anc[RG][4];
-  bool act[RG];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int r_first = c.rowb * RB + wave * RG * 16 + rg * 16;
-    act[rg] = __builtin_amdgcn_readfirstlane(r_first < c.rows_b ? 1 : 0) != 0;
-    const int r = r_first + lr;
-    const bool rv = r < c.rows_b;
-    const int node = rv ? r / a.G : 0;
-    const int h = c.kvh * a.G + (rv ? r % a.G : 0);
-    const uint16_t* src = qp + ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * DQK;
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      if (rv) qf[rg][k] = *reinterpret_cast<const bf16x8*>(src + 32 * k + 8 * lq);
-      else qf[rg][k] = bf16x8{};
-    }
-    const unsigned* ab = a.anc + (static_cast<size_t>(c.b) * a.N_max + node) * a.W;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) anc[rg][w] = (rv && w < a.W) ? ab[w] : 0u;
-  }
-
-  float m_run[RG], l_run[RG];
-  f32x4 o[RG][NDB];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    m_run[rg] = -INFINITY;
-    l_run[rg] = 0.f;
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) o[rg][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  uint4 rk[KLD];
-  uint4 rv0[VLD], rv1[VLD];
-  auto fetch = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci / KCH, ch = ci % KCH;
-      const int kk = t0 + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kk < c.k_end) {
-        bool tr;
-        const long off = key_row(a, c, kk, &tr) + static_cast<long>(c.kvh) * DQK + 8 * ch;
-        v = *reinterpret_cast<const uint4*>((tr ? kt : kc) + off);
-      }
-      rk[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int vi = tid + 256 * i;
-      const int p = vi / VCH, ch = vi % VCH;
-      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-      const int k0 = t0 + 2 * p;
-      if (k0 < c.k_end) {
-        bool tr;
-        const long off = key_row(a, c, k0, &tr) + static_cast<long>(c.kvh) * DV + 8 * ch;
-        x0 = *reinterpret_cast<const uint4*>((tr ? vt : vc) + off);
-      }
-      if (k0 + 1 < c.k_end) {
-        bool tr;
-        const long off = key_row(a, c, k0 + 1, &tr) + static_cast<long>(c.kvh) * DV + 8 * ch;
-        x1 = *reinterpret_cast<const uint4*>((tr ? vt : vc) + off);
-      }
-      rv0[i] = x0;
-      rv1[i] = x1;
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int ci = tid + 256 * i;
-      const int key = ci / KCH, ch = ci % KCH;
-      *reinterpret_cast<uint4*>(&sK[key * KSTR + 8 * ch]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int vi = tid + 256 * i;
-      const int p = vi / VCH, ch = vi % VCH;
-      const uint32_t w0[4] = {rv0[i].x, rv0[i].y, rv0[i].z, rv0[i].w};
-      const uint32_t w1[4] = {rv1[i].x, rv1[i].y, rv1[i].z, rv1[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sV[(8 * ch + 2 * j) * VSTR + p] = (w0[j] & 0xFFFFu) | (w1[j] << 16);
-        sV[(8 * ch + 2 * j + 1) * VSTR + p] = (w0[j] >> 16) | (w1[j] & 0xFFFF0000u);
-      }
-    }
-  };
-
-  if (PREFETCH && c.k_beg < c.k_end) fetch(c.k_beg);
-  for (int t0 = c.k_beg; t0 < c.k_end; t0 += KT) {
-    __syncthreads();  // the previous tile is no longer read
-    if (!PREFETCH) fetch(t0);
-    stash();
-    __syncthreads();
-    if (PREFETCH && t0 + KT < c.k_end) fetch(t0 + KT);
-
-    // scores, transposed: lane holds S^T[key = kb*16 + 4*lq + i][row = lr]
-    f32x4 s[RG][NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < NC; ++k) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + lr) * KSTR + 32 * k + 8 * lq]);
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-          if (act[rg]) s[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][k], s[rg][kb], 0, 0, 0);
-      }
-    }
-
-    const bool full = (t0 + KT <= c.k_end) && (t0 + KT <= c.l_b);
-    bf16x8 pf[RG][NST];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      if (!act[rg]) continue;
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = t0 + kb * 16 + 4 * lq + i;
-            const bool ok = key_visible(anc[rg], key, c.l_b, c.k_end);
-            s[rg][kb][i] = ok ? s[rg][kb][i] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[rg][kb][0], s[rg][kb][1]), fmaxf(s[rg][kb][2], s[rg][kb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m_run[rg], mx * scale);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m_run[rg] - muse);
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(fmaf(s[rg][kb][i], scale, -muse));
-          lsum += p;
-          pf[rg][kb >> 1][(kb & 1) * 4 + i] = static_cast<__bf16>(p);
-        }
-      }
-      l_run[rg] = l_run[rg] * alpha + lsum;
-      m_run[rg] = mnew;
-      if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) o[rg][d] *= alpha;
-      }
-    }
-
-    // values: O^T[dv][row] += V^T[dv][keys] * P^T[keys][row]
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const uint32_t* vrow = &sV[(d * 16 + lr) * VSTR + 16 * st];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 2 * lq);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8 + 2 * lq);
-        union {
-          uint4 u;
-          bf16x8 v;
-        } vf;
-        vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-          if (act[rg]) o[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rg][st], o[rg][d], 0, 0, 0);
-      }
-    }
-  }
-
-  // lane holds O^T[dv = d*16 + 4*lq + i][row = lr]
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    if (!act[rg]) continue;
-    float lt = l_run[rg];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const int r_loc = wave * RG * 16 + rg * 16 + lr;
-    const int r = c.rowb * RB + r_loc;
-    if (r >= c.rows_b) continue;
-    if (c.splits == 1) {
-      const int node = r / a.G, h = c.kvh * a.G + r % a.G;
-      const size_t orow = (static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h;
-      uint16_t* op = static_cast<uint16_t*>(a.out) + orow * DV;
-      const float inv = 1.0f / lt;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        union {
-          uint2 u;
-          __bf16 h4[4];
-        } pk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(o[rg][d][i] * inv);
-        *reinterpret_cast<uint2*>(op + d * 16 + 4 * lq) = pk.u;
-      }
-      if (lq == 0 && a.lse) a.lse[orow] = (m_run[rg] + log2f(lt)) * kLn2;
-    } else {
-      const size_t prow = static_cast<size_t>(blockIdx.x) * RB + r_loc;
-      float* pa = a.part_acc + prow * DV;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-        *reinterpret_cast<float4*>(pa + d * 16 + 4 * lq) =
-            make_float4(o[rg][d][0], o[rg][d][1], o[rg][d][2], o[rg][d][3]);
-      if (lq == 0) {
-        a.part_ml[prow * 2 + 0] = m_run[rg];
-        a.part_ml[prow * 2 + 1] = lt;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------ grouped-query MFMA path
 // Grouped-query heads of width 128 (the common bf16 case): 128 query rows per
 // work item (4 waves x 2 groups of 16 rows), keys streamed in tiles of 32.
@@ -674,9 +427,6 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
       if (rv) qf[rg][k] = *reinterpret_cast<const bf16x8*>(src + 32 * k + 8 * lq);
       else qf[rg][k] = bf16x8{};
     }
-    const unsigned* ab = a.anc + (static_cast<size_t>(c.b) * a.N_max + node) * a.W;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) anc[rg][w] = (rv && w < a.W) ? ab[w] : 0u;
   }
 
   // m_run: reference max per row (log2 units); muse: m_run, or 0 while no key
@@ -1013,6 +763,394 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
   if (tid == 0) a.counters[unit] = 0;
 }
 
+// ------------------------------------------------------ latent MFMA path
+// One latent KV head shared by every query head: the key is the 576-wide
+// latent row, the value its first 512 columns (the cache is passed once, as
+// both key and value).  A work item is 128 query rows (node x head) of one
+// request and a chunk of its keys; 4 waves, one per SIMD.
+//
+// Division of work.  Wave w computes the scores of rows 32w..32w+31 for all
+// 32 keys of a tile (its queries stay in registers for the whole item) and
+// turns them into bf16 weights, which go to LDS in the operand layout of the
+// value product.  The value product is split by output column instead: wave
+// w accumulates O^T for columns 128w..128w+127 of all 128 rows, reading every
+// wave's weights.  This way one K tile in LDS feeds both products, each wave
+// holds a quarter of the 128 x 512 fp32 accumulator, and the LDS bytes read
+// per MFMA stay low enough for the matrix cores to stay busy.
+//
+// K tiles (32 keys x 1152 bytes) reach LDS by LDS-DMA, one 1 KiB block per
+// instruction, in a ring of three slots (one tile in flight while two are
+// read).  Inside a tile, 16-byte granule C (columns 8C..8C+7) of key k sits
+//   C < 64:  block 4*(k/4) + C/16, row k%4 of 256 bytes, granule (C%16)^s(k)
+//   C >= 64: block 32 + k/8,       row k%8 of 128 bytes, granule (C-64)^t(k)
+// with s a bijection of k%16 and t(k) = (k/2)%8.  Every score operand read
+// (16 keys of one granule per 16 lanes) and every transposed value read
+// (4 keys x 2 granules per 16 lanes) then touches distinct banks, and each
+// DMA block reads whole 256- or 128-byte runs of 4 or 8 key rows.
+//
+// Softmax per row is online with a lazy reference max (as in the grouped
+// path): the max moves only when a tile exceeds it by kLazy (log2 units),
+// decided without branches; a wave that moves any of its rows' max posts the
+// factors and a flag, and before the next value product every wave rescales
+// the accumulator rows concerned (a rare branch).
+constexpr int kLatQK = 576, kLatV = 512;
+constexpr int kLatTile = 32 * kLatQK * 2;        // bytes of one K tile
+constexpr int kLatSlots = 3;
+constexpr int kLatP = kLatSlots * kLatTile;      // weights, two buffers of 8 KiB
+constexpr int kLatAlpha = kLatP + 2 * 8192;      // rescale factors [2][16][8]
+constexpr int kLatFlag = kLatAlpha + 2 * 512;    // rescale flags [2][4]
+constexpr int kLatStat = kLatFlag + 32;          // final (max, sum) per row
+constexpr int kLatLds = kLatStat + 128 * 8;
+
+__device__ __forceinline__ int lat_s(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+__device__ __forceinline__ int lat_t(int k) { return (k >> 1) & 7; }
+
+// s_waitcnt vmcnt(0) lgkmcnt(0): this wave's DMA blocks and LDS writes done
+__device__ __forceinline__ void wait_all_mem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x70);
+  asm volatile("" ::: "memory");
+}
+
+// sum of v over the lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float quad_group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ bool latent_item(const AttnArgs& a, ItemCtx& c, int& item) {
+  // ids are dealt to the XCDs round robin; give each XCD a contiguous run of
+  // items, so that the row blocks of one request share that XCD's L2
+  const int total = a.info[4 * a.B + 1];
+  const int per = (total + 7) >> 3;
+  const int id = static_cast<int>(blockIdx.x);
+  const int pos = id >> 3;
+  item = (id & 7) * per + pos;
+  if (pos >= per || item >= total) return false;
+  const int4 d = a.desc[item];
+  c.b = d.x;
+  c.kvh = d.y;
+  c.rowb = d.z;
+  c.split = d.w;
+  const int chunk = a.info[4 * a.B];
+  c.splits = a.info[4 * c.b + 1];
+  c.l_b = a.info[4 * c.b + 3];
+  c.n_b = clampi(a.n_nodes[c.b], 0, a.N_max);
+  c.keys_b = c.l_b + c.n_b;
+  c.k_beg = c.split * chunk;
+  c.k_end = min(c.keys_b, c.k_beg + chunk);
+  c.rows_b = c.n_b * a.G;
+  return c.k_beg < c.k_end;
+}
+
+__global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
+  constexpr int KT = 32, RB = 128, NC = kLatQK / 32;
+  __shared__ __align__(1024) char smem[kLatLds];
+
+  ItemCtx c;
+  int item;
+  if (!latent_item(a, c, item)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const long rstride = a.stride * 2;
+  const float scale = a.scale_log2;
+  const char* kc_b = static_cast<const char*>(a.kc) + static_cast<long>(c.b) * a.L_cap * rstride;
+  const char* kt_b = static_cast<const char*>(a.kt) + static_cast<long>(c.b) * a.N_max * rstride;
+  const int k_beg = c.k_beg, k_end = c.k_end, l_b = c.l_b;
+  const int nt = (k_end - k_beg + KT - 1) / KT;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TSV_LDS(smem)));
+
+  // ---- DMA: wave w fills blocks 4*kg + w (kg = 0..7) and tail block 32 + w
+  // source offsets are recomputed at each issue from an opaque copy of the
+  // lane id (a few VALU operations) rather than held in registers
+  auto issue = [&](int j, uint32_t slot_lds) {
+    const int t0 = k_beg + j * KT;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int tkey = 8 * wave + (ln >> 3);
+    const int tC = 64 + ((ln & 7) ^ lat_t(tkey));
+    if (t0 + KT <= k_end && t0 + KT <= l_b) {
+      const char* tp = kc_b + static_cast<long>(t0) * rstride;
+#pragma unroll
+      for (int kg = 0; kg < 8; ++kg) {
+        const int key = 4 * (kg & 3) + (ln >> 4);
+        const int C = 16 * wave + ((ln & 15) ^ lat_s(key));
+        dma_1k(slot_lds + (kg * 4 + wave) * 1024, tp + (kg >> 2) * 16 * rstride,
+               static_cast<uint32_t>(key * rstride + C * 16));
+      }
+      dma_1k(slot_lds + (32 + wave) * 1024, tp, static_cast<uint32_t>(tkey * rstride + tC * 16));
+    } else {
+      // a tile reaching into the scratch rows or past the chunk end: per-lane
+      // rows; keys at or past k_end re-read row k_end-1 (masked later)
+      auto one = [&](uint32_t dst, int key, int C) {
+        key = t0 + key;
+        key = key < k_end ? key : k_end - 1;
+        const bool tr = key >= l_b;
+        const char* src = (tr ? kt_b + static_cast<long>(key - l_b) * rstride
+                              : kc_b + static_cast<long>(key) * rstride) + C * 16;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
+                     : "memory", "m0");
+      };
+#pragma unroll
+      for (int kg = 0; kg < 8; ++kg) {
+        const int key = 4 * kg + (ln >> 4);
+        one(slot_lds + (kg * 4 + wave) * 1024, key, 16 * wave + ((ln & 15) ^ lat_s(key)));
+      }
+      one(slot_lds + (32 + wave) * 1024, tkey, tC);
+    }
+  };
+  issue(0, lds0);
+  if (nt > 1) issue(1, lds0 + kLatTile);
+
+  // ---- this wave's query rows (two groups of 16) and ancestor words
+  bf16x8 qf[2][NC];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const int r = c.rowb * RB + wave * 32 + rg * 16 + lr;
+    const bool rv = r < c.rows_b;   // idle rows compute on zero queries, never written
+    const int node = rv ? r / a.G : 0;
+    const int h = rv ? r % a.G : 0;
+    const uint16_t* src = static_cast<const uint16_t*>(a.q) +
+                          ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * kLatQK;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      if (rv) qf[rg][k] = *reinterpret_cast<const bf16x8*>(src + 32 * k + 8 * lq);
+      else qf[rg][k] = bf16x8{};
+    }
+  }
+
+  // ---- LDS offsets (bytes) of this lane's operand reads inside a tile
+  // score operand, key 16*kb + lr, granule 4*k + lq:
+  //   k < 16:  kofs[k % 4] + kb*16384 + (k/4)*1024;  k = 16, 17: ktl[k-16] + kb*2048
+  uint32_t kofs[4], ktl[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    kofs[q] = (lr >> 2) * 4096 + (lr & 3) * 256 + (((4 * q + lq) ^ lat_s(lr)) << 4);
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    ktl[e] = 32768 + (lr >> 3) * 1024 + (lr & 7) * 128 + (((4 * e + lq) ^ lat_t(lr)) << 4);
+  // transposed value reads (keys 4*lq + lr/4 and +16, columns 128*wave +
+  // 16*dd + 4*(lr%4)): vrow + ((2*dd ^ vsw) << 4), second half +16384
+  const int vkey = 4 * lq + (lr >> 2);
+  uint32_t vrow = (lq * 4 + wave) * 1024 + (lr >> 2) * 256 + (lr & 1) * 8;
+  uint32_t vsw = static_cast<uint32_t>(((lr & 3) >> 1) ^ lat_s(vkey));
+  const uint32_t prow = static_cast<uint32_t>(lane * 16);
+
+  float m_run[2], lsum[2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    m_run[rg] = -INFINITY;
+    lsum[rg] = 0.f;
+  }
+  f32x4 o[8][8];   // [dd][rb]: O^T[128*wave + 16*dd + 4*lq + i][16*rb + lr]
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd)
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) o[dd][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // S^T of tile j from slot base sb: lane holds S^T[key 16*kb + 4*lq + i][row lr]
+  auto scores = [&](f32x4 (&s)[2][2], uint32_t sb) {
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* base = smem + (sb - lds0);
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t off = k < 16 ? kofs[k & 3] + kb * 16384 + (k >> 2) * 1024 : ktl[k - 16] + kb * 2048;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(base + off);
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+          s[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][k], s[rg][kb], 0, 0, 0);
+      }
+  };
+  auto mask = [&](f32x4 (&s)[2][2], int j) {
+    const int t0 = k_beg + j * KT;
+    if (t0 + KT <= k_end && t0 + KT <= l_b) return;
+    asm volatile("" ::: "memory");  // a real branch: only the last tiles take it
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      // the row's ancestor words, read here rather than kept in registers
+      const int r = c.rowb * RB + wave * 32 + rg * 16 + lr;
+      const bool rv = r < c.rows_b;
+      const unsigned* ab = a.anc + (static_cast<size_t>(c.b) * a.N_max + (rv ? r / a.G : 0)) * a.W;
+      uint32_t anc[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) anc[w] = (rv && w < a.W) ? ab[w] : 0u;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = key_visible(anc, t0 + kb * 16 + 4 * lq + i, l_b, k_end);
+          s[rg][kb][i] = ok ? s[rg][kb][i] : -INFINITY;
+        }
+    }
+  };
+  // weights of tile j into LDS buffer j&1 (with rescale factors and flag)
+  auto softmax = [&](f32x4 (&s)[2][2], int j) {
+    const uint32_t buf = static_cast<uint32_t>(j & 1);
+    bool moved = false;
+    float alpha[2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      float mx = vmax3(s[rg][0][0], s[rg][0][1], s[rg][0][2]);
+      mx = vmax3(mx, s[rg][0][3], s[rg][1][0]);
+      mx = vmax3(mx, s[rg][1][1], s[rg][1][2]);
+      mx = vmax3(mx, s[rg][1][3], s[rg][1][3]);
+      const float mt = quad_group_max(mx) * scale;   // the row's max over the tile
+      const bool fresh = m_run[rg] == -INFINITY;
+      const bool up = fresh ? mt > -INFINITY : mt > m_run[rg] + kLazy;
+      const float al = up ? (fresh ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - mt)) : 1.f;
+      m_run[rg] = up ? mt : m_run[rg];
+      lsum[rg] *= al;
+      alpha[rg] = al;
+      moved |= up;
+      const float muse = m_run[rg] == -INFINITY ? 0.f : m_run[rg];
+      bf16x8 pf;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[rg][kb][i], scale, -muse));
+          ps += p;
+          pf[kb * 4 + i] = static_cast<__bf16>(p);
+        }
+      lsum[rg] += ps;
+      *reinterpret_cast<bf16x8*>(smem + kLatP + buf * 8192 + (2 * wave + rg) * 1024 + prow) = pf;
+    }
+    const bool any = __ballot(moved) != 0;
+    if (any && lq == 0) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+        *reinterpret_cast<float*>(smem + kLatAlpha + buf * 512 + (lr * 8 + 2 * wave + rg) * 4) = alpha[rg];
+    }
+    if (lane == 0) *reinterpret_cast<int*>(smem + kLatFlag + buf * 16 + wave * 4) = any ? 1 : 0;
+  };
+  // O^T[128w + 16dd + ..][rows] += V^T[..][keys of tile j] P^T(j)[keys][rows]
+  auto values = [&](uint32_t sv, int j) {
+    const uint32_t buf = static_cast<uint32_t>(j & 1);
+    bf16x8 pt[8];
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+      pt[rb] = *reinterpret_cast<const bf16x8*>(smem + kLatP + buf * 8192 + rb * 1024 + prow);
+    const char* base = smem + (sv - lds0);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const uint32_t off = vrow + (((2 * dd) ^ vsw) << 4);
+      union {
+        s16x4 h[2];
+        bf16x8 v;
+      } vf;
+      vf.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(base + off));
+      vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(base + off + 16384));
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb)
+        o[dd][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pt[rb], o[dd][rb], 0, 0, 0);
+    }
+  };
+  // rows whose reference max moved in tile j: scale their accumulators
+  auto rescale = [&](int j) {
+    const uint32_t buf = static_cast<uint32_t>(j & 1);
+    const int4 fl = *reinterpret_cast<const int4*>(smem + kLatFlag + buf * 16);
+    const int fm = __builtin_amdgcn_readfirstlane((fl.x ? 1 : 0) | (fl.y ? 2 : 0) | (fl.z ? 4 : 0) | (fl.w ? 8 : 0));
+    if (fm == 0) return;
+    asm volatile("" ::: "memory");  // a real branch: rare after the first tile
+    const float* al = reinterpret_cast<const float*>(smem + kLatAlpha + buf * 512 + lr * 32);
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+      const float f = ((fm >> (rb >> 1)) & 1) ? al[rb] : 1.f;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) o[dd][rb] *= f;
+    }
+  };
+
+  f32x4 sn[2][2];
+  wait_vmcnt<0>();
+  lds_barrier();
+  scores(sn, lds0);
+  mask(sn, 0);
+  softmax(sn, 0);
+
+  uint32_t s_cur = lds0, s_nxt = lds0 + kLatTile, s_aft = lds0 + 2 * kLatTile;
+  for (int t = 0; t < nt; ++t) {
+    // tile t+1 resident, weights of tile t posted; every wave is done with
+    // tile t-1, whose slot takes tile t+2
+    wait_all_mem();
+    lds_barrier();
+    if (t + 2 < nt) issue(t + 2, s_aft);
+    asm volatile("" : "+v"(vrow), "+v"(vsw));
+    rescale(t);
+    // the last step scores a stale slot as tile nt, whose keys all lie past
+    // k_end: fully masked, it leaves every row's max and sum unchanged
+    scores(sn, s_nxt);
+    mask(sn, t + 1);
+    values(s_cur, t);
+    softmax(sn, t + 1);
+    const uint32_t s_old = s_cur;
+    s_cur = s_nxt;
+    s_nxt = s_aft;
+    s_aft = s_old;
+  }
+
+  // ---- row totals to every wave
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const float l = quad_group_sum(lsum[rg]);
+    if (lq == 0)
+      *reinterpret_cast<float2*>(smem + kLatStat + (wave * 32 + rg * 16 + lr) * 8) = make_float2(m_run[rg], l);
+  }
+  __syncthreads();
+
+  if (c.splits == 1) {
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+      const int r_loc = rb * 16 + lr;
+      const int r = c.rowb * RB + r_loc;
+      if (r >= c.rows_b) continue;
+      const float2 ml = *reinterpret_cast<const float2*>(smem + kLatStat + r_loc * 8);
+      const size_t orow = (static_cast<size_t>(c.b) * a.N_max + r / a.G) * a.Hq + r % a.G;
+      uint16_t* op = static_cast<uint16_t*>(a.out) + orow * kLatV + 128 * wave + 4 * lq;
+      const float inv = 1.0f / ml.y;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        union {
+          uint2 u;
+          __bf16 h4[4];
+        } pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(o[dd][rb][i] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * dd) = pk.u;
+      }
+      if (a.lse && lq == 0 && (rb >> 1) == wave) a.lse[orow] = (ml.x + log2f(ml.y)) * kLn2;
+    }
+    return;
+  }
+  // partial (max, sum, unnormalised accumulator) for the combine kernel
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb) {
+    const int r_loc = rb * 16 + lr;
+    if (c.rowb * RB + r_loc >= c.rows_b) continue;
+    const size_t pr = static_cast<size_t>(item) * RB + r_loc;
+    float* pa = a.part_acc + pr * kLatV + 128 * wave + 4 * lq;
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd)
+      *reinterpret_cast<float4*>(pa + 16 * dd) = make_float4(o[dd][rb][0], o[dd][rb][1], o[dd][rb][2], o[dd][rb][3]);
+    if (lq == 0 && (rb >> 1) == wave) {
+      const float2 ml = *reinterpret_cast<const float2*>(smem + kLatStat + r_loc * 8);
+      a.part_ml[pr * 2 + 0] = ml.x;
+      a.part_ml[pr * 2 + 1] = ml.y;
+    }
+  }
+}
+
 // --------------------------------------------------------------- VALU path
 template <typename T>
 __device__ __forceinline__ float ld_elem(const T* p);
@@ -1295,7 +1433,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 }  // namespace
 
-AttnPlan attn_plan(const AttnShape& sh, bool aligned) {
+AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
   AttnPlan p;
   const bool bf = sh.dtype == TSV_BF16;
   p.chunk = p.S = p.units = p.rbs = 0;
@@ -1331,12 +1469,12 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned) {
     off = align_up(off + static_cast<size_t>(p.items_max) * p.RB * sh.d_v * sizeof(float));
     p.bytes = off;
     return p;
-  } else if (bf && aligned && sh.d_qk == 576 && sh.d_v == 512) {
+  } else if (bf && aligned && shared_value && sh.d_qk == 576 && sh.d_v == 512) {
     p.path = kPathMfmaLatent;
-    p.RB = 64;
+    p.RB = 128;
     p.KT = 32;
     p.min_chunk = 256;
-    p.target_items = 1024;
+    p.target_items = 512;
   } else {
     p.path = kPathValu;
     p.RB = kValuRows;
@@ -1371,7 +1509,7 @@ hipError_t launch_attention(const AttnArgs& a, AttnPath path, int dtype, hipStre
   if (e != hipSuccess) return e;
   dim3 grid(a.items_max), block(256);
   if (path == kPathMfmaLatent) {
-    attn_mfma_kernel<576, 512, 1, 32, false><<<grid, block, 0, s>>>(a);
+    attn_latent_kernel<<<dim3((a.items_max + 7) / 8 * 8), block, 0, s>>>(a);
   } else if (dtype == TSV_F32) {
     attn_valu_kernel<float><<<grid, block, 0, s>>>(a);
   } else {

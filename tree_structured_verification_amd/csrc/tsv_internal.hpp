@@ -83,8 +83,9 @@ struct AttnPlan {
   size_t off_cnt;    // arrival counters, one int per unit (zero between calls)
   size_t off_info, off_desc, off_ml, off_acc, bytes;
 };
-// `aligned` says whether pointers and strides allow 16-byte vector access.
-AttnPlan attn_plan(const AttnShape& sh, bool aligned);
+// `aligned` says whether pointers and strides allow 16-byte vector access;
+// `shared_value` whether the value rows are the key rows (one latent head).
+AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value);
 
 struct AttnArgs {
   const void* q;
