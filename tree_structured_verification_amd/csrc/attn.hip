@@ -1034,26 +1034,59 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
     }
     if (lane == 0) *reinterpret_cast<int*>(smem + kLatFlag + buf * 16 + wave * 4) = any ? 1 : 0;
   };
-  // O^T[128w + 16dd + ..][rows] += V^T[..][keys of tile j] P^T(j)[keys][rows]
-  auto values = [&](uint32_t sv, int j) {
+  // Scores of tile j+1 and the value product of tile j
+  //   O^T[128w + 16dd + ..][rows] += V^T[..][keys of tile j] P^T(j)[keys][rows]
+  // interleaved: each of the 36 score steps (one K operand read, two MFMAs)
+  // carries two value MFMAs, so that every LDS read has MFMA work to hide
+  // behind.  The scheduling barriers keep that order (and the register use
+  // it implies: with the queries and the accumulator resident, the register
+  // file has room for about one operand in flight).
+  auto fused = [&](f32x4 (&s)[2][2], uint32_t sb, uint32_t sv, int j) {
     const uint32_t buf = static_cast<uint32_t>(j & 1);
     bf16x8 pt[8];
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb)
       pt[rb] = *reinterpret_cast<const bf16x8*>(smem + kLatP + buf * 8192 + rb * 1024 + prow);
-    const char* base = smem + (sv - lds0);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
+    const char* kbase = smem + (sb - lds0);
+    const char* vbase = smem + (sv - lds0);
+    auto kread = [&](int n) {
+      const int k = n >> 1, kb = n & 1;
+      const uint32_t off = k < 16 ? kofs[k & 3] + kb * 16384 + (k >> 2) * 1024 : ktl[k - 16] + kb * 2048;
+      return *reinterpret_cast<const bf16x8*>(kbase + off);
+    };
+    auto vread = [&](int dd) {
       const uint32_t off = vrow + (((2 * dd) ^ vsw) << 4);
       union {
         s16x4 h[2];
         bf16x8 v;
       } vf;
-      vf.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(base + off));
-      vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(base + off + 16384));
+      vf.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off));
+      vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off + 16384));
+      return vf.v;
+    };
 #pragma unroll
-      for (int rb = 0; rb < 8; ++rb)
-        o[dd][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pt[rb], o[dd][rb], 0, 0, 0);
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 vf = vread(0), vn = vf;
+    bf16x8 kf = kread(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < 2 * NC; ++n) {
+      const bf16x8 kn = n + 1 < 2 * NC ? kread(n + 1) : kf;
+      if (n < 32 && (n & 3) == 0 && (n >> 2) + 1 < 8) vn = vread((n >> 2) + 1);
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+        s[rg][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][n >> 1], s[rg][n & 1], 0, 0, 0);
+      if (n < 32) {
+        const int dd = n >> 2, rb0 = 2 * (n & 3);
+#pragma unroll
+        for (int rb = rb0; rb < rb0 + 2; ++rb)
+          o[dd][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[rb], o[dd][rb], 0, 0, 0);
+        if ((n & 3) == 3) vf = vn;
+      }
+      kf = kn;
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // rows whose reference max moved in tile j: scale their accumulators
@@ -1090,9 +1123,8 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
     rescale(t);
     // the last step scores a stale slot as tile nt, whose keys all lie past
     // k_end: fully masked, it leaves every row's max and sum unchanged
-    scores(sn, s_nxt);
+    fused(sn, s_nxt, s_cur, t);
     mask(sn, t + 1);
-    values(s_cur, t);
     softmax(sn, t + 1);
     const uint32_t s_old = s_cur;
     s_cur = s_nxt;
