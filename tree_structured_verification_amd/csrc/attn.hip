@@ -427,6 +427,9 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
       if (rv) qf[rg][k] = *reinterpret_cast<const bf16x8*>(src + 32 * k + 8 * lq);
       else qf[rg][k] = bf16x8{};
     }
+    const unsigned* ab = a.anc + (static_cast<size_t>(c.b) * a.N_max + node) * a.W;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) anc[rg][w] = (rv && w < a.W) ? ab[w] : 0u;
   }
 
   // m_run: reference max per row (log2 units); muse: m_run, or 0 while no key
@@ -690,20 +693,30 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
   // acknowledgement wait is a write-back of every dirty line of the L2, and
   // the published rows never are dirty there; issued by every workgroup it
   // costs more than the rest of the combine.
-  // Layout private to this kernel, in lane order so that every store and
-  // load instruction covers 512 contiguous bytes: per (unit, split), per
-  // (wave, row group): accumulators [d][pair][lane] as float2, and the row
-  // (max, sum) pairs [lr] as float2.
+  // What a split publishes is its rows normalised by their own sums (O/l,
+  // rounded to bf16: half the bytes of fp32, and the combine scales them
+  // back by w*l in fp32) with the row (max, sum) pairs in fp32.  Layout
+  // private to this kernel, in lane order so that every store and load
+  // instruction covers 512 contiguous bytes: per (unit, split), per (wave,
+  // row group): normalised rows [d][lane] as 4 x bf16, and the row (max,
+  // sum) pairs [lr] as float2.
   const size_t item = static_cast<size_t>(unit) * a.S + c.split;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const int wr = wave * RG + rg;
-    uint64_t* pa = reinterpret_cast<uint64_t*>(a.part_acc + item * RB * D) + static_cast<size_t>(wr) * NDB * 2 * 64;
+    uint64_t* pa = reinterpret_cast<uint64_t*>(a.part_acc + item * RB * D) + static_cast<size_t>(wr) * NDB * 64;
+    const float lt = lacc[rg][0];
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
+    for (int d = 0; d < NDB; ++d) {
+      union {
+        float2 f;
+        __bf16 h4[4];
+      } pk;
 #pragma unroll
-      for (int ip = 0; ip < 2; ++ip)
-        st_coherent2(pa + (d * 2 + ip) * 64 + lane, o[rg][d][2 * ip], o[rg][d][2 * ip + 1]);
+      for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(o[rg][d][i] * inv);
+      st_coherent2(pa + d * 64 + lane, pk.f.x, pk.f.y);
+    }
     if (lq == 0)
       st_coherent2(reinterpret_cast<uint64_t*>(a.part_ml + item * RB * 2) + wr * 16 + lr, m_run[rg], lacc[rg][0]);
   }
@@ -736,27 +749,35 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
     for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s2 = 0; s2 < c.splits; ++s2) {
       if (s2 == c.split) {
+        // this split's rows from registers, rounded exactly as published, so
+        // that the sum is the same whichever split arrives last
+        const float lt = lacc[rg][0];
         const float w = m_run[rg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - M);
-        L = fmaf(w, lacc[rg][0], L);
+        L = fmaf(w, lt, L);
+        const float wl = w * lt;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[d][i] = fmaf(w, o[rg][d][i], acc[d][i]);
+          for (int i = 0; i < 4; ++i)
+            acc[d][i] = fmaf(wl, static_cast<float>(static_cast<__bf16>(o[rg][d][i] * inv)), acc[d][i]);
         continue;
       }
       const float2 ml = ml_of(s2);
       const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
       L = fmaf(w, ml.y, L);
+      const float wl = w * ml.y;   // weight of the normalised row
       const uint64_t* pa = reinterpret_cast<const uint64_t*>(a.part_acc + (static_cast<size_t>(unit) * a.S + s2) * RB * D) +
-                           static_cast<size_t>(wr) * NDB * 2 * 64;
+                           static_cast<size_t>(wr) * NDB * 64;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int ip = 0; ip < 2; ++ip) {
-          const float2 v = ld_coherent2(pa + (d * 2 + ip) * 64 + lane);
-          acc[d][2 * ip] = fmaf(w, v.x, acc[d][2 * ip]);
-          acc[d][2 * ip + 1] = fmaf(w, v.y, acc[d][2 * ip + 1]);
-        }
+      for (int d = 0; d < NDB; ++d) {
+        const float2 v = ld_coherent2(pa + d * 64 + lane);
+        const uint32_t u0 = __float_as_uint(v.x), u1 = __float_as_uint(v.y);
+        acc[d][0] = fmaf(wl, __uint_as_float(u0 << 16), acc[d][0]);
+        acc[d][1] = fmaf(wl, __uint_as_float(u0 & 0xFFFF0000u), acc[d][1]);
+        acc[d][2] = fmaf(wl, __uint_as_float(u1 << 16), acc[d][2]);
+        acc[d][3] = fmaf(wl, __uint_as_float(u1 & 0xFFFF0000u), acc[d][3]);
+      }
     }
     write_row(rg, acc, M, L);
   }
