@@ -23,7 +23,11 @@ workload on this host's cores.
     python bench.py --attention-only --copy-calibration 256 --steps 10 --warmup 2
 
 runs only the attention calls (after three 256 MiB device copies of known
-traffic), for the FETCH_SIZE / WRITE_SIZE counter runs.
+traffic), for the FETCH_SIZE / WRITE_SIZE counter runs;
+--attention-workload N does the same on workload N of workloads/gen.py
+(3 = mla_bf16, 5 = long_mla, ...) and prints the mean time per call with
+the achieved matrix throughput and HBM bandwidth on algorithmic flops and
+bytes (for the counter runs of the other kernels' shapes).
 """
 
 import argparse
@@ -86,6 +90,54 @@ def attention_bytes(cfg, prefix, n):
     return prefix_bytes + nodes * per_node
 
 
+def attention_only(wid, K, W, dev):
+    """K timed tree_verify_attn calls (after W) on workload wid, inputs in
+    three rotating copies; prints one JSON line."""
+    cfg = config(wid)
+    print(f"[bench] attention only, workload {cfg.name}", file=sys.stderr, flush=True)
+    ins = attention_inputs(cfg, 0, dev)
+    marg = marginals(cfg, 0, dev)
+    pl = ins["prefix_len"]
+    tree = tsv.build_tree(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=cfg.cost,
+                          prefix_len=pl if cfg.cost is not None else None)
+    del marg
+    keys = ("q", "k_cache", "v_cache", "k_tree", "v_tree")
+    sets = [ins] + [{k: ins[k].clone() for k in keys} for _ in range(ROTATE - 1)]
+    if cfg.mla:   # one latent cache serves as key and value
+        for st in sets:
+            st["v_cache"], st["v_tree"] = st["k_cache"], st["k_tree"]
+    B, N = cfg.B, cfg.N_max
+    out = torch.empty(B, N, cfg.Hq, cfg.d_v, dtype=cfg.torch_dtype, device=dev)
+    lse = torch.empty(B, N, cfg.Hq, dtype=torch.float32, device=dev)
+    ws = tsv.workspace(tsv.workspace_size(1, B, 1, 1, 1, N, cfg.L_cap, cfg.Hq, cfg.Hkv,
+                                          cfg.d_qk, cfg.d_v, 0 if cfg.dtype == "f32" else 1), dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(W + K)]
+    stream = torch.cuda.current_stream(dev)
+    for s in range(W + K):
+        st = sets[s % ROTATE]
+        ev[s][0].record(stream)
+        tsv.tree_verify_attn(st["q"], st["k_cache"], st["v_cache"], st["k_tree"], st["v_tree"],
+                             pl, tree["n_nodes"], tree["anc_bits"], cfg.Hkv, cfg.d_v,
+                             cfg.sm_scale, out=out, lse=lse, ws=ws)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev[W:]])) / 1e3
+    n = tree["n_nodes"].cpu().numpy()
+    depth = tree["depth"].cpu().numpy()
+    prefix = pl.cpu().numpy().astype(np.int64)
+    # each node attends to the prefix and to its ancestors (depth of them)
+    pairs = sum(int(n[b]) * int(prefix[b]) + int(depth[b, :n[b]].sum()) for b in range(B))
+    flops = 2.0 * pairs * cfg.Hq * (cfg.d_qk + cfg.d_v)
+    nbytes = attention_bytes(cfg, prefix, n)
+    print(json.dumps({"attention_workload": cfg.name, "calls": K, "us_per_call": round(t * 1e6, 1),
+                      "tflops": round(flops / t / 1e12, 1),
+                      "mfma_frac_bf16": round(flops / t / 2.5e15, 4),
+                      "gbs": round(nbytes / t / 1e9, 1),
+                      "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                      "algorithmic_flops": flops, "algorithmic_bytes": nbytes}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +148,8 @@ def main():
                     help="requests of the workload the CPU oracle runs")
     ap.add_argument("--attention-only", action="store_true",
                     help="run only the tree_verify_attn calls of the steps (for counter runs)")
+    ap.add_argument("--attention-workload", type=int, default=0, metavar="N",
+                    help="time only tree_verify_attn on workload N (implies --attention-only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB three times between device buffers, so that "
                          "byte counters can be scaled by a kernel of known traffic")
@@ -113,6 +167,9 @@ def main():
             bufs[2 * i + 1].copy_(bufs[2 * i])
         torch.cuda.synchronize()
         del bufs
+    if args.attention_workload:
+        attention_only(args.attention_workload, args.steps, args.warmup, dev)
+        return
     cfg = config(WORKLOAD)
     print(f"[bench] generating workload {cfg.name} on {torch.cuda.get_device_name(dev)}",
           file=sys.stderr, flush=True)

@@ -818,18 +818,25 @@ constexpr int kLatQK = 576, kLatV = 512;
 constexpr int kLatTile = 32 * kLatQK * 2;        // bytes of one K tile
 constexpr int kLatSlots = 3;
 constexpr int kLatP = kLatSlots * kLatTile;      // weights, two buffers of 8 KiB
-constexpr int kLatAlpha = kLatP + 2 * 8192;      // rescale factors [2][16][8]
-constexpr int kLatFlag = kLatAlpha + 2 * 512;    // rescale flags [2][4]
-constexpr int kLatStat = kLatFlag + 32;          // final (max, sum) per row
+constexpr int kLatAlpha = kLatP + 2 * 8192;      // rescale factors [2][4 copies][16][8]
+constexpr int kLatFlag = kLatAlpha + 2 * 2048;   // rescale flags [2][4 waves][64 lanes]
+constexpr int kLatStat = kLatFlag + 2 * 1024;    // final (max, sum) per row
 constexpr int kLatLds = kLatStat + 128 * 8;
 
-__device__ __forceinline__ int lat_s(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+__device__ __forceinline__ int lat_s(int k) { return ((k & 3) << 1) | ((k & 4) << 1) | ((k >> 3) & 1); }
 __device__ __forceinline__ int lat_t(int k) { return (k >> 1) & 7; }
 
 // s_waitcnt vmcnt(0) lgkmcnt(0): this wave's DMA blocks and LDS writes done
 __device__ __forceinline__ void wait_all_mem() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0x70);
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS writes done (DMA loads may remain)
+__device__ __forceinline__ void wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("" ::: "memory");
 }
 
@@ -1014,110 +1021,120 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
         }
     }
   };
-  // weights of tile j into LDS buffer j&1 (with rescale factors and flag)
-  auto softmax = [&](f32x4 (&s)[2][2], int j) {
-    const uint32_t buf = static_cast<uint32_t>(j & 1);
-    bool moved = false;
-    float alpha[2];
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      float mx = vmax3(s[rg][0][0], s[rg][0][1], s[rg][0][2]);
-      mx = vmax3(mx, s[rg][0][3], s[rg][1][0]);
-      mx = vmax3(mx, s[rg][1][1], s[rg][1][2]);
-      mx = vmax3(mx, s[rg][1][3], s[rg][1][3]);
-      const float mt = quad_group_max(mx) * scale;   // the row's max over the tile
-      const bool fresh = m_run[rg] == -INFINITY;
-      const bool up = fresh ? mt > -INFINITY : mt > m_run[rg] + kLazy;
-      const float al = up ? (fresh ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - mt)) : 1.f;
-      m_run[rg] = up ? mt : m_run[rg];
-      lsum[rg] *= al;
-      alpha[rg] = al;
-      moved |= up;
-      const float muse = m_run[rg] == -INFINITY ? 0.f : m_run[rg];
-      bf16x8 pf;
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[rg][kb][i], scale, -muse));
-          ps += p;
-          pf[kb * 4 + i] = static_cast<__bf16>(p);
-        }
-      lsum[rg] += ps;
-      *reinterpret_cast<bf16x8*>(smem + kLatP + buf * 8192 + (2 * wave + rg) * 1024 + prow) = pf;
-    }
-    const bool any = __ballot(moved) != 0;
-    if (any && lq == 0) {
-#pragma unroll
-      for (int rg = 0; rg < 2; ++rg)
-        *reinterpret_cast<float*>(smem + kLatAlpha + buf * 512 + (lr * 8 + 2 * wave + rg) * 4) = alpha[rg];
-    }
-    if (lane == 0) *reinterpret_cast<int*>(smem + kLatFlag + buf * 16 + wave * 4) = any ? 1 : 0;
+  auto kread = [&](const char* kbase, int n) {
+    const int k = n >> 1, kb = n & 1;
+    const uint32_t off = k < 16 ? kofs[k & 3] + kb * 16384 + (k >> 2) * 1024 : ktl[k - 16] + kb * 2048;
+    return *reinterpret_cast<const bf16x8*>(kbase + off);
   };
-  // Scores of tile j+1 and the value product of tile j
-  //   O^T[128w + 16dd + ..][rows] += V^T[..][keys of tile j] P^T(j)[keys][rows]
-  // interleaved: each of the 36 score steps (one K operand read, two MFMAs)
-  // carries two value MFMAs, so that every LDS read has MFMA work to hide
-  // behind.  The scheduling barriers keep that order (and the register use
-  // it implies: with the queries and the accumulator resident, the register
-  // file has room for about one operand in flight).
-  auto fused = [&](f32x4 (&s)[2][2], uint32_t sb, uint32_t sv, int j) {
+  auto vread = [&](const char* vbase, int dd) {
+    const uint32_t off = vrow + (((2 * dd) ^ vsw) << 4);
+    union {
+      s16x4 h[2];
+      bf16x8 v;
+    } vf;
+    vf.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off));
+    vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off + 16384));
+    return vf.v;
+  };
+  // Phase 1 of a step: the scores of tile j+1 (36 groups of one K operand
+  // read, issued two groups ahead, and two MFMAs) with the softmax of tile j
+  // cut into small pieces, one after each group, so that the VALU work runs
+  // while the matrix cores are busy.  The scheduling barriers keep that order.
+  // The weights, rescale factors and flag of tile j go to LDS.
+  auto phase1 = [&](f32x4 (&s)[2][2], uint32_t sb, f32x4 (&x)[2][2], int j) {
     const uint32_t buf = static_cast<uint32_t>(j & 1);
-    bf16x8 pt[8];
-#pragma unroll
-    for (int rb = 0; rb < 8; ++rb)
-      pt[rb] = *reinterpret_cast<const bf16x8*>(smem + kLatP + buf * 8192 + rb * 1024 + prow);
     const char* kbase = smem + (sb - lds0);
-    const char* vbase = smem + (sv - lds0);
-    auto kread = [&](int n) {
-      const int k = n >> 1, kb = n & 1;
-      const uint32_t off = k < 16 ? kofs[k & 3] + kb * 16384 + (k >> 2) * 1024 : ktl[k - 16] + kb * 2048;
-      return *reinterpret_cast<const bf16x8*>(kbase + off);
-    };
-    auto vread = [&](int dd) {
-      const uint32_t off = vrow + (((2 * dd) ^ vsw) << 4);
-      union {
-        s16x4 h[2];
-        bf16x8 v;
-      } vf;
-      vf.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off));
-      vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off + 16384));
-      return vf.v;
-    };
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 vf = vread(0), vn = vf;
-    bf16x8 kf = kread(0);
+    float mx[2], mt[2], muse[2], ps[2], alpha[2];
+    bf16x8 pf[2];
+    bool moved = false;
+    // piece m of the softmax of row group rg (13 pieces per row group)
+    auto piece = [&](int rg, int m) {
+      if (m == 0) {
+        mx[rg] = vmax3(x[rg][0][0], x[rg][0][1], x[rg][0][2]);
+        mx[rg] = vmax3(mx[rg], x[rg][0][3], x[rg][1][0]);
+      } else if (m == 1) {
+        mx[rg] = vmax3(mx[rg], x[rg][1][1], x[rg][1][2]);
+        mx[rg] = vmax3(mx[rg], x[rg][1][3], x[rg][1][3]);
+      } else if (m == 2) {
+        mt[rg] = quad_group_max(mx[rg]) * scale;   // the row's max over the tile
+      } else if (m == 3) {
+        const bool fresh = m_run[rg] == -INFINITY;
+        const bool up = fresh ? mt[rg] > -INFINITY : mt[rg] > m_run[rg] + kLazy;
+        const float al = up ? (fresh ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - mt[rg])) : 1.f;
+        m_run[rg] = up ? mt[rg] : m_run[rg];
+        lsum[rg] *= al;
+        alpha[rg] = al;
+        moved |= up;
+        muse[rg] = m_run[rg] == -INFINITY ? 0.f : m_run[rg];
+        ps[rg] = 0.f;
+      } else if (m < 12) {
+        const int e = m - 4;
+        const float p = __builtin_amdgcn_exp2f(fmaf(x[rg][e >> 2][e & 3], scale, -muse[rg]));
+        ps[rg] += p;
+        pf[rg][e] = static_cast<__bf16>(p);
+      } else {
+        lsum[rg] += ps[rg];
+        *reinterpret_cast<bf16x8*>(smem + kLatP + buf * 8192 + (2 * wave + rg) * 1024 + prow) = pf[rg];
+      }
+    };
+    bf16x8 kf[3];
+    kf[0] = kread(kbase, 0);
+    kf[1] = kread(kbase, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < 2 * NC; ++n) {
-      const bf16x8 kn = n + 1 < 2 * NC ? kread(n + 1) : kf;
-      if (n < 32 && (n & 3) == 0 && (n >> 2) + 1 < 8) vn = vread((n >> 2) + 1);
+      if (n + 2 < 2 * NC) kf[(n + 2) % 3] = kread(kbase, n + 2);
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg)
-        s[rg][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][n >> 1], s[rg][n & 1], 0, 0, 0);
-      if (n < 32) {
-        const int dd = n >> 2, rb0 = 2 * (n & 3);
+        s[rg][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n % 3], qf[rg][n >> 1], s[rg][n & 1], 0, 0, 0);
+      if (n < 26) piece(n / 13, n % 13);
+      if (n == 26) {
+        // written by every lane, without branches and to distinct addresses
+        // (each of the four lanes of a row keeps its own copy of the factor,
+        // each lane its own copy of the wave's flag)
+        const bool any = __ballot(moved) != 0;
 #pragma unroll
-        for (int rb = rb0; rb < rb0 + 2; ++rb)
-          o[dd][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[rb], o[dd][rb], 0, 0, 0);
-        if ((n & 3) == 3) vf = vn;
+        for (int rg = 0; rg < 2; ++rg)
+          *reinterpret_cast<float*>(smem + kLatAlpha + buf * 2048 + lq * 512 + (lr * 8 + 2 * wave + rg) * 4) = alpha[rg];
+        *reinterpret_cast<int*>(smem + kLatFlag + buf * 1024 + wave * 256 + lane * 4) = any ? 1 : 0;
       }
-      kf = kn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Phase 2: O^T[128w + 16dd + ..][rows] += V^T[..][keys of tile j] P^T(j),
+  // the transposed value operand of block dd+1 read while block dd's eight
+  // MFMAs run.
+  auto phase2 = [&](uint32_t sv, int j) {
+    const uint32_t buf = static_cast<uint32_t>(j & 1);
+    const char* vbase = smem + (sv - lds0);
+    bf16x8 pt[8];
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+      pt[rb] = *reinterpret_cast<const bf16x8*>(smem + kLatP + buf * 8192 + rb * 1024 + prow);
+    bf16x8 vf[2];
+    vf[0] = vread(vbase, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      if (dd + 1 < 8) vf[(dd + 1) & 1] = vread(vbase, dd + 1);
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb)
+        o[dd][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd & 1], pt[rb], o[dd][rb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // rows whose reference max moved in tile j: scale their accumulators
   auto rescale = [&](int j) {
     const uint32_t buf = static_cast<uint32_t>(j & 1);
-    const int4 fl = *reinterpret_cast<const int4*>(smem + kLatFlag + buf * 16);
-    const int fm = __builtin_amdgcn_readfirstlane((fl.x ? 1 : 0) | (fl.y ? 2 : 0) | (fl.z ? 4 : 0) | (fl.w ? 8 : 0));
+    const int* fl = reinterpret_cast<const int*>(smem + kLatFlag + buf * 1024 + lane * 4);
+    const int fm = __builtin_amdgcn_readfirstlane((fl[0] ? 1 : 0) | (fl[64] ? 2 : 0) | (fl[128] ? 4 : 0) | (fl[192] ? 8 : 0));
     if (fm == 0) return;
     asm volatile("" ::: "memory");  // a real branch: rare after the first tile
-    const float* al = reinterpret_cast<const float*>(smem + kLatAlpha + buf * 512 + lr * 32);
+    const float* al = reinterpret_cast<const float*>(smem + kLatAlpha + buf * 2048 + lq * 512 + lr * 32);
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
       const float f = ((fm >> (rb >> 1)) & 1) ? al[rb] : 1.f;
@@ -1126,27 +1143,34 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
     }
   };
 
-  f32x4 sn[2][2];
+  f32x4 sc[2][2], sn[2][2];
   wait_vmcnt<0>();
   lds_barrier();
-  scores(sn, lds0);
-  mask(sn, 0);
-  softmax(sn, 0);
+  scores(sc, lds0);
+  mask(sc, 0);
 
+  // Step t: (1) the scores of tile t+1 beside the softmax of tile t, (2)
+  // after a barrier that publishes the weights, the value product of tile t.
+  // The last step scores a stale slot as tile nt, whose keys all lie past
+  // k_end (fully masked, never used).
   uint32_t s_cur = lds0, s_nxt = lds0 + kLatTile, s_aft = lds0 + 2 * kLatTile;
   for (int t = 0; t < nt; ++t) {
-    // tile t+1 resident, weights of tile t posted; every wave is done with
-    // tile t-1, whose slot takes tile t+2
+    // tile t+1 resident; every wave is done with step t-1 (its weights and
+    // tile t-1, whose slot takes tile t+2)
     wait_all_mem();
     lds_barrier();
     if (t + 2 < nt) issue(t + 2, s_aft);
     asm volatile("" : "+v"(vrow), "+v"(vsw));
-    rescale(t);
-    // the last step scores a stale slot as tile nt, whose keys all lie past
-    // k_end: fully masked, it leaves every row's max and sum unchanged
-    fused(sn, s_nxt, s_cur, t);
+    phase1(sn, s_nxt, sc, t);
     mask(sn, t + 1);
-    softmax(sn, t + 1);
+    wait_lgkm0();   // this wave's weights written (tile t+2 stays in flight)
+    lds_barrier();
+    rescale(t);
+    phase2(s_cur, t);
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[rg][kb] = sn[rg][kb];
     const uint32_t s_old = s_cur;
     s_cur = s_nxt;
     s_nxt = s_aft;
