@@ -1,6 +1,7 @@
 """tree_verify_attn on the GPU vs the fp64 oracle (tolerance 1e-5 fp32,
 2e-2 bf16), plus bitwise properties: sibling isolation and determinism."""
 
+import ctypes
 import math
 import zlib
 
@@ -10,6 +11,7 @@ import torch
 
 import oracle
 import tree_structured_verification_amd as tsv
+from tree_structured_verification_amd import _lib
 from tests._helpers import DEV, TOL, check_attention, np32, oracle_trees
 from workloads import attention_inputs, config, marginals
 
@@ -200,3 +202,34 @@ def test_invalid_arguments():
         tsv.tree_verify_attn(q, kc, kc, kt, kt, pl, n, anc, 2, 64, 0.1,
                              ws=torch.empty(64, dtype=torch.uint8, device=DEV))
     assert e.value.code == -3
+
+
+def test_wide_heads_value_cache_of_its_own():
+    """Head widths 576 / 512 with a value cache of its own (not the key rows,
+    so not the latent path): rows padded to the key's stride and passed
+    through the C entry point; the generic kernel, checked against the oracle."""
+    rng = np.random.default_rng(11)
+    B, N_max, Hq, dq, dv, L = 2, 6, 16, 576, 512, 160
+    prefix = [130, 40]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    rn = lambda *s: torch.randn(*s, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    q, kc, kt = rn(B, N_max, Hq, dq), rn(B, L, dq), rn(B, N_max, dq)
+    vc, vt = rn(B, L, dq), rn(B, N_max, dq)   # the value is the first dv columns
+    pl = torch.tensor(prefix, dtype=torch.int32, device=DEV)
+    trees = _random_trees(rng, B, N_max, [6, 3])
+    n = torch.tensor([t.n for t in trees], dtype=torch.int32, device=DEV)
+    anc = torch.from_numpy(np.stack([t.anc_bits for t in trees]).view(np.int32)).to(DEV)
+    out = torch.full((B, N_max, Hq, dv), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, N_max, Hq, dtype=torch.float32, device=DEV)
+    ws = tsv.workspace(tsv.workspace_size(1, B, 1, 1, 1, N_max, L, Hq, 1, dq, dv, tsv.TSV_BF16), DEV)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    scale = 1 / math.sqrt(dq)
+    rc = _lib.lib().tree_verify_attn(P(q), P(kc), P(vc), P(kt), P(vt), dq, P(pl), P(n), P(anc),
+                                     B, N_max, L, Hq, 1, dq, dv, tsv.TSV_BF16,
+                                     ctypes.c_float(scale), P(out), P(lse), P(ws), ws.numel(),
+                                     None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    check_attention(out, lse, q, kc.unsqueeze(2), vc[..., :dv].unsqueeze(2), kt.unsqueeze(2),
+                    vt[..., :dv].unsqueeze(2), prefix, trees, scale, TOL[torch.bfloat16], False, dv)

@@ -203,7 +203,6 @@ struct WaveSelect {
   }
 };
 
-constexpr int kMergeCap = 4096;  // segments * k, enforced by topk_plan
 constexpr int kMaxSegments = 16;
 
 // One workgroup per row, wavefront w scanning segment w.
@@ -212,7 +211,7 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
     const float* __restrict__ x, int rows, int V, int k, int nseg, int seg_len,
     int* __restrict__ out_idx, float* __restrict__ out_p) {
   __shared__ uint64_t queue[kMaxSegments][64];
-  __shared__ uint64_t keys[kMergeCap];
+  __shared__ uint64_t keys[kMaxSegments * 128];   // list hand-over, up to 128 keys per wave
   __shared__ uint32_t published[kMaxSegments];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x;
@@ -325,36 +324,30 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
   }
   sel.finish();
 
-  // the first k keys of each list (only they can reach the row's top k),
-  // then one bitonic sort of all of them in LDS
+  // Tree merge of the wave lists (each holds its segment's best keys, and
+  // the row's top k is among them): in round r, wave w with w % 2r == r
+  // hands its list through LDS to wave w - r, which merges it into its own.
+  // A wave's LDS slot is read only in the round it sends, and it sends only
+  // after its last merge, so one barrier per round orders everything.
+  for (int r = 1; r < nseg; r <<= 1) {
+    if ((wave & (2 * r - 1)) == r) {
 #pragma unroll
-  for (int s2 = 0; s2 < SLOTS; ++s2)
-    if (s2 * 64 + lane < k) keys[wave * k + s2 * 64 + lane] = sel.list.v[s2];
-  const int n = nseg * k;
-  int P = 1;
-  while (P < n) P <<= 1;
-  const int t = threadIdx.x, nt = blockDim.x;
-  for (int i = n + t; i < P; i += nt) keys[i] = 0;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < P / 2; i += nt) {
-        const int lo = 2 * i - (i & (stride - 1));   // lower index of the pair
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t a = keys[lo], b = keys[hi];
-        if ((a < b) == desc) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
-      }
-      __syncthreads();
+      for (int s2 = 0; s2 < SLOTS; ++s2) keys[wave * 128 + s2 * 64 + lane] = sel.list.v[s2];
+    }
+    __syncthreads();
+    if ((wave & (2 * r - 1)) == 0 && wave + r < nseg) {
+#pragma unroll
+      for (int s2 = 0; s2 < SLOTS; ++s2) sel.list.merge(keys[(wave + r) * 128 + s2 * 64 + lane]);
     }
   }
-  for (int pos = t; pos < k; pos += nt) {
-    const uint64_t key = keys[pos];
-    // every row holds V >= k elements, so the first k slots are filled;
-    // the guard keeps an impossible empty slot inside the row
+  if (wave != 0) return;
+#pragma unroll
+  for (int s2 = 0; s2 < SLOTS; ++s2) {
+    const int pos = s2 * 64 + lane;
+    if (pos >= k) continue;
+    const uint64_t key = sel.list.v[s2];
+    // every row holds V >= k elements, so the first k places are filled;
+    // the guard keeps an impossible empty place inside the row
     const uint32_t idx = key ? sel_key_index(key) : 0u;
     out_idx[static_cast<size_t>(row) * k + pos] = static_cast<int>(idx);
     // re-read the element so the stored probability keeps its exact bits
@@ -371,12 +364,9 @@ TopkPlan topk_plan(int rows, int V, int k) {
   p.k = k;
   p.slots = k <= 64 ? 1 : 2;
   p.vec = (V % 4) == 0;
-  // segments of at least ~8k elements, at most kMaxSegments per row, and
-  // segments * k within the merge buffer
-  int most = kMaxSegments;
-  if (most > kMergeCap / k) most = kMergeCap / k;
+  // segments of at least ~8k elements, at most kMaxSegments per row
   int nseg = (V + 8191) / 8192;
-  if (nseg > most) nseg = most;
+  if (nseg > kMaxSegments) nseg = kMaxSegments;
   if (nseg < 1) nseg = 1;
   int len = (V + nseg - 1) / nseg;
   len = (len + 1023) / 2048 * 2048 + 1024;  // one warm-up block of 1024, then steps of 2048
