@@ -148,9 +148,10 @@ int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
  * 1 <= d_qk, d_v <= 576; B <= 4096.  Accumulation is fp32.
  * Workspace: zero before the first call, see the conventions above.  The key
  * range of a (request, KV head, row block) may be split over several
- * workgroups whose partial results the last of them combines, so the exact
- * rounding of `out` depends on the split sizes (which depend on B, N_max,
- * L_cap and the head shape, never on the data).
+ * workgroups whose partial results are combined in fp32 (for bf16 heads of
+ * width 128 the partial rows are exchanged normalised and rounded to bf16),
+ * so the exact rounding of `out` depends on the split sizes (which depend on
+ * B, N_max, L_cap and the head shape, never on the data or on timing).
  */
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const void* k_tree, const void* v_tree, long kv_row_stride,

@@ -6,21 +6,23 @@
 // attention the tree is a mask over the shared KV -- here, per-node ancestor
 // bitsets applied to the scratch keys of the last tiles.
 //
-// Work decomposition (all on the device, no host round-trip):
-//   * a query row is (node, query head); the rows of one request that share
-//     a KV head form "units" of RB rows;
-//   * each unit's keys are the virtual sequence prefix[0, l_b) ++ scratch[0,
-//     n_b), split into chunks; one work item = (request, KV head, row block,
-//     chunk).  A one-workgroup planner sizes the chunk from the total work so
-//     that about `target_items` items exist, and writes the item list;
-//   * an item streams its keys through LDS in tiles, keeps an online softmax
-//     per row in fp32 and writes either the final row (single chunk) or a
-//     partial (max, sum, accumulator) for the combine kernel.
-// Grouped/latent bf16 shapes use MFMA (v_mfma_f32_16x16x32_bf16): the score
-// tile is computed transposed (keys x rows) so that its output layout is
-// directly the B operand of the value product, and the value tile is stored
-// transposed in LDS (key pairs packed per dword) for the A operand.
-// Other shapes and fp32 use a plain VALU kernel.
+// Work decomposition (all on the device, no host round-trip): a query row is
+// (node, query head); the rows of one request that share a KV head form
+// "units" of RB rows; a unit's keys are the virtual sequence prefix[0, l_b)
+// ++ scratch[0, n_b), cut into chunks (split-K); a work item is (unit, chunk)
+// and keeps an online softmax per row in fp32.  Three paths:
+//   * grouped bf16 heads of width 128: one kernel whose workgroups decode
+//     their item from their id, stream K/V tiles by LDS-DMA and combine the
+//     splits of a unit themselves (the last one to arrive);
+//   * one latent head whose value is the start of the key row (576/512):
+//     128-row items, one K tile in LDS feeding both products, behind a
+//     one-workgroup planner (item list) and a combine kernel;
+//   * every other shape and fp32: a VALU kernel with the same planner and
+//     combine.
+// The MFMA paths compute the score tile transposed (keys x rows), so that
+// its output layout is directly the B operand of the value product
+// (v_mfma_f32_16x16x32_bf16), and read the value operand with
+// ds_read_b64_tr_b16 from rows in their natural layout.
 
 #include "tsv_device.hpp"
 #include "tsv_internal.hpp"
