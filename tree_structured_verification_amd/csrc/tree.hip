@@ -11,7 +11,8 @@
 // better-ranked sibling or its parent.  Each frontier entry is one 64-bit key
 // that orders exactly like the selection order
 //   (score desc, depth asc, parent's position asc, rank asc),
-// so a pop is a wave-wide max over at most 5 keys per lane.  Scores are fp32
+// and the frontier is kept sorted by it across the lanes, so a pop reads
+// lane 0.  Scores are fp32
 // products (never fused); the stop rule is evaluated in fp64 with explicit
 // round-to-nearest operations in a fixed order.
 
@@ -38,9 +39,32 @@ __device__ __forceinline__ double round_cost(const tsv_cost& c, int n, double l)
   return __dadd_rn(c.c_d, v);
 }
 
-// SLOTS frontier entries per lane; the frontier never holds more than
-// 1 + 2 * cap entries, so 64 * SLOTS > 2 * cap suffices.
-template <int SLOTS>
+// The frontier is kept sorted (descending key) across the lanes: position
+// P = 64 * s + lane of slot s.  A pop takes position 0 and shifts the rest
+// down one place; an insert counts the keys above the new one (one ballot
+// per slot) and shifts the positions from there up one place.  The shifts
+// are whole-wavefront DPP moves (wave_shl / wave_shr), the boundary lane
+// taking the neighbouring slot's value, so a round costs no wave-wide
+// reduction.  Capacity 64 * SL >= cap: an entry pushed past it would need
+// more pops than remain to reach the front, so dropping it changes nothing.
+template <int CTRL>
+__device__ __forceinline__ uint32_t wave_shift_u32(uint32_t v, uint32_t fill) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v),
+                                                           CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t wave_shift_u64(uint64_t v, uint64_t fill) {
+  const uint32_t lo = wave_shift_u32<CTRL>(static_cast<uint32_t>(v), static_cast<uint32_t>(fill));
+  const uint32_t hi = wave_shift_u32<CTRL>(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(fill >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+constexpr int kShl1 = 0x130;  // lane l takes lane l + 1 (lane 63 takes the fill)
+constexpr int kShr1 = 0x138;  // lane l takes lane l - 1 (lane 0 takes the fill)
+
+template <int SL>
 __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   __shared__ float s_p[kMaxTopkTable];
   __shared__ int s_i[kMaxTopkTable];
@@ -70,40 +94,59 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       }
     }
   }
+  // the best child of a node at depth d has probability p[d][0]: lane d keeps it
+  const float q_first = lane < a.gamma ? a.tk_p[tbase + static_cast<size_t>(lane) * a.k] : 0.f;
   __syncthreads();
 
-  // Frontier slot = 64-bit order key split in (hi = ordered score bits,
-  // lo = depth/parent/rank fields, 0 = empty) plus the entry's exact score
-  // and its parent's score, so a pop reads everything from the winner lane.
-  // Updates are selects (no lane-dependent branches).
-  uint32_t fhi[SLOTS], flo[SLOTS];
-  float fsc[SLOTS], fps[SLOTS];
+  // entry = order key (0 = empty), its exact score and its parent's score
+  uint64_t fk[SL];
+  float fsc[SL], fps[SL];
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    fhi[s] = 0;
-    flo[s] = 0;
+  for (int s = 0; s < SL; ++s) {
+    fk[s] = 0;
     fsc[s] = 0.f;
     fps[s] = 0.f;
   }
-  int cnt = 0;
-  auto push = [&](float score, float parent_score, int depth, int parent, int rank) {
-    const uint64_t key = frontier_key(score, depth, parent, rank);
-    const uint32_t kh = static_cast<uint32_t>(key >> 32), kl = static_cast<uint32_t>(key);
-    const bool mine = lane == (cnt & 63);
-    const int S = cnt >> 6;
+  auto insert = [&](uint64_t x, float xs, float xp) {
+    int pos = 0;
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const bool w = mine && s == S;
-      fhi[s] = w ? kh : fhi[s];
-      flo[s] = w ? kl : flo[s];
-      fsc[s] = w ? score : fsc[s];
-      fps[s] = w ? parent_score : fps[s];
+    for (int s = 0; s < SL; ++s) pos += __popcll(__ballot(fk[s] > x));
+    uint64_t ck = 0;
+    float cs = 0.f, cp = 0.f;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const uint64_t k63 = readlane_u64(fk[s], 63);
+      const float s63 = readlane_f32(fsc[s], 63), p63 = readlane_f32(fps[s], 63);
+      const uint64_t shk = wave_shift_u64<kShr1>(fk[s], ck);
+      const float shs = __uint_as_float(wave_shift_u32<kShr1>(__float_as_uint(fsc[s]), __float_as_uint(cs)));
+      const float shp = __uint_as_float(wave_shift_u32<kShr1>(__float_as_uint(fps[s]), __float_as_uint(cp)));
+      const int P = s * 64 + lane;
+      const bool keep = P < pos, here = P == pos;
+      fk[s] = keep ? fk[s] : (here ? x : shk);
+      fsc[s] = keep ? fsc[s] : (here ? xs : shs);
+      fps[s] = keep ? fps[s] : (here ? xp : shp);
+      ck = k63;
+      cs = s63;
+      cp = p63;
     }
-    ++cnt;
+  };
+  auto drop_front = [&]() {
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const uint64_t nk = s + 1 < SL ? readlane_u64(fk[s + 1 < SL ? s + 1 : s], 0) : 0;
+      const float ns = s + 1 < SL ? readlane_f32(fsc[s + 1 < SL ? s + 1 : s], 0) : 0.f;
+      const float np = s + 1 < SL ? readlane_f32(fps[s + 1 < SL ? s + 1 : s], 0) : 0.f;
+      fk[s] = wave_shift_u64<kShl1>(fk[s], nk);
+      fsc[s] = __uint_as_float(wave_shift_u32<kShl1>(__float_as_uint(fsc[s]), __float_as_uint(ns)));
+      fps[s] = __uint_as_float(wave_shift_u32<kShl1>(__float_as_uint(fps[s]), __float_as_uint(np)));
+    }
   };
 
   // the root's best child: score 1 * q, depth 1, rank 0
-  push(__fmul_rn(1.0f, s_p[0]), 1.0f, 1, -1, 0);
+  {
+    const float r0 = __fmul_rn(1.0f, s_p[0]);
+    insert(frontier_key(r0, 1, -1, 0), r0, 1.0f);
+  }
 
   const double l = a.adaptive ? static_cast<double>(a.prefix_len[b]) : 0.0;
   double phi = 0.0;
@@ -111,36 +154,16 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 
   int m = 0;
   while (m < a.cap) {
-    // best slot of this lane (hi, then lo)
-    uint32_t bh = fhi[0], bl = flo[0];
-    int bs = 0;
-    float bsc = fsc[0], bps = fps[0];
-#pragma unroll
-    for (int s = 1; s < SLOTS; ++s) {
-      const bool better = fhi[s] > bh || (fhi[s] == bh && flo[s] > bl);
-      bh = better ? fhi[s] : bh;
-      bl = better ? flo[s] : bl;
-      bs = better ? s : bs;
-      bsc = better ? fsc[s] : bsc;
-      bps = better ? fps[s] : bps;
-    }
-    const uint32_t wh = wave_max_u32(bh);
-    if (wh == 0) break;  // every candidate taken
-    uint64_t cand = __ballot(bh == wh);
-    uint32_t wl;
-    if (__popcll(cand) == 1) {
-      wl = __builtin_amdgcn_readlane(bl, __ffsll(static_cast<long long>(cand)) - 1);
-    } else {  // equal scores: settle by depth, parent position, rank
-      wl = wave_max_u32(bh == wh ? bl : 0u);
-      cand = __ballot(bh == wh && bl == wl);
-    }
-    const int wlane = __ffsll(static_cast<long long>(cand)) - 1;
-    const int wslot = __builtin_amdgcn_readlane(bs, wlane);
+    const uint64_t hk = readlane_u64(fk[0], 0);
+    if (hk == 0) break;  // every candidate taken
+    const uint32_t wl = static_cast<uint32_t>(hk);
     const int rank = 127 - static_cast<int>(wl & 127);
     const int par = 255 - static_cast<int>((wl >> 7) & 255) - 1;
     const int dep = 63 - static_cast<int>((wl >> 15) & 63) + 1;
-    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsc), wlane));
-    const float ps = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bps), wlane));
+    const float sc = readlane_f32(fsc[0], 0);
+    const float ps = readlane_f32(fps[0], 0);
+    const float q_sib = rank + 1 < a.k ? s_p[(dep - 1) * a.k + rank + 1] : 0.f;
+    const float q_kid = dep < a.gamma ? readlane_f32(q_first, dep) : 0.f;
     if (a.adaptive) {
       const double phi2 = __dadd_rn(phi, static_cast<double>(sc));
       const double th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, m + 1, l));
@@ -154,16 +177,15 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       n_rank[m] = rank;
       n_sc[m] = sc;
     }
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const bool w = lane == wlane && s == wslot;
-      fhi[s] = w ? 0u : fhi[s];
-      flo[s] = w ? 0u : flo[s];
+    drop_front();
+    if (rank + 1 < a.k) {
+      const float v = __fmul_rn(ps, q_sib);
+      insert(frontier_key(v, dep, par, rank + 1), v, ps);
     }
-    const float q_sib = rank + 1 < a.k ? s_p[(dep - 1) * a.k + rank + 1] : 0.f;
-    const float q_kid = dep < a.gamma ? s_p[dep * a.k] : 0.f;
-    if (rank + 1 < a.k) push(__fmul_rn(ps, q_sib), ps, dep, par, rank + 1);
-    if (dep < a.gamma) push(__fmul_rn(sc, q_kid), sc, dep + 1, m, 0);
+    if (dep < a.gamma) {
+      const float v = __fmul_rn(sc, q_kid);
+      insert(frontier_key(v, dep + 1, m, 0), v, sc);
+    }
     ++m;
   }
   const int n = m;
@@ -202,16 +224,11 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 }  // namespace
 
 hipError_t launch_best_first(const TreeArgs& a, hipStream_t s) {
-  // frontier entries: at most 1 + 2 * cap (each pop adds two, removes one)
-  const int need = 1 + 2 * a.cap;
-  if (need <= 64)
+  // sorted frontier of 64 or 128 places (at least cap)
+  if (a.cap <= 64)
     best_first_kernel<1><<<dim3(a.B), dim3(64), 0, s>>>(a);
-  else if (need <= 128)
-    best_first_kernel<2><<<dim3(a.B), dim3(64), 0, s>>>(a);
-  else if (need <= 192)
-    best_first_kernel<3><<<dim3(a.B), dim3(64), 0, s>>>(a);
   else
-    best_first_kernel<5><<<dim3(a.B), dim3(64), 0, s>>>(a);
+    best_first_kernel<2><<<dim3(a.B), dim3(64), 0, s>>>(a);
   return hipGetLastError();
 }
 
