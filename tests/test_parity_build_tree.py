@@ -47,7 +47,7 @@ def test_ties_segments_and_vocab_tail(top_k, V):
     rng = np.random.default_rng(top_k * 7 + V)
     marg = _quantised(rng, (3, 5, V), 4)
     N_max = 128
-    for n_budget in (0, 1, 17, 128):
+    for n_budget in (0, 1, 17, 64, 65, 128):   # 64 / 65: the two frontier capacities
         _run(marg, top_k, n_budget, N_max)
 
 
