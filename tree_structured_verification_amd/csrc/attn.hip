@@ -983,24 +983,6 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) o[dd][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // S^T of tile j from slot base sb: lane holds S^T[key 16*kb + 4*lq + i][row lr]
-  auto scores = [&](f32x4 (&s)[2][2], uint32_t sb) {
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const char* base = smem + (sb - lds0);
-#pragma unroll
-    for (int k = 0; k < NC; ++k)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t off = k < 16 ? kofs[k & 3] + kb * 16384 + (k >> 2) * 1024 : ktl[k - 16] + kb * 2048;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(base + off);
-#pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
-          s[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][k], s[rg][kb], 0, 0, 0);
-      }
-  };
   auto mask = [&](f32x4 (&s)[2][2], int j) {
     const int t0 = k_beg + j * KT;
     if (t0 + KT <= k_end && t0 + KT <= l_b) return;
@@ -1038,18 +1020,38 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
     vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off + 16384));
     return vf.v;
   };
-  // Phase 1 of a step: the scores of tile j+1 (36 groups of one K operand
-  // read, issued two groups ahead, and two MFMAs) with the softmax of tile j
-  // cut into small pieces, one after each group, so that the VALU work runs
-  // while the matrix cores are busy.  The scheduling barriers keep that order.
-  // The weights, rescale factors and flag of tile j go to LDS.
-  auto phase1 = [&](f32x4 (&s)[2][2], uint32_t sb, f32x4 (&x)[2][2], int j) {
-    const uint32_t buf = static_cast<uint32_t>(j & 1);
+  // The scores of a tile: 36 groups of one K operand read (issued two
+  // groups ahead) and two MFMAs; lane holds S^T[key 16*kb + 4*lq + i][row lr].
+  auto scores_p = [&](f32x4 (&s)[2][2], uint32_t sb) {
     const char* kbase = smem + (sb - lds0);
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 kf[3];
+    kf[0] = kread(kbase, 0);
+    kf[1] = kread(kbase, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < 2 * NC; ++n) {
+      if (n + 2 < 2 * NC) kf[(n + 2) % 3] = kread(kbase, n + 2);
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+        s[rg][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n % 3], qf[rg][n >> 1], s[rg][n & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // The value product of tile j,
+  //   O^T[128w + 16dd + ..][rows] += V^T[..][keys of tile j] P^T(j),
+  // the transposed value operand of block dd+1 read while block dd's eight
+  // MFMAs run, with the softmax of tile j+1 (scores x) cut into small pieces
+  // between the MFMA groups, so that the VALU work runs while the matrix
+  // cores are busy (the scheduling barriers keep that order).  Weights,
+  // rescale factors and flags of tile j+1 go to LDS buffer (j+1) & 1.
+  auto values_softmax = [&](auto with_values, uint32_t sv, int j, f32x4 (&x)[2][2]) {
+    constexpr bool WV = decltype(with_values)::value != 0;
+    const uint32_t buf = static_cast<uint32_t>(j & 1), nbuf = buf ^ 1u;
+    const char* vbase = smem + (sv - lds0);
     float mx[2], mt[2], muse[2], ps[2], alpha[2];
     bf16x8 pf[2];
     bool moved = false;
@@ -1080,52 +1082,40 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
         pf[rg][e] = static_cast<__bf16>(p);
       } else {
         lsum[rg] += ps[rg];
-        *reinterpret_cast<bf16x8*>(smem + kLatP + buf * 8192 + (2 * wave + rg) * 1024 + prow) = pf[rg];
+        *reinterpret_cast<bf16x8*>(smem + kLatP + nbuf * 8192 + (2 * wave + rg) * 1024 + prow) = pf[rg];
       }
     };
-    bf16x8 kf[3];
-    kf[0] = kread(kbase, 0);
-    kf[1] = kread(kbase, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int n = 0; n < 2 * NC; ++n) {
-      if (n + 2 < 2 * NC) kf[(n + 2) % 3] = kread(kbase, n + 2);
+    auto publish = [&]() {
+      // written by every lane, without branches and to distinct addresses
+      // (each of the four lanes of a row keeps its own copy of the factor,
+      // each lane its own copy of the wave's flag)
+      const bool any = __ballot(moved) != 0;
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg)
-        s[rg][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n % 3], qf[rg][n >> 1], s[rg][n & 1], 0, 0, 0);
-      if (n < 26) piece(n / 13, n % 13);
-      if (n == 26) {
-        // written by every lane, without branches and to distinct addresses
-        // (each of the four lanes of a row keeps its own copy of the factor,
-        // each lane its own copy of the wave's flag)
-        const bool any = __ballot(moved) != 0;
+        *reinterpret_cast<float*>(smem + kLatAlpha + nbuf * 2048 + lq * 512 + (lr * 8 + 2 * wave + rg) * 4) = alpha[rg];
+      *reinterpret_cast<int*>(smem + kLatFlag + nbuf * 1024 + wave * 256 + lane * 4) = any ? 1 : 0;
+    };
+    bf16x8 pt[8], vf[2];
+    if constexpr (WV) {
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
-          *reinterpret_cast<float*>(smem + kLatAlpha + buf * 2048 + lq * 512 + (lr * 8 + 2 * wave + rg) * 4) = alpha[rg];
-        *reinterpret_cast<int*>(smem + kLatFlag + buf * 1024 + wave * 256 + lane * 4) = any ? 1 : 0;
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int rb = 0; rb < 8; ++rb)
+        pt[rb] = *reinterpret_cast<const bf16x8*>(smem + kLatP + buf * 8192 + rb * 1024 + prow);
+      vf[0] = vread(vbase, 0);
     }
-  };
-  // Phase 2: O^T[128w + 16dd + ..][rows] += V^T[..][keys of tile j] P^T(j),
-  // the transposed value operand of block dd+1 read while block dd's eight
-  // MFMAs run.
-  auto phase2 = [&](uint32_t sv, int j) {
-    const uint32_t buf = static_cast<uint32_t>(j & 1);
-    const char* vbase = smem + (sv - lds0);
-    bf16x8 pt[8];
-#pragma unroll
-    for (int rb = 0; rb < 8; ++rb)
-      pt[rb] = *reinterpret_cast<const bf16x8*>(smem + kLatP + buf * 8192 + rb * 1024 + prow);
-    bf16x8 vf[2];
-    vf[0] = vread(vbase, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-      if (dd + 1 < 8) vf[(dd + 1) & 1] = vread(vbase, dd + 1);
+      if (WV && dd + 1 < 8) vf[(dd + 1) & 1] = vread(vbase, dd + 1);
 #pragma unroll
-      for (int rb = 0; rb < 8; ++rb)
-        o[dd][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd & 1], pt[rb], o[dd][rb], 0, 0, 0);
+      for (int rb = 0; rb < 8; ++rb) {
+        if constexpr (WV)
+          o[dd][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd & 1], pt[rb], o[dd][rb], 0, 0, 0);
+        // 26 pieces and the publication over the 64 MFMAs: one after every
+        // second MFMA of the first 54
+        const int slot = dd * 8 + rb;
+        if ((slot & 1) && (slot >> 1) < 26) piece((slot >> 1) / 13, (slot >> 1) % 13);
+        if (slot == 55) publish();
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1148,31 +1138,26 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
   f32x4 sc[2][2], sn[2][2];
   wait_vmcnt<0>();
   lds_barrier();
-  scores(sc, lds0);
+  scores_p(sc, lds0);
   mask(sc, 0);
+  values_softmax(IC<0>{}, lds0, -1, sc);   // the weights of tile 0 alone
 
-  // Step t: (1) the scores of tile t+1 beside the softmax of tile t, (2)
-  // after a barrier that publishes the weights, the value product of tile t.
-  // The last step scores a stale slot as tile nt, whose keys all lie past
-  // k_end (fully masked, never used).
+  // Step t: the scores of tile t+1, then the value product of tile t beside
+  // the softmax of tile t+1, whose weights the next step reads.  The last
+  // step scores a stale slot as tile nt, whose keys all lie past k_end: fully
+  // masked, it leaves every row's max and sum unchanged.
   uint32_t s_cur = lds0, s_nxt = lds0 + kLatTile, s_aft = lds0 + 2 * kLatTile;
   for (int t = 0; t < nt; ++t) {
-    // tile t+1 resident; every wave is done with step t-1 (its weights and
-    // tile t-1, whose slot takes tile t+2)
+    // tile t+1 resident and the weights of tile t posted; every wave is done
+    // with tile t-1, whose slot takes tile t+2
     wait_all_mem();
     lds_barrier();
     if (t + 2 < nt) issue(t + 2, s_aft);
     asm volatile("" : "+v"(vrow), "+v"(vsw));
-    phase1(sn, s_nxt, sc, t);
-    mask(sn, t + 1);
-    wait_lgkm0();   // this wave's weights written (tile t+2 stays in flight)
-    lds_barrier();
     rescale(t);
-    phase2(s_cur, t);
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sc[rg][kb] = sn[rg][kb];
+    scores_p(sn, s_nxt);
+    mask(sn, t + 1);
+    values_softmax(IC<1>{}, s_cur, t, sn);
     const uint32_t s_old = s_cur;
     s_cur = s_nxt;
     s_nxt = s_aft;
