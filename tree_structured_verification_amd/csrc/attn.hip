@@ -1020,7 +1020,7 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
     vf.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TSV_LDS4(vbase + off + 16384));
     return vf.v;
   };
-  // The scores of a tile: 36 groups of one K operand read (issued two
+  // The scores of a tile: 36 groups of one K operand read (issued six
   // groups ahead) and two MFMAs; lane holds S^T[key 16*kb + 4*lq + i][row lr].
   auto scores_p = [&](f32x4 (&s)[2][2], uint32_t sb) {
     const char* kbase = smem + (sb - lds0);
@@ -1028,16 +1028,17 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 kf[3];
-    kf[0] = kread(kbase, 0);
-    kf[1] = kread(kbase, 1);
+    constexpr int AH = 6;   // operand reads in flight
+    bf16x8 kf[AH + 1];
+#pragma unroll
+    for (int n = 0; n < AH; ++n) kf[n] = kread(kbase, n);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < 2 * NC; ++n) {
-      if (n + 2 < 2 * NC) kf[(n + 2) % 3] = kread(kbase, n + 2);
+      if (n + AH < 2 * NC) kf[(n + AH) % (AH + 1)] = kread(kbase, n + AH);
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg)
-        s[rg][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n % 3], qf[rg][n >> 1], s[rg][n & 1], 0, 0, 0);
+        s[rg][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n % (AH + 1)], qf[rg][n >> 1], s[rg][n & 1], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
