@@ -702,7 +702,11 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
   // instruction covers 512 contiguous bytes: per (unit, split), per (wave,
   // row group): normalised rows [d][lane] as 4 x bf16, and the row (max,
   // sum) pairs [lr] as float2.
+  // own[rg][d] keeps this split's rows exactly as published, so that the
+  // combine computes its term like every other split's (same bits whichever
+  // split arrives last); the fp32 accumulators are dead from here on.
   const size_t item = static_cast<size_t>(unit) * a.S + c.split;
+  float2 own[RG][NDB];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const int wr = wave * RG + rg;
@@ -717,6 +721,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
       } pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk.h4[i] = static_cast<__bf16>(o[rg][d][i] * inv);
+      own[rg][d] = pk.f;
       st_coherent2(pa + d * 64 + lane, pk.f.x, pk.f.y);
     }
     if (lq == 0)
@@ -731,57 +736,122 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // no stale cached copy of the rows
 
+  // Each load below goes to the level shared by all XCDs: under the key
+  // stream of the other workgroups a round trip costs over a microsecond, so
+  // loads are issued in as few dependent groups as the registers allow.
+  const int ns = c.splits, own_s = c.split;
+  auto ml_ptr = [&](int s2, int wr) {
+    return reinterpret_cast<const uint64_t*>(a.part_ml + (static_cast<size_t>(unit) * a.S + s2) * RB * 2) +
+           wr * 16 + lr;
+  };
+  auto rows_ptr = [&](int s2, int wr) {
+    return reinterpret_cast<const uint64_t*>(a.part_acc + (static_cast<size_t>(unit) * a.S + s2) * RB * D) +
+           static_cast<size_t>(wr) * NDB * 64 + lane;
+  };
+  // one split's term of the combined row, weighted by 2^(m - M) * l; the
+  // terms are summed in split order whichever split arrived last
+  auto term = [&](float m, float l, const float2 (&r)[NDB], float Mx, float& L, f32x4 (&acc)[NDB]) {
+    const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - Mx);
+    L = fmaf(w, l, L);
+    const float wl = w * l;   // weight of the normalised row
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int wr = wave * RG + rg;
-    auto ml_of = [&](int s2) {
-      return ld_coherent2(reinterpret_cast<const uint64_t*>(a.part_ml + (static_cast<size_t>(unit) * a.S + s2) * RB * 2) +
-                          wr * 16 + lr);
-    };
-    float M = m_run[rg];
-    for (int s2 = 0; s2 < c.splits; ++s2) {
-      if (s2 == c.split) continue;
-      M = fmaxf(M, ml_of(s2).x);
+    for (int d = 0; d < NDB; ++d) {
+      const uint32_t u0 = __float_as_uint(r[d].x), u1 = __float_as_uint(r[d].y);
+      acc[d][0] = fmaf(wl, __uint_as_float(u0 << 16), acc[d][0]);
+      acc[d][1] = fmaf(wl, __uint_as_float(u0 & 0xFFFF0000u), acc[d][1]);
+      acc[d][2] = fmaf(wl, __uint_as_float(u1 << 16), acc[d][2]);
+      acc[d][3] = fmaf(wl, __uint_as_float(u1 & 0xFFFF0000u), acc[d][3]);
     }
-    // summed in split order whichever split arrived last, so that the bits
-    // do not depend on the arrival order
-    float L = 0.f;
-    f32x4 acc[NDB];
+  };
+
+  constexpr int kR = 3;  // other splits held in registers at once
+  if (ns <= kR + 1) {
+    // every other split's pairs and rows, both row groups, in one group of
+    // loads.  Slot j holds split j + (j >= own_s); slots past the last
+    // split repeat it and are never used.
+    const int nr = ns - 1;
+    auto split_of = [&](int j) { const int r = min(j, nr - 1); return r + (r >= own_s ? 1 : 0); };
+    float2 mlr[RG][kR], rws[RG][kR][NDB];
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < c.splits; ++s2) {
-      if (s2 == c.split) {
-        // this split's rows from registers, rounded exactly as published, so
-        // that the sum is the same whichever split arrives last
-        const float lt = lacc[rg][0];
-        const float w = m_run[rg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rg] - M);
-        L = fmaf(w, lt, L);
-        const float wl = w * lt;
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    for (int j = 0; j < kR; ++j)
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+      for (int rg = 0; rg < RG; ++rg) mlr[rg][j] = ld_coherent2(ml_ptr(split_of(j), wave * RG + rg));
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[d][i] = fmaf(wl, static_cast<float>(static_cast<__bf16>(o[rg][d][i] * inv)), acc[d][i]);
-        continue;
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int j = 0; j < kR; ++j) {
+        const uint64_t* pa = rows_ptr(split_of(j), wave * RG + rg);
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) rws[rg][j][d] = ld_coherent2(pa + d * 64);
       }
-      const float2 ml = ml_of(s2);
-      const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      L = fmaf(w, ml.y, L);
-      const float wl = w * ml.y;   // weight of the normalised row
-      const uint64_t* pa = reinterpret_cast<const uint64_t*>(a.part_acc + (static_cast<size_t>(unit) * a.S + s2) * RB * D) +
-                           static_cast<size_t>(wr) * NDB * 64;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        const float2 v = ld_coherent2(pa + d * 64 + lane);
-        const uint32_t u0 = __float_as_uint(v.x), u1 = __float_as_uint(v.y);
-        acc[d][0] = fmaf(wl, __uint_as_float(u0 << 16), acc[d][0]);
-        acc[d][1] = fmaf(wl, __uint_as_float(u0 & 0xFFFF0000u), acc[d][1]);
-        acc[d][2] = fmaf(wl, __uint_as_float(u1 << 16), acc[d][2]);
-        acc[d][3] = fmaf(wl, __uint_as_float(u1 & 0xFFFF0000u), acc[d][3]);
+    for (int rg = 0; rg < RG; ++rg) {
+      float M = m_run[rg];
+#pragma unroll
+      for (int j = 0; j < kR; ++j) M = fmaxf(M, j < nr ? mlr[rg][j].x : -INFINITY);
+      float L = 0.f;
+      f32x4 acc[NDB];
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // slots in split order, this split's own term inserted before slot
+      // own_s (or after the last slot)
+#pragma unroll
+      for (int j = 0; j < kR; ++j) {
+        if (j == own_s) term(m_run[rg], lacc[rg][0], own[rg], M, L, acc);
+        if (j >= nr) break;
+        term(mlr[rg][j].x, mlr[rg][j].y, rws[rg][j], M, L, acc);
       }
+      if (own_s == nr && nr >= kR) term(m_run[rg], lacc[rg][0], own[rg], M, L, acc);
+      write_row(rg, acc, M, L);
     }
-    write_row(rg, acc, M, L);
+  } else {
+    // many splits: the pairs of up to kMl splits, then the rows of kAcc
+    // splits at a time
+    constexpr int kMl = 8, kAcc = 2;
+    float M[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) M[rg] = m_run[rg];
+    for (int s0 = 0; s0 < ns; s0 += kMl) {
+      float2 v[RG][kMl];
+#pragma unroll
+      for (int j = 0; j < kMl; ++j)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) v[rg][j] = ld_coherent2(ml_ptr(min(s0 + j, ns - 1), wave * RG + rg));
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int j = 0; j < kMl; ++j) M[rg] = fmaxf(M[rg], v[rg][j].x);
+    }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const int wr = wave * RG + rg;
+      float L = 0.f;
+      f32x4 acc[NDB];
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < ns; s0 += kAcc) {
+        float2 mlv[kAcc], rows[kAcc][NDB];
+#pragma unroll
+        for (int j = 0; j < kAcc; ++j) {
+          const int s2 = min(s0 + j, ns - 1);
+          mlv[j] = ld_coherent2(ml_ptr(s2, wr));
+          const uint64_t* pa = rows_ptr(s2, wr);
+#pragma unroll
+          for (int d = 0; d < NDB; ++d) rows[j][d] = ld_coherent2(pa + d * 64);
+        }
+#pragma unroll
+        for (int j = 0; j < kAcc; ++j) {
+          const int s2 = s0 + j;
+          if (s2 >= ns) break;
+          if (s2 == own_s) term(m_run[rg], lacc[rg][0], own[rg], M[rg], L, acc);
+          else term(mlv[j].x, mlv[j].y, rows[j], M[rg], L, acc);
+        }
+      }
+      write_row(rg, acc, M[rg], L);
+      // keeps the next row group's loads below this one's arithmetic (both
+      // groups' rows in flight at once would not fit the register file)
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if (tid == 0) a.counters[unit] = 0;
 }
