@@ -11,6 +11,7 @@
  *
  * A round is four calls, in this order:
  *   build_tree        drafter marginals -> best-first draft tree (+ budget)
+ *                     (or build_tree_expand: per-node distributions -> tree)
  *   tree_verify_attn  branch-aware attention of every tree node
  *   accept_walk       target argmax -> longest accepted root-to-node path
  *   commit_path       accepted scratch KV -> persistent cache
@@ -120,6 +121,42 @@ int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * build_tree_expand -- the same tree from per-node conditional expansion.
+ *
+ * [review] "How it works", steps 1-2, and its notation (s draft steps,
+ * top-k, budget D): the drafter runs s steps; at each step every node of the
+ * newest level branches into the top-k tokens of its OWN next-token
+ * distribution (the toy: A -> {B, C}, then B -> {B, C} and C -> {A, B}), and
+ * the candidates are pruned to the budget by cumulative score.  [review] "Our
+ * perspective": pruning by cumulative score.  The budget rules are
+ * build_tree's ([caddtree] Methodology, items 2-4).
+ *
+ * Inputs
+ *   probs       fp32 [B][P][V]  the expanded nodes' next-token distributions
+ *               (finite, >= 0), P = 1 + k + ... + k^(steps-1), in level order
+ *               of the complete k-ary expansion: row 0 is the root's (the last
+ *               accepted token), and the child of rank r (in the top-k order
+ *               below) of the node with row i has row k*i + 1 + r.  Nodes of
+ *               depth `steps` are leaves and have no row.
+ *   steps       1 <= steps <= 64 (maximum depth)
+ *   top_k       1 <= top_k <= min(V, 128); P * top_k <= 4096
+ *   n_budget, cost, prefix_len, N_max   as for build_tree
+ * Outputs       as for build_tree, with depth = draft step and
+ *   topk_idx    int32 [B][P][top_k] or NULL   each row's top-k ids
+ *   topk_p      fp32  [B][P][top_k] or NULL   and their probabilities
+ * Order, ties and arithmetic are build_tree's: a candidate's score is the
+ * fp32 product of the probabilities along its path, nodes are numbered by
+ * the nested key (-score, depth, key(parent), rank), so the tree is
+ * ancestor-closed and parents precede children.
+ * Workspace: tsv_workspace_size(4, B, steps, V, top_k, N_max, ...).
+ */
+int build_tree_expand(const float* probs, int B, int steps, int V, int top_k,
+                      int n_budget, const tsv_cost* cost, const int* prefix_len,
+                      int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                      float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * tree_verify_attn -- branch-aware tree attention over a shared prefix.
  *
  * [review] Difficulty 1 (paper section 3.1) and "How it works", step 3: each
@@ -207,7 +244,8 @@ int commit_path(void* k_cache, void* v_cache, int* prefix_len,
                 int dtype, int* status, void* stream);
 
 /* Workspace bytes needed by entry point `which` (0 build_tree,
- * 1 tree_verify_attn, 2 accept_walk, 3 commit_path) for these sizes.
+ * 1 tree_verify_attn, 2 accept_walk, 3 commit_path, 4 build_tree_expand,
+ * whose `gamma` argument is its number of steps) for these sizes.
  * Arguments an entry point does not use are ignored.  Returns 0 for
  * invalid sizes. */
 size_t tsv_workspace_size(int which, int B, int gamma, int V, int top_k,

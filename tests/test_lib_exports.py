@@ -21,8 +21,8 @@ def _declared():
 
 def test_all_declared_symbols_exported():
     names = _declared()
-    assert names == sorted(["build_tree", "tree_verify_attn", "accept_walk", "commit_path",
-                            "tsv_workspace_size", "tsv_status_string"])
+    assert names == sorted(["build_tree", "build_tree_expand", "tree_verify_attn", "accept_walk",
+                            "commit_path", "tsv_workspace_size", "tsv_status_string"])
     lib = ctypes.CDLL(tsv._lib.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -43,6 +43,11 @@ def test_workspace_sizes():
     assert ws(1, 16, 1, 1, 1, 32, 4112, 30, 8, 128, 128, 1) == 0    # Hq % Hkv
     assert ws(2, 16, 16, 151936, 1, 32, dtype=1) > 0
     assert ws(3) == 0
+    assert ws(4, 8, 3, 129280, 2, 8) > 0            # 7 expanded rows of top-2
+    assert ws(4, 1, 11, 16, 2, 8) > 0               # 2047 rows x 2 = 4094 list entries
+    assert ws(4, 1, 12, 16, 2, 8) == 0              # 4095 rows x 2 > 4096
+    assert ws(4, 1, 6, 16, 4, 8) == 0               # 1365 rows x 4 > 4096
+    assert ws(4, 1, 65, 16, 1, 8) == 0              # depth beyond 64
     # larger caps never need less workspace
     assert ws(1, 64, 1, 1, 1, 128, 32784, 32, 8, 128, 128, 1) >= ws(1, 16, 1, 1, 1, 32, 4112, 32, 8, 128, 128, 1)
 
@@ -72,6 +77,16 @@ def test_host_validation_without_launch():
     assert L.tree_verify_attn(p, p, p, p, p, 1200, p, p, p, 1, 4, 10, 4, 2, 600, 64, 1, 0.1,
                               p, nul, p, 1 << 30, nul) == -2      # head dim > 576
     assert L.accept_walk(p, 1, 1, 4, 8, 65, p, p, p, p, p, p, p, 1 << 20, nul) == -2  # gamma
+    assert L.build_tree_expand(nul, 1, 2, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                               1 << 20, nul) == -1                # null probabilities
+    assert L.build_tree_expand(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                               1 << 20, nul) == -1                # top_k > V
+    assert L.build_tree_expand(p, 1, 6, 16, 4, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                               1 << 20, nul) == -2                # list table too large
+    assert L.build_tree_expand(p, 1, 3, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                               16, nul) == -3                     # workspace too small
+    assert L.build_tree_expand(p, 1, 3, 8, 2, 9, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                               1 << 20, nul) == -1                # budget > N_max
     assert L.commit_path(p, nul, p, p, p, 64, p, p, 1, 4, 8, 1, 64, 64, 2, 1, p, nul) == -1
 
 

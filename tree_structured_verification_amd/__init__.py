@@ -1,7 +1,8 @@
 """Tree-structured speculative verification on AMD Instinct MI355X (gfx950).
 
 One verification round = four calls into the HIP library libtsv.so
-(include/tsv.h): build_tree, tree_verify_attn, accept_walk, commit_path.
+(include/tsv.h): build_tree (or build_tree_expand), tree_verify_attn,
+accept_walk, commit_path.
 This package is the thin Python binding over that C ABI.
 """
 
@@ -11,6 +12,8 @@ from ._lib import (  # noqa: F401
     TsvError,
     accept_walk,
     build_tree,
+    build_tree_expand,
+    expanded_rows,
     commit_path,
     lib,
     status_string,

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libtsv.so")
 
 TSV_F32, TSV_BF16 = 0, 1
 TSV_OK, TSV_EINVAL, TSV_EUNSUPPORTED, TSV_EWORKSPACE, TSV_EHIP = 0, -1, -2, -3, -4
-WS_BUILD, WS_ATTN, WS_WALK, WS_COMMIT = 0, 1, 2, 3
+WS_BUILD, WS_ATTN, WS_WALK, WS_COMMIT, WS_EXPAND = 0, 1, 2, 3, 4
 
 
 class TsvError(RuntimeError):
@@ -43,6 +43,8 @@ _F = ctypes.c_float
 _SIGS = {
     "build_tree": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "build_tree_expand": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
+                          _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "tree_verify_attn": [_P, _P, _P, _P, _P, _L, _P, _P, _P, _I, _I, _I, _I, _I,
                          _I, _I, _I, _F, _P, _P, _P, _S, _P],
     "accept_walk": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
@@ -159,6 +161,50 @@ def build_tree(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: int,
         _ptr(out.get("topk_idx")), _ptr(out.get("topk_p")), _ptr(ws), ws.numel(),
         _stream(dev))
     _check("build_tree", code)
+    return out
+
+
+def expanded_rows(steps: int, top_k: int) -> int:
+    """Rows of build_tree_expand's input per request: 1 + k + ... + k^(steps-1)."""
+    return sum(top_k ** d for d in range(steps))
+
+
+def build_tree_expand(probs: torch.Tensor, steps: int, top_k: int, n_budget: int, N_max: int,
+                      cost=None, prefix_len: Optional[torch.Tensor] = None,
+                      with_topk: bool = False, out: Optional[dict] = None,
+                      ws: Optional[torch.Tensor] = None) -> dict:
+    """probs fp32 [B, P, V]: the expanded nodes' distributions in level order
+    (P = expanded_rows(steps, top_k)); outputs as for build_tree."""
+    _dev(probs, "probs", torch.float32)
+    B, P, V = probs.shape
+    if P != expanded_rows(steps, top_k):
+        raise ValueError(f"probs has {P} rows per request, {steps} steps of top-{top_k} "
+                         f"need {expanded_rows(steps, top_k)}")
+    dev = probs.device
+    W = (N_max + 31) // 32
+    if out is None:
+        out = dict(
+            n_nodes=torch.empty(B, dtype=torch.int32, device=dev),
+            parent=torch.empty(B, N_max, dtype=torch.int32, device=dev),
+            token=torch.empty(B, N_max, dtype=torch.int32, device=dev),
+            depth=torch.empty(B, N_max, dtype=torch.int32, device=dev),
+            score=torch.empty(B, N_max, dtype=torch.float32, device=dev),
+            anc_bits=torch.empty(B, N_max, W, dtype=torch.int32, device=dev),
+        )
+        if with_topk:
+            out["topk_idx"] = torch.empty(B, P, top_k, dtype=torch.int32, device=dev)
+            out["topk_p"] = torch.empty(B, P, top_k, dtype=torch.float32, device=dev)
+    if prefix_len is not None:
+        _dev(prefix_len, "prefix_len", torch.int32)
+    if ws is None:
+        ws = workspace(workspace_size(WS_EXPAND, B, steps, V, top_k, N_max), dev)
+    code = lib().build_tree_expand(
+        _ptr(probs), B, steps, V, top_k, n_budget, _cost_struct(cost),
+        _ptr(prefix_len), N_max, _ptr(out["n_nodes"]), _ptr(out["parent"]),
+        _ptr(out["token"]), _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc_bits"]),
+        _ptr(out.get("topk_idx")), _ptr(out.get("topk_p")), _ptr(ws), ws.numel(),
+        _stream(dev))
+    _check("build_tree_expand", code)
     return out
 
 

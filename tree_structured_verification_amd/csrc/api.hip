@@ -24,13 +24,17 @@ bool dtype_ok(int dtype) { return dtype == TSV_F32 || dtype == TSV_BF16; }
 
 bool finite_nonneg(double x) { return isfinite(x) && x >= 0.0; }
 
+int launch_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_EHIP; }
+
 struct BuildLayout {
   TopkPlan plan;
   size_t off_seg, off_idx, off_p, bytes;
 };
-BuildLayout build_layout(int B, int gamma, int V, int top_k) {
+// rows_per_b: top-k lists per request (gamma positions, or the expanded
+// nodes of build_tree_expand)
+BuildLayout build_layout(int B, int rows_per_b, int V, int top_k) {
   BuildLayout L;
-  const int rows = B * gamma;
+  const int rows = B * rows_per_b;
   L.plan = topk_plan(rows, V, top_k);
   size_t off = 0;
   L.off_seg = off;
@@ -49,6 +53,70 @@ bool build_sizes_ok(int B, int gamma, int V, int top_k, int N_max) {
   if (gamma * top_k > kMaxTopkTable) return false;
   if (static_cast<long long>(B) * gamma > (1LL << 24)) return false;
   return true;
+}
+
+// Expanded nodes of an s-step, k-ary expansion: 1 + k + ... + k^(s-1), or
+// -1 when that exceeds kMaxTopkTable (the tree kernel's list table).
+int expanded_rows(int steps, int k) {
+  long long rows = 0, level = 1;
+  for (int d = 0; d < steps; ++d) {
+    rows += level;
+    if (rows > kMaxTopkTable) return -1;
+    level *= k;
+    if (level > kMaxTopkTable) level = kMaxTopkTable + 1;
+  }
+  return static_cast<int>(rows);
+}
+
+bool expand_sizes_ok(int B, int steps, int V, int top_k, int N_max) {
+  if (B < 1 || steps < 1 || V < 1 || top_k < 1 || N_max < 1) return false;
+  if (steps > kMaxGamma || N_max > kMaxNodes || top_k > kMaxTopk || top_k > V) return false;
+  const int P = expanded_rows(steps, top_k);
+  if (P < 0 || static_cast<long long>(P) * top_k > kMaxTopkTable) return false;
+  if (static_cast<long long>(B) * P > (1LL << 24)) return false;
+  return true;
+}
+
+bool cost_ok(const tsv_cost* cost) {
+  return isfinite(cost->a) && isfinite(cost->c_d) && cost->a + cost->c_d > 0.0 &&
+         finite_nonneg(cost->b) && finite_nonneg(cost->c) && finite_nonneg(cost->e);
+}
+
+// top-k of every list, then the best-first tree; shared by both builders
+int launch_build(const float* probs, int B, int rows_per_b, int steps, int V, int top_k,
+                 int n_budget, const tsv_cost* cost, const int* prefix_len, int N_max,
+                 int* n_nodes, int* parent, int* token, int* depth, float* score,
+                 unsigned* anc_bits, int* topk_idx, float* topk_p, void* ws,
+                 size_t ws_bytes, void* stream, bool per_node) {
+  const BuildLayout L = build_layout(B, rows_per_b, V, top_k);
+  if (!ws || ws_bytes < L.bytes || !aligned_to(ws, kAlign)) return TSV_EWORKSPACE;
+  char* w = static_cast<char*>(ws);
+  int* tk_idx = topk_idx ? topk_idx : reinterpret_cast<int*>(w + L.off_idx);
+  float* tk_p = topk_p ? topk_p : reinterpret_cast<float*>(w + L.off_p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_topk(probs, L.plan, reinterpret_cast<uint64_t*>(w + L.off_seg),
+                             tk_idx, tk_p, s);
+  if (e != hipSuccess) return TSV_EHIP;
+  TreeArgs a;
+  a.tk_idx = tk_idx;
+  a.tk_p = tk_p;
+  a.B = B;
+  a.gamma = steps;
+  a.k = top_k;
+  a.N_max = N_max;
+  a.cap = n_budget;
+  a.adaptive = cost ? 1 : 0;
+  a.rows = rows_per_b;
+  a.per_node = per_node ? 1 : 0;
+  a.cost = cost ? *cost : tsv_cost{0, 0, 0, 0, 0};
+  a.prefix_len = prefix_len;
+  a.n_nodes = n_nodes;
+  a.parent = parent;
+  a.token = token;
+  a.depth = depth;
+  a.score = score;
+  a.anc_bits = anc_bits;
+  return launch_status(launch_best_first(a, s));
 }
 
 bool attn_sizes_ok(int B, int N_max, int L_cap, int Hq, int Hkv, int d_qk, int d_v) {
@@ -75,7 +143,6 @@ size_t walk_bytes(int B, int N_max, int V, int dtype) {
   return align_up(static_cast<size_t>(rows) * p.nseg * sizeof(uint64_t));
 }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_EHIP; }
 
 }  // namespace
 
@@ -109,6 +176,9 @@ size_t tsv_workspace_size(int which, int B, int gamma, int V, int top_k,
       return walk_bytes(B, N_max, V, dtype);
     case 3:
       return 0;
+    case 4:
+      if (!expand_sizes_ok(B, gamma, V, top_k, N_max)) return 0;
+      return build_layout(B, expanded_rows(gamma, top_k), V, top_k).bytes;
     default:
       return 0;
   }
@@ -125,39 +195,27 @@ int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
   if (B < 1 || gamma < 1 || V < 1 || top_k < 1 || N_max < 1) return TSV_EINVAL;
   if (top_k > V || n_budget < 0 || n_budget > N_max) return TSV_EINVAL;
   if (!build_sizes_ok(B, gamma, V, top_k, N_max)) return TSV_EUNSUPPORTED;
-  if (cost) {
-    if (!prefix_len) return TSV_EINVAL;
-    if (!isfinite(cost->a) || !isfinite(cost->c_d) || !(cost->a + cost->c_d > 0.0) ||
-        !finite_nonneg(cost->b) || !finite_nonneg(cost->c) || !finite_nonneg(cost->e))
-      return TSV_EINVAL;
-  }
-  const BuildLayout L = build_layout(B, gamma, V, top_k);
-  if (!ws || ws_bytes < L.bytes || !aligned_to(ws, kAlign)) return TSV_EWORKSPACE;
-  char* w = static_cast<char*>(ws);
-  int* tk_idx = topk_idx ? topk_idx : reinterpret_cast<int*>(w + L.off_idx);
-  float* tk_p = topk_p ? topk_p : reinterpret_cast<float*>(w + L.off_p);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_topk(marginals, L.plan, reinterpret_cast<uint64_t*>(w + L.off_seg),
-                             tk_idx, tk_p, s);
-  if (e != hipSuccess) return TSV_EHIP;
-  TreeArgs a;
-  a.tk_idx = tk_idx;
-  a.tk_p = tk_p;
-  a.B = B;
-  a.gamma = gamma;
-  a.k = top_k;
-  a.N_max = N_max;
-  a.cap = n_budget;
-  a.adaptive = cost ? 1 : 0;
-  a.cost = cost ? *cost : tsv_cost{0, 0, 0, 0, 0};
-  a.prefix_len = prefix_len;
-  a.n_nodes = n_nodes;
-  a.parent = parent;
-  a.token = token;
-  a.depth = depth;
-  a.score = score;
-  a.anc_bits = anc_bits;
-  return launch_status(launch_best_first(a, s));
+  if (cost && (!prefix_len || !cost_ok(cost))) return TSV_EINVAL;
+  return launch_build(marginals, B, gamma, gamma, V, top_k, n_budget, cost, prefix_len, N_max,
+                      n_nodes, parent, token, depth, score, anc_bits, topk_idx, topk_p, ws,
+                      ws_bytes, stream, false);
+}
+
+int build_tree_expand(const float* probs, int B, int steps, int V, int top_k,
+                      int n_budget, const tsv_cost* cost, const int* prefix_len,
+                      int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                      float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!probs || !n_nodes || !parent || !token || !depth || !score || !anc_bits)
+    return TSV_EINVAL;
+  if ((topk_idx == nullptr) != (topk_p == nullptr)) return TSV_EINVAL;
+  if (B < 1 || steps < 1 || V < 1 || top_k < 1 || N_max < 1) return TSV_EINVAL;
+  if (top_k > V || n_budget < 0 || n_budget > N_max) return TSV_EINVAL;
+  if (!expand_sizes_ok(B, steps, V, top_k, N_max)) return TSV_EUNSUPPORTED;
+  if (cost && (!prefix_len || !cost_ok(cost))) return TSV_EINVAL;
+  return launch_build(probs, B, expanded_rows(steps, top_k), steps, V, top_k, n_budget, cost,
+                      prefix_len, N_max, n_nodes, parent, token, depth, score, anc_bits,
+                      topk_idx, topk_p, ws, ws_bytes, stream, true);
 }
 
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,

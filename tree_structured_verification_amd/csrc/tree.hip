@@ -5,6 +5,14 @@
 // budget is found by adding nodes in that order while the throughput
 // (1 + Phi_n) / (C_d + C_v(n; l)) still rises.
 //
+// Two sources of children.  Per position: a node at depth d branches on the
+// top-k list of drafter position d (one list per position, shared by every
+// node of that depth).  Per node ([review] "How it works", steps 1-2): every
+// node of depth < s branches on the top-k of its own distribution; the lists
+// are in level order of the complete k-ary expansion, so the child of rank r
+// of the node whose token came from list i has list k*i + 1 + r (the root's
+// list is 0).  Each frontier entry then carries the list its token came from.
+//
 // One wavefront per request.  The frontier holds, for every popped node, its
 // best unpopped child and its next unpopped sibling -- enough because a
 // node's children are ranked by probability, so a child never beats its
@@ -64,16 +72,16 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
 constexpr int kShl1 = 0x130;  // lane l takes lane l + 1 (lane 63 takes the fill)
 constexpr int kShr1 = 0x138;  // lane l takes lane l - 1 (lane 0 takes the fill)
 
-template <int SL>
+template <int SL, bool PER_NODE>
 __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   __shared__ float s_p[kMaxTopkTable];
   __shared__ int s_i[kMaxTopkTable];
-  __shared__ int n_par[128], n_dep[128], n_rank[128];
+  __shared__ int n_par[128], n_dep[128], n_rank[128], n_row[128];
   __shared__ float n_sc[128];
 
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const int gk = a.gamma * a.k;
+  const int gk = a.rows * a.k;
   const size_t tbase = static_cast<size_t>(b) * gk;
   // the table in batches of 8 loads per lane, all in flight together
   for (int e0 = 0; e0 < gk; e0 += 8 * 64) {
@@ -95,24 +103,28 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     }
   }
   // the best child of a node at depth d has probability p[d][0]: lane d keeps it
-  const float q_first = lane < a.gamma ? a.tk_p[tbase + static_cast<size_t>(lane) * a.k] : 0.f;
+  const float q_first = (!PER_NODE && lane < a.gamma) ? a.tk_p[tbase + static_cast<size_t>(lane) * a.k] : 0.f;
   __syncthreads();
 
-  // entry = order key (0 = empty), its exact score and its parent's score
+  // entry = order key (0 = empty), its exact score, its parent's score and
+  // (per node) the list its token comes from
   uint64_t fk[SL];
   float fsc[SL], fps[SL];
+  int frw[SL];
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
     fk[s] = 0;
     fsc[s] = 0.f;
     fps[s] = 0.f;
+    frw[s] = 0;
   }
-  auto insert = [&](uint64_t x, float xs, float xp) {
+  auto insert = [&](uint64_t x, float xs, float xp, int xr) {
     int pos = 0;
 #pragma unroll
     for (int s = 0; s < SL; ++s) pos += __popcll(__ballot(fk[s] > x));
     uint64_t ck = 0;
     float cs = 0.f, cp = 0.f;
+    int cr = 0;
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const uint64_t k63 = readlane_u64(fk[s], 63);
@@ -128,6 +140,12 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       ck = k63;
       cs = s63;
       cp = p63;
+      if constexpr (PER_NODE) {
+        const int r63 = __builtin_amdgcn_readlane(frw[s], 63);
+        const int shr = static_cast<int>(wave_shift_u32<kShr1>(static_cast<uint32_t>(frw[s]), static_cast<uint32_t>(cr)));
+        frw[s] = keep ? frw[s] : (here ? xr : shr);
+        cr = r63;
+      }
     }
   };
   auto drop_front = [&]() {
@@ -139,13 +157,17 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       fk[s] = wave_shift_u64<kShl1>(fk[s], nk);
       fsc[s] = __uint_as_float(wave_shift_u32<kShl1>(__float_as_uint(fsc[s]), __float_as_uint(ns)));
       fps[s] = __uint_as_float(wave_shift_u32<kShl1>(__float_as_uint(fps[s]), __float_as_uint(np)));
+      if constexpr (PER_NODE) {
+        const int nr = s + 1 < SL ? __builtin_amdgcn_readlane(frw[s + 1 < SL ? s + 1 : s], 0) : 0;
+        frw[s] = static_cast<int>(wave_shift_u32<kShl1>(static_cast<uint32_t>(frw[s]), static_cast<uint32_t>(nr)));
+      }
     }
   };
 
   // the root's best child: score 1 * q, depth 1, rank 0
   {
     const float r0 = __fmul_rn(1.0f, s_p[0]);
-    insert(frontier_key(r0, 1, -1, 0), r0, 1.0f);
+    insert(frontier_key(r0, 1, -1, 0), r0, 1.0f, 0);
   }
 
   const double l = a.adaptive ? static_cast<double>(a.prefix_len[b]) : 0.0;
@@ -162,8 +184,13 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     const int dep = 63 - static_cast<int>((wl >> 15) & 63) + 1;
     const float sc = readlane_f32(fsc[0], 0);
     const float ps = readlane_f32(fps[0], 0);
-    const float q_sib = rank + 1 < a.k ? s_p[(dep - 1) * a.k + rank + 1] : 0.f;
-    const float q_kid = dep < a.gamma ? readlane_f32(q_first, dep) : 0.f;
+    // list of the popped node's token (shared with its siblings) and the
+    // list its children come from
+    const int row = PER_NODE ? __builtin_amdgcn_readlane(frw[0], 0) : dep - 1;
+    const int kid_row = PER_NODE ? a.k * row + 1 + rank : dep;
+    const float q_sib = rank + 1 < a.k ? s_p[row * a.k + rank + 1] : 0.f;
+    float q_kid = 0.f;
+    if (dep < a.gamma) q_kid = PER_NODE ? s_p[kid_row * a.k] : readlane_f32(q_first, dep);
     if (a.adaptive) {
       const double phi2 = __dadd_rn(phi, static_cast<double>(sc));
       const double th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, m + 1, l));
@@ -175,16 +202,17 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       n_par[m] = par;
       n_dep[m] = dep;
       n_rank[m] = rank;
+      n_row[m] = row;
       n_sc[m] = sc;
     }
     drop_front();
     if (rank + 1 < a.k) {
       const float v = __fmul_rn(ps, q_sib);
-      insert(frontier_key(v, dep, par, rank + 1), v, ps);
+      insert(frontier_key(v, dep, par, rank + 1), v, ps, row);
     }
     if (dep < a.gamma) {
       const float v = __fmul_rn(sc, q_kid);
-      insert(frontier_key(v, dep + 1, m, 0), v, sc);
+      insert(frontier_key(v, dep + 1, m, 0), v, sc, kid_row);
     }
     ++m;
   }
@@ -196,7 +224,7 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   for (int i = lane; i < a.N_max; i += 64) {
     const bool v = i < n;
     a.parent[nb + i] = v ? n_par[i] : -1;
-    a.token[nb + i] = v ? s_i[(n_dep[i] - 1) * a.k + n_rank[i]] : -1;
+    a.token[nb + i] = v ? s_i[n_row[i] * a.k + n_rank[i]] : -1;
     a.depth[nb + i] = v ? n_dep[i] : -1;
     a.score[nb + i] = v ? n_sc[i] : 0.0f;
     uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
@@ -225,10 +253,17 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 
 hipError_t launch_best_first(const TreeArgs& a, hipStream_t s) {
   // sorted frontier of 64 or 128 places (at least cap)
-  if (a.cap <= 64)
-    best_first_kernel<1><<<dim3(a.B), dim3(64), 0, s>>>(a);
-  else
-    best_first_kernel<2><<<dim3(a.B), dim3(64), 0, s>>>(a);
+  if (a.per_node) {
+    if (a.cap <= 64)
+      best_first_kernel<1, true><<<dim3(a.B), dim3(64), 0, s>>>(a);
+    else
+      best_first_kernel<2, true><<<dim3(a.B), dim3(64), 0, s>>>(a);
+  } else {
+    if (a.cap <= 64)
+      best_first_kernel<1, false><<<dim3(a.B), dim3(64), 0, s>>>(a);
+    else
+      best_first_kernel<2, false><<<dim3(a.B), dim3(64), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

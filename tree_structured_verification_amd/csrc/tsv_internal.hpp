@@ -30,6 +30,9 @@ struct TreeArgs {
   const int* tk_idx;
   const float* tk_p;
   int B, gamma, k, N_max, cap, adaptive;
+  // rows of top-k lists per request: gamma (one per position), or the
+  // expanded nodes in level order when per_node is set
+  int rows, per_node;
   tsv_cost cost;
   const int* prefix_len;
   int* n_nodes;

@@ -8,12 +8,16 @@ GPU path and the CPU oracle can take their inputs from it.
 
 from .gen import (  # noqa: F401
     CONFIGS,
+    EXPAND_CONFIGS,
     Config,
     Cost,
+    ExpandConfig,
     attention_inputs,
     config,
     drafter_logits,
+    expand_config,
     marginals,
+    node_distributions,
     prefix_lengths,
     target_logits,
 )

@@ -19,6 +19,14 @@ distributions of five workloads:
   5 long_mla         8 requests, latent attention as in 3, prefix 65536,
                      top-4 over 16 positions, budget 128, bf16
 
+and, for trees built by per-node conditional expansion (every expanded node
+has its own next-token distribution over the 129280-token vocabulary of 3/5):
+
+  101 s3_k2_d6       4 requests, 3 steps, top-2, budget 6
+  102 s4_k2_d5       16 requests, 4 steps, top-2, budget 5
+  103 s5_k2_d8       64 requests, 5 steps, top-2, budget 8
+  104 s3_k2_d6_b64   64 requests, 3 steps, top-2, budget 6
+
 Recipe (identical for every workload):
   * drafter logits ~ N(0, sigma) per (request, position, token), drawn in fp64;
     sigma is a standard deviation;
@@ -177,6 +185,60 @@ def marginals(cfg: Config, seed: int = 0, device="cpu") -> torch.Tensor:
     out = torch.empty((cfg.B, cfg.gamma, cfg.V), dtype=torch.float32, device=device)
     for b in range(cfg.B):
         lg = drafter_logits(cfg, seed, b, device) / float(temps[b])
+        out[b] = torch.softmax(lg, dim=-1).to(torch.float32)
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class ExpandConfig:
+    """Inputs of a tree built by per-node conditional expansion: s draft steps,
+    top-k per node, budget D (the review's s<s>_k<k>_d<D> notation), over the
+    DeepSeek-V4 vocabulary of the latent workloads.  Every expanded node (the
+    root and each node of depth < s) has its own next-token distribution."""
+
+    id: int
+    name: str
+    B: int
+    steps: int
+    top_k: int
+    n_budget: int
+    N_max: int
+    V: int = 129280
+    sigma: float = 3.0
+    cost: Optional[Cost] = None
+
+    @property
+    def rows(self) -> int:
+        """Expanded nodes per request: 1 + k + ... + k^(s-1)."""
+        return sum(self.top_k ** d for d in range(self.steps))
+
+    def replace(self, **kw) -> "ExpandConfig":
+        return dataclasses.replace(self, **kw)
+
+
+EXPAND_CONFIGS = {
+    # the review's best throughput point (three steps, top-2, budget 6) at
+    # batch 4, and its other named points at larger batches
+    101: ExpandConfig(101, "s3_k2_d6", B=4, steps=3, top_k=2, n_budget=6, N_max=8),
+    102: ExpandConfig(102, "s4_k2_d5", B=16, steps=4, top_k=2, n_budget=5, N_max=8),
+    103: ExpandConfig(103, "s5_k2_d8", B=64, steps=5, top_k=2, n_budget=8, N_max=8),
+    # the batch-64 end of the review's sweep, for throughput
+    104: ExpandConfig(104, "s3_k2_d6_b64", B=64, steps=3, top_k=2, n_budget=6, N_max=8),
+}
+
+
+def expand_config(cfg_id: int, **overrides) -> ExpandConfig:
+    cfg = EXPAND_CONFIGS[cfg_id]
+    return cfg.replace(**overrides) if overrides else cfg
+
+
+def node_distributions(cfg: ExpandConfig, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Next-token distributions of every expanded node, fp32 [B, rows, V], rows
+    in level order (row 0 the root's; the child of rank r of the node with
+    row i has row k*i + 1 + r).  Logits ~ N(0, sigma) in fp64, softmax, fp32."""
+    out = torch.empty((cfg.B, cfg.rows, cfg.V), dtype=torch.float32, device=device)
+    for b in range(cfg.B):
+        lg = _randn((cfg.rows, cfg.V), seed, cfg, _T_DRAFT, b, device, torch.float64) * cfg.sigma
         out[b] = torch.softmax(lg, dim=-1).to(torch.float32)
     return out
 
