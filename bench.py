@@ -28,6 +28,12 @@ traffic), for the FETCH_SIZE / WRITE_SIZE counter runs;
 (3 = mla_bf16, 5 = long_mla, ...) and prints the mean time per call with
 the achieved matrix throughput and HBM bandwidth on algorithmic flops and
 bytes (for the counter runs of the other kernels' shapes).
+
+    python bench.py --expand-workload 104 --cpu-requests 4
+
+times build_tree_expand alone (per-node conditional expansion, workloads
+101..104 of workloads/gen.py) on three rotating input copies and reports its
+HBM bandwidth on algorithmic bytes, with the oracle on the first requests.
 """
 
 import argparse
@@ -138,6 +144,71 @@ def attention_only(wid, K, W, dev):
                       "algorithmic_flops": flops, "algorithmic_bytes": nbytes}), flush=True)
 
 
+def expand_bytes(cfg, n_nodes):
+    """Algorithmic bytes of one build_tree_expand call: every expanded node's
+    distribution read once, its top-k list written and read once, the tree
+    outputs written once."""
+    P, k = cfg.rows, cfg.top_k
+    W = (cfg.N_max + 31) // 32
+    lists = cfg.B * P * k * 8 * 2
+    outputs = cfg.B * (4 + cfg.N_max * (4 * 4 + 4 * W))
+    return cfg.B * P * cfg.V * 4 + lists + outputs
+
+
+def expand_only(wid, K, W, dev, cpu_requests):
+    """K timed build_tree_expand calls (after W) on expansion workload wid,
+    inputs in three rotating copies; prints one JSON line."""
+    import oracle
+    from workloads import expand_config, node_distributions
+
+    cfg = expand_config(wid)
+    print(f"[bench] build_tree_expand, workload {cfg.name}", file=sys.stderr, flush=True)
+    x0 = node_distributions(cfg, 0, dev)
+    sets = [x0] + [x0.clone() for _ in range(ROTATE - 1)]
+    B, N = cfg.B, cfg.N_max
+    Wd = (N + 31) // 32
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(n_nodes=torch.empty(B, **i32), parent=torch.empty(B, N, **i32),
+               token=torch.empty(B, N, **i32), depth=torch.empty(B, N, **i32),
+               score=torch.empty(B, N, dtype=torch.float32, device=dev),
+               anc_bits=torch.empty(B, N, Wd, **i32))
+    ws = tsv.workspace(tsv.workspace_size(4, B, cfg.steps, cfg.V, cfg.top_k, N), dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(W + K)]
+    stream = torch.cuda.current_stream(dev)
+    for s in range(W + K):
+        ev[s][0].record(stream)
+        tsv.build_tree_expand(sets[s % ROTATE], cfg.steps, cfg.top_k, cfg.n_budget, N,
+                              out=out, ws=ws)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev[W:]])) / 1e3
+    nbytes = expand_bytes(cfg, out["n_nodes"])
+    n_gpu = out["n_nodes"].cpu().numpy()
+    # the oracle on the first requests of the same inputs
+    reqs = list(range(min(cpu_requests, B)))
+    host = x0[reqs].cpu().numpy()
+    t0 = time.perf_counter()
+    idx, p = oracle.topk_per_position(host, cfg.top_k)
+    trees = [oracle.select_tree_expand(idx[j], p[j], cfg.steps, cfg.n_budget, N)
+             for j in range(len(reqs))]
+    dt = time.perf_counter() - t0
+    if [tr.n for tr in trees] != n_gpu[reqs].tolist():
+        raise RuntimeError("oracle and GPU trees differ in size")
+    print(json.dumps({
+        "expand_workload": cfg.name, "B": B, "steps": cfg.steps, "top_k": cfg.top_k,
+        "budget": cfg.n_budget, "V": cfg.V, "rows_per_request": cfg.rows, "calls": K,
+        "us_per_call": round(t * 1e6, 1),
+        "tree_nodes_per_s": round(float(n_gpu.sum()) / t, 1),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": {"value": round(sum(tr.n for tr in trees) / dt, 2),
+                         "unit": "tree nodes/s", "cores": 1, "kind": "oracle",
+                         "sample": f"top-k and tree of {len(reqs)} of the {B} requests, "
+                                   f"{dt:.1f} s"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +221,9 @@ def main():
                     help="run only the tree_verify_attn calls of the steps (for counter runs)")
     ap.add_argument("--attention-workload", type=int, default=0, metavar="N",
                     help="time only tree_verify_attn on workload N (implies --attention-only)")
+    ap.add_argument("--expand-workload", type=int, default=0, metavar="N",
+                    help="time only build_tree_expand on expansion workload N "
+                         "(101..104 of workloads/gen.py)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB three times between device buffers, so that "
                          "byte counters can be scaled by a kernel of known traffic")
@@ -169,6 +243,9 @@ def main():
         del bufs
     if args.attention_workload:
         attention_only(args.attention_workload, args.steps, args.warmup, dev)
+        return
+    if args.expand_workload:
+        expand_only(args.expand_workload, args.steps, args.warmup, dev, args.cpu_requests)
         return
     cfg = config(WORKLOAD)
     print(f"[bench] generating workload {cfg.name} on {torch.cuda.get_device_name(dev)}",
