@@ -71,13 +71,23 @@ def _as_node_rows(marg, k):
     return np.concatenate([np.repeat(marg[d][None], k ** d, axis=0) for d in range(gamma)])
 
 
+@pytest.mark.parametrize("quant", [None, 8])
 @pytest.mark.parametrize("steps,k,V,n,adaptive", [
     (2, 2, 5, 6, False), (3, 2, 8, 14, False), (3, 3, 6, 20, False), (4, 2, 7, 30, True),
     (2, 4, 9, 20, True), (5, 1, 4, 5, False), (3, 2, 4, 3, True)])
-def test_reduces_to_per_position_builder(steps, k, V, n, adaptive):
+def test_reduces_to_per_position_builder(steps, k, V, n, adaptive, quant):
+    """quant: probabilities in multiples of 1/quant, so that equal scores occur
+    among siblings and across depths (the tie order of the per-position
+    builder is pinned by its own tests)."""
     rng = np.random.default_rng(steps * 100 + k * 10 + V)
     for trial in range(5):
-        marg = rng.dirichlet(np.full(V, 0.4), size=steps).astype(np.float32)
+        if quant:
+            marg = rng.integers(0, quant // 2, size=(steps, V)).astype(np.float64)
+            marg[:, 0] = quant - (marg[:, 1:].sum(-1) % quant)
+            marg = (marg / marg.sum(-1, keepdims=True)).astype(np.float32)
+            marg[:, -1] = 0.5
+        else:
+            marg = rng.dirichlet(np.full(V, 0.4), size=steps).astype(np.float32)
         rows = _as_node_rows(marg, k)
         cost = Cost(a=0.3, b=0.02, c=1e-3, e=1e-5, c_d=0.2) if adaptive else None
         N_max = max(n, 1)
@@ -185,3 +195,19 @@ def test_rejects_wrong_row_count():
     idx, p = topk_per_position(np.full((4, 3), 1 / 3, dtype=np.float32), 2)
     with pytest.raises(ValueError):
         expand_candidates(idx, p, 2)
+
+
+def test_depth_orders_equal_scores():
+    """Equal scores at different depths: the shallower node comes first even
+    when the deeper one's parent scores higher (dyadic values, exact in fp32).
+    Tokens 0/1; a = root's token 0 (0.75), b = token 1 (0.25); a's children
+    0.5 each (0.375), b's 0.75 / 0.25; every depth-2 node's children 0.5 each.
+    b's first child (0.25 * 0.75 = 0.1875, depth 2) precedes the four
+    grandchildren of a (0.375 * 0.5 = 0.1875, depth 3)."""
+    rows = np.array([[0.75, 0.25], [0.5, 0.5], [0.75, 0.25],
+                     [0.5, 0.5], [0.5, 0.5], [0.5, 0.5], [0.5, 0.5]], dtype=np.float32)
+    idx, p = topk_per_position(rows, 2)
+    tree = select_tree_expand(idx, p, 3, 9, 16)
+    assert _paths(tree) == [(0,), (0, 0), (0, 1), (1,), (1, 0),
+                            (0, 0, 0), (0, 0, 1), (0, 1, 0), (0, 1, 1)]
+    assert [float(x) for x in tree.score[:9]] == [0.75, 0.375, 0.375, 0.25] + [0.1875] * 5

@@ -161,3 +161,12 @@ def test_invalid_arguments_return_status():
     with pytest.raises(tsv.TsvError) as e:
         tsv.build_tree_expand(y, 6, 4, 2, 4)          # 1365 x 4 list entries > 4096
     assert e.value.code == -2
+
+
+def test_depth_orders_equal_scores():
+    """Equal dyadic scores across depths: the shallower node first even when
+    the deeper one's parent scores higher (same rows as the oracle's pin)."""
+    rows = np.array([[0.75, 0.25], [0.5, 0.5], [0.75, 0.25],
+                     [0.5, 0.5], [0.5, 0.5], [0.5, 0.5], [0.5, 0.5]], dtype=np.float32)[None]
+    for n in (4, 5, 6, 9, 14):
+        _run(rows, 3, 2, n, 16)
