@@ -34,6 +34,12 @@ bytes (for the counter runs of the other kernels' shapes).
 times build_tree_expand alone (per-node conditional expansion, workloads
 101..104 of workloads/gen.py) on three rotating input copies and reports its
 HBM bandwidth on algorithmic bytes, with the oracle on the first requests.
+
+    python bench.py --cost-profile
+
+measures the grouped attention's cost over an (n, l) grid, fits the convex
+monotone C_v(n; l) and reports how much perturbing the fitted coefficients by
+up to 20 % changes the adaptive budgets of workload 4.
 """
 
 import argparse
@@ -52,7 +58,7 @@ if ROOT not in sys.path:
 
 import tree_structured_verification_amd as tsv  # noqa: E402
 from tree_structured_verification_amd import _lib  # noqa: E402
-from workloads import attention_inputs, config, marginals, target_logits  # noqa: E402
+from workloads import Cost, attention_inputs, config, marginals, target_logits  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = 2
@@ -209,6 +215,75 @@ def expand_only(wid, K, W, dev, cpu_requests):
                                    f"{dt:.1f} s"}}), flush=True)
 
 
+def cost_profile(dev, perturbations=20):
+    """Measure C_v(n; l) of the grouped-query attention on this GPU (16
+    requests, 32/8 heads x 128, bf16), fit the convex monotone model, and test
+    the adaptive budget's robustness to perturbed coefficients on the adaptive
+    workload's marginals; prints one JSON line."""
+    import dataclasses
+    from tree_structured_verification_amd.profile_cost import calibrate
+    from workloads import prefix_lengths
+
+    print("[bench] measuring tree_verify_attn over an (n, l) grid", file=sys.stderr, flush=True)
+    cost, (n, l, t) = calibrate(16, 32, 8, 128, c_d=0.0)
+    A = np.stack([np.ones_like(n), n, n * n, l * n, l], 1)
+    coef = np.array([cost.a, cost.b, cost.c, cost.e, cost.f])
+    pred = A @ coef
+    r2 = 1.0 - float(np.sum((pred - t) ** 2)) / float(np.sum((t - t.mean()) ** 2))
+    # drafting cost: half the verification cost of one node at the median
+    # prefix, the ratio C_d / C_v(1) of the adaptive workload's coefficients
+    # (the drafter itself is not here)
+    lmed = float(np.median(prefix_lengths(config(4))))
+    cv1 = cost.a + cost.b + cost.c + cost.e * lmed + cost.f * lmed
+    base = Cost(a=cost.a, b=cost.b, c=cost.c, e=cost.e, c_d=0.5 * cv1, f=cost.f)
+    cfg = config(4)
+    marg = marginals(cfg, 0, dev)
+    pl_np = prefix_lengths(cfg)
+    pl = torch.from_numpy(pl_np).to(dev)
+
+    def run(c):
+        g = tsv.build_tree(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=c, prefix_len=pl)
+        torch.cuda.synchronize()
+        return g["n_nodes"].cpu().numpy(), g["score"].cpu().numpy()
+
+    def theta(c, scores, nb, lb):
+        phi = float(np.sum(scores[:nb].astype(np.float64)))
+        m = float(nb)
+        return (1.0 + phi) / (c.c_d + ((((c.a + c.b * m) + c.c * (m * m)) + (c.e * lb) * m) + c.f * lb))
+
+    n0, s0 = run(base)
+    # every request's scores in best-first order up to the cap (fixed budget)
+    gfull = tsv.build_tree(marg, cfg.top_k, cfg.n_budget, cfg.N_max)
+    torch.cuda.synchronize()
+    sfull = gfull["score"].cpu().numpy()
+    rng = np.random.default_rng(0)
+    changed, dn, loss = [], [], []
+    for _ in range(perturbations):
+        f = rng.uniform(0.8, 1.2, 6)
+        pc = Cost(a=base.a * f[0], b=base.b * f[1], c=base.c * f[2], e=base.e * f[3],
+                  c_d=base.c_d * f[4], f=base.f * f[5])
+        n1, _ = run(pc)
+        changed.append(float(np.mean(n1 != n0)))
+        dn.append(float(np.mean(np.abs(n1.astype(np.int64) - n0))))
+        # modelled throughput (true = unperturbed cost) at the perturbed budgets
+        th0 = sum(theta(base, sfull[b], n0[b], pl_np[b]) for b in range(cfg.B))
+        th1 = sum(theta(base, sfull[b], n1[b], pl_np[b]) for b in range(cfg.B))
+        loss.append(1.0 - th1 / th0)
+    print(json.dumps({
+        "cost_profile": "tree_verify_attn, 16 requests, Hq 32 / Hkv 8 x 128, bf16",
+        "unit": "us per request per call", "points": int(n.size),
+        "fit": {"a": cost.a, "b": cost.b, "c": cost.c, "e": cost.e, "f": cost.f, "c_d": base.c_d,
+                "r2": round(r2, 5),
+                "max_rel_err": round(float(np.max(np.abs(pred - t) / t)), 4)},
+        "adaptive_workload_nstar": {"mean": round(float(n0.mean()), 2), "std": round(float(n0.std()), 2),
+                                    "zero": int(np.sum(n0 == 0))},
+        "perturbed_20pct": {"runs": perturbations, "frac_requests_changed": round(float(np.mean(changed)), 4),
+                            "mean_abs_dn": round(float(np.mean(dn)), 3),
+                            "mean_modelled_throughput_loss": round(float(np.mean(loss)), 6),
+                            "max_modelled_throughput_loss": round(float(np.max(loss)), 6)},
+        "grid": [[float(x), float(y), round(float(z), 3)] for x, y, z in zip(n, l, t)]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +299,9 @@ def main():
     ap.add_argument("--expand-workload", type=int, default=0, metavar="N",
                     help="time only build_tree_expand on expansion workload N "
                          "(101..104 of workloads/gen.py)")
+    ap.add_argument("--cost-profile", action="store_true",
+                    help="measure and fit the verification cost C_v(n; l) and test the "
+                         "adaptive budget's robustness to perturbed coefficients")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB three times between device buffers, so that "
                          "byte counters can be scaled by a kernel of known traffic")
@@ -243,6 +321,9 @@ def main():
         del bufs
     if args.attention_workload:
         attention_only(args.attention_workload, args.steps, args.warmup, dev)
+        return
+    if args.cost_profile:
+        cost_profile(dev)
         return
     if args.expand_workload:
         expand_only(args.expand_workload, args.steps, args.warmup, dev, args.cpu_requests)

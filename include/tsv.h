@@ -15,6 +15,8 @@
  *   tree_verify_attn  branch-aware attention of every tree node
  *   accept_walk       target argmax -> longest accepted root-to-node path
  *   commit_path       accepted scratch KV -> persistent cache
+ * and, once per deployment, tsv_fit_cost: measured latencies -> the cost
+ * model build_tree's adaptive budget uses.
  *
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer to a caller-owned, contiguous,
@@ -68,10 +70,13 @@ enum {
 
 /* Round-cost coefficients ([caddtree] Methodology, item 1, with item 5's
  * convex, monotone verification cost):
- *   C(n; l) = c_d + C_v(n; l),  C_v(n; l) = a + b*n + c*n^2 + e*l*n.
- * Requirements: a + c_d > 0 and b, c, e >= 0 (so C > 0, convex, monotone). */
+ *   C(n; l) = c_d + C_v(n; l),  C_v(n; l) = a + b*n + c*n^2 + e*l*n + f*l.
+ * The f*l term is the part of a request's verification that does not depend
+ * on its tree size (reading its prefix once); f = 0 gives the plain family.
+ * Requirements: a + c_d > 0 and b, c, e, f >= 0 (so C > 0, convex and
+ * monotone in n). */
 typedef struct {
-  double a, b, c, e, c_d;
+  double a, b, c, e, c_d, f;
 } tsv_cost;
 
 /*
@@ -111,7 +116,7 @@ typedef struct {
  *   (-score, depth, key(parent), rank), so parents precede children.
  *   Scores are fp32 products parent_score * q (root 1, round-to-nearest,
  *   never fused); Phi and C are fp64 in the order
- *   c_d + (((a + b*n) + c*(n*n)) + (e*l)*n); a node is added iff
+ *   c_d + ((((a + b*n) + c*(n*n)) + (e*l)*n) + f*l); a node is added iff
  *   (1 + Phi_{n+1}) / C(n+1) > (1 + Phi_n) / C(n).
  */
 int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
@@ -242,6 +247,34 @@ int commit_path(void* k_cache, void* v_cache, int* prefix_len,
                 const int* accept_len, const int* accept_nodes, int B,
                 int N_max, int L_cap, int Hkv, int d_k, int d_v, int gamma,
                 int dtype, int* status, void* stream);
+
+/*
+ * tsv_fit_cost -- the convex, monotone verification cost from measured
+ * latencies (host computation, run once, offline).
+ *
+ * [caddtree] Methodology, item 5: C_v(n; l) is estimated once by convex
+ * regression on latencies measured over node counts and context lengths,
+ * which keeps it convex and monotone so that the throughput objective of
+ * item 3 stays unimodal (the greedy stop of build_tree is then exact).
+ *
+ * Fits C_v(n; l) = a + b*n + c*n^2 + e*l*n + f*l with a, b, c, e, f >= 0 by
+ * non-negative least squares: the model is non-decreasing and convex in n
+ * for every l, and non-decreasing in l.
+ *
+ * Inputs (HOST pointers): n, l, t double [m], the node count, context length
+ * and measured verification latency of each point (finite, >= 0; t in any
+ * time unit); 5 <= m <= 2^24; c_d the drafting cost in the same unit
+ * (copied to out->c_d).
+ * Output: *out (HOST) = {a, b, c, e, c_d, f}, ready for build_tree's `cost`.
+ * When every point has one context length, e and f are not separable from
+ * b and a; the optimum's value is still unique and the first optimal
+ * support in the order (a, b, c, e, f) is returned.
+ * Returns TSV_OK, or TSV_EINVAL for null pointers, m out of range or
+ * non-finite / negative inputs (out untouched).  Allocates nothing and
+ * touches no device.
+ */
+int tsv_fit_cost(const double* n, const double* l, const double* t, int m,
+                 double c_d, tsv_cost* out);
 
 /* Workspace bytes needed by entry point `which` (0 build_tree,
  * 1 tree_verify_attn, 2 accept_walk, 3 commit_path, 4 build_tree_expand,

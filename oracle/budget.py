@@ -12,8 +12,9 @@ Readings fixed here:
   * Phi_m is the sum of the first m best-first prefix probabilities (the
     drafter's surrogate for the expected accepted length; the "1 +" is the
     target's bonus token);
-  * C_v(n; l) = a + b*n + c*n^2 + e*l*n, evaluated in fp64 in exactly the order
-    c_d + (((a + b*n) + c*(n*n)) + (e*l)*n), no fused multiply-add;
+  * C_v(n; l) = a + b*n + c*n^2 + e*l*n + f*l, evaluated in fp64 in exactly
+    the order c_d + ((((a + b*n) + c*(n*n)) + (e*l)*n) + f*l), no fused
+    multiply-add (f, the part that does not grow with n, defaults to 0);
   * Phi is accumulated in fp64 in best-first order; the gain test is
     Theta(m+1) <= Theta(m) -> stop, with Theta(m) = (1 + Phi_m) / C(m);
   * n* = 0 is legal (no tree; the round still yields the bonus token).
@@ -24,7 +25,8 @@ def round_cost(n: int, prefix_len: int, cost) -> float:
     """C(n; l) in fp64, fixed evaluation order."""
     n = float(n)
     l = float(prefix_len)
-    return cost.c_d + (((cost.a + cost.b * n) + cost.c * (n * n)) + (cost.e * l) * n)
+    f = getattr(cost, "f", 0.0)
+    return cost.c_d + ((((cost.a + cost.b * n) + cost.c * (n * n)) + (cost.e * l) * n) + f * l)
 
 
 def throughput(n: int, phi: float, prefix_len: int, cost) -> float:

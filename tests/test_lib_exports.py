@@ -22,7 +22,8 @@ def _declared():
 def test_all_declared_symbols_exported():
     names = _declared()
     assert names == sorted(["build_tree", "build_tree_expand", "tree_verify_attn", "accept_walk",
-                            "commit_path", "tsv_workspace_size", "tsv_status_string"])
+                            "commit_path", "tsv_fit_cost", "tsv_workspace_size",
+                            "tsv_status_string"])
     lib = ctypes.CDLL(tsv._lib.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

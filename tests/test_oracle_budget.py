@@ -62,7 +62,8 @@ def test_unimodal_in_exact_arithmetic(seed):
 
 @pytest.mark.parametrize("seed", range(6))
 def test_comparative_statics(seed):
-    """n* falls (weakly) as l, b, c or e grow and rises as a or C_d grow."""
+    """n* falls (weakly) as l, b, c or e grow and rises as a, C_d or f (a fixed
+    cost per unit of context) grow."""
     scores = _scores(seed, temp=0.5)
     base = CFG4
     def n_of(cost, l):
@@ -74,7 +75,8 @@ def test_comparative_statics(seed):
                                     ("c", [0.0, 1e-4, 1e-3, 1e-2], True),
                                     ("e", [0.0, 1e-6, 1e-5, 1e-4], True),
                                     ("a", [0.0, 1.0, 4.0, 16.0], False),
-                                    ("c_d", [0.0, 0.5, 2.0, 8.0], False)):
+                                    ("c_d", [0.0, 0.5, 2.0, 8.0], False),
+                                    ("f", [0.0, 1e-5, 1e-4, 1e-3], False)):
         ns = [n_of(dataclasses.replace(base, **{field: v}), 8000) for v in vals]
         assert ns == sorted(ns, reverse=decreasing), (field, ns)
 

@@ -19,8 +19,9 @@ def _grid():
     return nn.ravel(), ll.ravel()
 
 
-@pytest.mark.parametrize("coef", [(10.0, 0.3, 1e-3, 2e-4), (5.0, 0.0, 2e-3, 1e-4),
-                                  (0.0, 1.0, 0.0, 0.0), (3.0, 0.2, 0.0, 5e-5)])
+@pytest.mark.parametrize("coef", [(10.0, 0.3, 1e-3, 2e-4, 0.0), (5.0, 0.0, 2e-3, 1e-4, 1e-3),
+                                  (0.0, 1.0, 0.0, 0.0, 0.0), (3.0, 0.2, 0.0, 5e-5, 2e-3),
+                                  (1.0, 0.0, 0.0, 0.0, 1e-3)])
 def test_exact_recovery(coef):
     n, l = _grid()
     t = design(n, l) @ np.array(coef)
@@ -51,7 +52,7 @@ def _brute_force(A, t):
 def test_matches_brute_force_over_active_sets(seed):
     rng = np.random.default_rng(seed)
     n, l = _grid()
-    true = rng.uniform(0, 1, 4) * np.array([20, 0.5, 2e-3, 3e-4]) * (rng.random(4) > 0.3)
+    true = rng.uniform(0, 1, 5) * np.array([20, 0.5, 2e-3, 3e-4, 2e-3]) * (rng.random(5) > 0.3)
     # latencies with noise, sometimes pulling a coefficient below zero
     t = design(n, l) @ true + rng.normal(0, 2.0, n.shape) + rng.normal(0, 5) * (n < 4)
     t = np.maximum(t, 0.0)
@@ -82,14 +83,14 @@ def test_fitted_model_is_monotone_and_convex_in_n():
     n, l = _grid()
     t = np.abs(rng.normal(100, 60, n.shape))     # arbitrary, even decreasing data
     coef, _ = fit_cost(n, l, t)
-    a, b, c, e = coef
+    a, b, c, e, f = coef
     for L in (0.0, 1000.0, 65536.0):
         m = np.arange(0, 129, dtype=np.float64)
-        cv = a + b * m + c * m * m + e * L * m
+        cv = a + b * m + c * m * m + e * L * m + f * L
         assert np.all(np.diff(cv) >= -1e-12)
         assert np.all(np.diff(cv, 2) >= -1e-12)
 
 
 def test_rejects_too_few_points():
     with pytest.raises(ValueError):
-        fit_cost([1, 2, 3], [1, 1, 1], [1, 2, 3])
+        fit_cost([1, 2, 3, 4], [1, 1, 1, 1], [1, 2, 3, 4])

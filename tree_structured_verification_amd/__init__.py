@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     build_tree,
     build_tree_expand,
     expanded_rows,
+    fit_cost,
     commit_path,
     lib,
     status_string,

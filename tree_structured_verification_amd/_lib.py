@@ -31,7 +31,7 @@ class TsvError(RuntimeError):
 
 class tsv_cost(ctypes.Structure):
     _fields_ = [("a", ctypes.c_double), ("b", ctypes.c_double), ("c", ctypes.c_double),
-                ("e", ctypes.c_double), ("c_d", ctypes.c_double)]
+                ("e", ctypes.c_double), ("c_d", ctypes.c_double), ("f", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -50,6 +50,9 @@ _SIGS = {
     "accept_walk": [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "commit_path": [_P, _P, _P, _P, _P, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                     _I, _P, _P],
+    "tsv_fit_cost": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                     ctypes.POINTER(ctypes.c_double), _I, ctypes.c_double,
+                     ctypes.POINTER(tsv_cost)],
     "tsv_workspace_size": [_I] * 12,
     "tsv_status_string": [_I],
 }
@@ -126,7 +129,7 @@ def _cost_struct(cost):
     if cost is None:
         return None
     return ctypes.byref(tsv_cost(float(cost.a), float(cost.b), float(cost.c),
-                                 float(cost.e), float(cost.c_d)))
+                                 float(cost.e), float(cost.c_d), float(getattr(cost, "f", 0.0))))
 
 
 def build_tree(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: int,
@@ -205,6 +208,23 @@ def build_tree_expand(probs: torch.Tensor, steps: int, top_k: int, n_budget: int
         _ptr(out.get("topk_idx")), _ptr(out.get("topk_p")), _ptr(ws), ws.numel(),
         _stream(dev))
     _check("build_tree_expand", code)
+    return out
+
+
+def fit_cost(n, l, t, c_d: float = 0.0) -> tsv_cost:
+    """Non-negative least-squares fit of C_v(n; l) = a + b n + c n^2 + e l n + f l to
+    measured latencies t at (n, l) (host sequences); returns the tsv_cost
+    struct (with c_d) for build_tree's adaptive budget."""
+    import numpy as np
+    n = np.ascontiguousarray(n, dtype=np.float64)
+    l = np.ascontiguousarray(l, dtype=np.float64)
+    t = np.ascontiguousarray(t, dtype=np.float64)
+    if not (n.shape == l.shape == t.shape) or n.ndim != 1:
+        raise ValueError("n, l and t must be 1-D sequences of one length")
+    dp = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    out = tsv_cost()
+    code = lib().tsv_fit_cost(dp(n), dp(l), dp(t), int(n.size), float(c_d), ctypes.byref(out))
+    _check("tsv_fit_cost", code)
     return out
 
 

@@ -79,7 +79,8 @@ bool expand_sizes_ok(int B, int steps, int V, int top_k, int N_max) {
 
 bool cost_ok(const tsv_cost* cost) {
   return isfinite(cost->a) && isfinite(cost->c_d) && cost->a + cost->c_d > 0.0 &&
-         finite_nonneg(cost->b) && finite_nonneg(cost->c) && finite_nonneg(cost->e);
+         finite_nonneg(cost->b) && finite_nonneg(cost->c) && finite_nonneg(cost->e) &&
+         finite_nonneg(cost->f);
 }
 
 // top-k of every list, then the best-first tree; shared by both builders
@@ -108,7 +109,7 @@ int launch_build(const float* probs, int B, int rows_per_b, int steps, int V, in
   a.adaptive = cost ? 1 : 0;
   a.rows = rows_per_b;
   a.per_node = per_node ? 1 : 0;
-  a.cost = cost ? *cost : tsv_cost{0, 0, 0, 0, 0};
+  a.cost = cost ? *cost : tsv_cost{0, 0, 0, 0, 0, 0};
   a.prefix_len = prefix_len;
   a.n_nodes = n_nodes;
   a.parent = parent;

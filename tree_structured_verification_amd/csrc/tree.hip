@@ -44,6 +44,7 @@ __device__ __forceinline__ double round_cost(const tsv_cost& c, int n, double l)
   double v = __dadd_rn(c.a, __dmul_rn(c.b, m));
   v = __dadd_rn(v, __dmul_rn(c.c, __dmul_rn(m, m)));
   v = __dadd_rn(v, __dmul_rn(__dmul_rn(c.e, l), m));
+  v = __dadd_rn(v, __dmul_rn(c.f, l));
   return __dadd_rn(c.c_d, v);
 }
 

@@ -61,13 +61,14 @@ import torch
 
 @dataclasses.dataclass(frozen=True)
 class Cost:
-    """Round-cost coefficients: C(n; l) = c_d + a + b*n + c*n^2 + e*l*n."""
+    """Round-cost coefficients: C(n; l) = c_d + a + b*n + c*n^2 + e*l*n + f*l."""
 
     a: float
     b: float
     c: float
     e: float
     c_d: float
+    f: float = 0.0
 
 
 @dataclasses.dataclass(frozen=True)
