@@ -16,6 +16,8 @@ It is written to be read against the pages, not to be fast:
              node branching on its own conditional distribution
   budget     round cost C = C_d + C_v(n; l) and the throughput stop rule
   costfit    the convex, monotone C_v fitted to measured latencies (NNLS)
+  global_budget  batch-global admission of tree nodes against an engine
+             throughput table, with early stopping
   attention  naive per-node attention in fp64 with explicit ancestor walks
   walk       greedy accept walk over the target's argmax
   commit     copy of the accepted chain into the persistent cache
@@ -41,5 +43,6 @@ from .tree import ancestor_bits, select_tree, TreeResult  # noqa: F401
 from .expand import expand_candidates, expanded_rows, select_tree_expand  # noqa: F401
 from .attention import attend_node, attend_request  # noqa: F401
 from .costfit import fit_cost  # noqa: F401
+from .global_budget import global_budget, global_order  # noqa: F401
 from .walk import accept_walk, row_argmax  # noqa: F401
 from .commit import commit_path  # noqa: F401
