@@ -11,7 +11,8 @@
  *
  * A round is four calls, in this order:
  *   build_tree        drafter marginals -> best-first draft tree (+ budget)
- *                     (or build_tree_expand: per-node distributions -> tree)
+ *                     (or build_tree_expand: per-node distributions -> tree;
+ *                     select_global_budget: one budget across the batch)
  *   tree_verify_attn  branch-aware attention of every tree node
  *   accept_walk       target argmax -> longest accepted root-to-node path
  *   commit_path       accepted scratch KV -> persistent cache
@@ -160,6 +161,39 @@ int build_tree_expand(const float* probs, int B, int steps, int V, int top_k,
                       int N_max, int* n_nodes, int* parent, int* token, int* depth,
                       float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * select_global_budget -- one verification budget for the whole batch.
+ *
+ * [dspark] Confidence-scheduled verification, hardware-aware prefix
+ * scheduler: verification lengths are chosen by one global throughput
+ * maximisation over the R active requests, Theta = tau * SPS(B), SPS a
+ * table of engine steps per second at batch size B profiled once; a global
+ * sort of the candidates and greedy admission respect each request's prefix
+ * order (its survival probabilities do not increase along it), and admission
+ * stops as soon as the throughput would fall.
+ *
+ * Applied to trees built by build_tree / build_tree_expand (typically with a
+ * fixed budget as the per-request cap): request r's candidates are its first
+ * n_nodes[r] nodes in best-first order with their scores a_{r,j};
+ * tau = R + admitted scores, B = R + admitted nodes (every request verifies
+ * its root plus its admitted nodes).  Candidates go in the order score
+ * descending, request ascending, position ascending; the next one is
+ * admitted iff (tau + a) * SPS(B + 1) > tau * SPS(B), in fp64 with tau summed
+ * in admission order; the walk stops at the first refusal or when B + 1
+ * reaches sps_len.  Every request keeps a prefix of its nodes, so its tree
+ * stays ancestor-closed.
+ *
+ * In/out (device): n_nodes [B] (available -> admitted), and the tree arrays
+ * of build_tree, whose entries at or past the admitted count are reset to
+ * build_tree's padding (-1, 0.0f, 0).  sps: DEVICE double [sps_len],
+ * finite and >= 0.  Scores must be finite and >= 0 (-0 == +0).
+ * Limits: N_max <= 128, B <= 4096, B * N_max <= 8192.  One workgroup, no
+ * workspace.
+ */
+int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, float* score,
+                         unsigned* anc_bits, int B, int N_max, const double* sps,
+                         long sps_len, void* stream);
 
 /*
  * tree_verify_attn -- branch-aware tree attention over a shared prefix.

@@ -22,8 +22,8 @@ def _declared():
 def test_all_declared_symbols_exported():
     names = _declared()
     assert names == sorted(["build_tree", "build_tree_expand", "tree_verify_attn", "accept_walk",
-                            "commit_path", "tsv_fit_cost", "tsv_workspace_size",
-                            "tsv_status_string"])
+                            "commit_path", "select_global_budget", "tsv_fit_cost",
+                            "tsv_workspace_size", "tsv_status_string"])
     lib = ctypes.CDLL(tsv._lib.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -78,6 +78,10 @@ def test_host_validation_without_launch():
     assert L.tree_verify_attn(p, p, p, p, p, 1200, p, p, p, 1, 4, 10, 4, 2, 600, 64, 1, 0.1,
                               p, nul, p, 1 << 30, nul) == -2      # head dim > 576
     assert L.accept_walk(p, 1, 1, 4, 8, 65, p, p, p, p, p, p, p, 1 << 20, nul) == -2  # gamma
+    assert L.select_global_budget(p, p, p, p, p, p, 4, 8, nul, 10, nul) == -1   # null table
+    assert L.select_global_budget(p, p, p, p, p, p, 4, 129, p, 10, nul) == -1   # N_max > 128
+    assert L.select_global_budget(p, p, p, p, p, p, 65, 128, p, 10, nul) == -2  # 8320 candidates
+    assert L.select_global_budget(p, p, p, p, p, p, 4, 8, p, 0, nul) == -1      # empty table
     assert L.build_tree_expand(nul, 1, 2, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
                                1 << 20, nul) == -1                # null probabilities
     assert L.build_tree_expand(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,

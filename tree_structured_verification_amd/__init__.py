@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     fit_cost,
     commit_path,
     lib,
+    select_global_budget,
     status_string,
     tree_verify_attn,
     workspace,

@@ -53,6 +53,7 @@ _SIGS = {
     "tsv_fit_cost": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                      ctypes.POINTER(ctypes.c_double), _I, ctypes.c_double,
                      ctypes.POINTER(tsv_cost)],
+    "select_global_budget": [_P, _P, _P, _P, _P, _P, _I, _I, _P, _L, _P],
     "tsv_workspace_size": [_I] * 12,
     "tsv_status_string": [_I],
 }
@@ -226,6 +227,22 @@ def fit_cost(n, l, t, c_d: float = 0.0) -> tsv_cost:
     code = lib().tsv_fit_cost(dp(n), dp(l), dp(t), int(n.size), float(c_d), ctypes.byref(out))
     _check("tsv_fit_cost", code)
     return out
+
+
+def select_global_budget(tree: dict, sps: torch.Tensor) -> dict:
+    """Batch-global admission over build_tree's outputs (modified in place):
+    tree["n_nodes"] becomes each request's admitted count.  sps: float64
+    device tensor, engine steps per second at every batch size."""
+    for k in ("n_nodes", "parent", "token", "depth", "score", "anc_bits"):
+        _dev(tree[k], k)
+    _dev(sps, "sps", torch.float64)
+    B, N_max = tree["parent"].shape
+    code = lib().select_global_budget(
+        _ptr(tree["n_nodes"]), _ptr(tree["parent"]), _ptr(tree["token"]), _ptr(tree["depth"]),
+        _ptr(tree["score"]), _ptr(tree["anc_bits"]), B, N_max, _ptr(sps), sps.numel(),
+        _stream(tree["n_nodes"].device))
+    _check("select_global_budget", code)
+    return tree
 
 
 def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

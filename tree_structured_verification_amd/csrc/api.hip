@@ -219,6 +219,27 @@ int build_tree_expand(const float* probs, int B, int steps, int V, int top_k,
                       topk_idx, topk_p, ws, ws_bytes, stream, true);
 }
 
+int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, float* score,
+                         unsigned* anc_bits, int B, int N_max, const double* sps, long sps_len,
+                         void* stream) {
+  if (!n_nodes || !parent || !token || !depth || !score || !anc_bits || !sps) return TSV_EINVAL;
+  if (B < 1 || N_max < 1 || N_max > kMaxNodes || sps_len < 1) return TSV_EINVAL;
+  if (B > kMaxGlobalRequests || static_cast<long long>(B) * N_max > kMaxGlobalCandidates)
+    return TSV_EUNSUPPORTED;
+  GlobalBudgetArgs a;
+  a.n_nodes = n_nodes;
+  a.parent = parent;
+  a.token = token;
+  a.depth = depth;
+  a.score = score;
+  a.anc_bits = anc_bits;
+  a.B = B;
+  a.N_max = N_max;
+  a.sps = sps;
+  a.sps_len = sps_len;
+  return launch_status(launch_global_budget(a, static_cast<hipStream_t>(stream)));
+}
+
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const void* k_tree, const void* v_tree, long kv_row_stride,
                      const int* prefix_len, const int* n_nodes,

@@ -44,6 +44,22 @@ struct TreeArgs {
 };
 hipError_t launch_best_first(const TreeArgs& a, hipStream_t s);
 
+// ---- select_global_budget ----------------------------------------------
+constexpr int kMaxGlobalRequests = 4096;
+constexpr int kMaxGlobalCandidates = 8192;   // B * N_max, sorted in LDS
+struct GlobalBudgetArgs {
+  int* n_nodes;
+  int* parent;
+  int* token;
+  int* depth;
+  float* score;
+  unsigned* anc_bits;
+  int B, N_max;
+  const double* sps;
+  long sps_len;
+};
+hipError_t launch_global_budget(const GlobalBudgetArgs& a, hipStream_t s);
+
 // ---- accept_walk -------------------------------------------------------
 struct ArgmaxPlan {
   int rows, V, nseg, seg_len;
