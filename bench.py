@@ -40,6 +40,11 @@ HBM bandwidth on algorithmic bytes, with the oracle on the first requests.
 measures the grouped attention's cost over an (n, l) grid, fits the convex
 monotone C_v(n; l) and reports how much perturbing the fitted coefficients by
 up to 20 % changes the adaptive budgets of workload 4.
+
+    python bench.py --global-budget
+
+times select_global_budget (one budget across the batch) on workload 4's
+trees: 64 requests x 128 candidates against a linear-step-time table.
 """
 
 import argparse
@@ -284,6 +289,47 @@ def cost_profile(dev, perturbations=20):
         "grid": [[float(x), float(y), round(float(z), 3)] for x, y, z in zip(n, l, t)]}), flush=True)
 
 
+def global_budget_bench(dev, K, W):
+    """Time select_global_budget on the adaptive workload's trees (64
+    requests, 128 best-first nodes each: the largest batch of one sort),
+    against a linear-step-time engine table; prints one JSON line."""
+    cfg = config(4)
+    marg = marginals(cfg, 0, dev)
+    base = tsv.build_tree(marg, cfg.top_k, cfg.N_max, cfg.N_max)
+    torch.cuda.synchronize()
+    B, M = cfg.B, cfg.B * cfg.N_max
+    # engine step time 1 ms + 2 us per verified token (illustrative)
+    sps = (1e6 / (1000.0 + 2.0 * torch.arange(B + M + 1, dtype=torch.float64))).to(dev)
+    work = {k: v.clone() for k, v in base.items()}
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(W + K)]
+    stream = torch.cuda.current_stream(dev)
+    for s in range(W + K):
+        for k, v in base.items():
+            work[k].copy_(v)
+        ev[s][0].record(stream)
+        tsv.select_global_budget(work, sps)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev[W:]])) * 1e3
+    n = work["n_nodes"].cpu().numpy()
+    # the oracle on the same trees
+    import oracle
+    host = {k: v.cpu().numpy() for k, v in base.items()}
+    t0 = time.perf_counter()
+    want = oracle.global_budget(host["score"], host["n_nodes"], sps.cpu().numpy())
+    dt = time.perf_counter() - t0
+    if not np.array_equal(want, n):
+        raise RuntimeError("oracle and GPU budgets differ")
+    print(json.dumps({"global_budget": f"{B} requests x {cfg.N_max} candidates "
+                      "(adaptive workload trees), engine step 1000 + 2 B us",
+                      "calls": K, "us_per_call": round(t, 2), "admitted": int(n.sum()),
+                      "requests_with_nodes": int(np.sum(n > 0)),
+                      "cpu_baseline": {"value_us_per_call": round(dt * 1e6, 1), "cores": 1,
+                                       "kind": "oracle", "sample": "the same call, once"}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,6 +345,8 @@ def main():
     ap.add_argument("--expand-workload", type=int, default=0, metavar="N",
                     help="time only build_tree_expand on expansion workload N "
                          "(101..104 of workloads/gen.py)")
+    ap.add_argument("--global-budget", action="store_true",
+                    help="time select_global_budget on the adaptive workload's trees")
     ap.add_argument("--cost-profile", action="store_true",
                     help="measure and fit the verification cost C_v(n; l) and test the "
                          "adaptive budget's robustness to perturbed coefficients")
@@ -324,6 +372,9 @@ def main():
         return
     if args.cost_profile:
         cost_profile(dev)
+        return
+    if args.global_budget:
+        global_budget_bench(dev, args.steps, args.warmup)
         return
     if args.expand_workload:
         expand_only(args.expand_workload, args.steps, args.warmup, dev, args.cpu_requests)
