@@ -18,6 +18,7 @@ It is written to be read against the pages, not to be fast:
   costfit    the convex, monotone C_v fitted to measured latencies (NNLS)
   global_budget  batch-global admission of tree nodes against an engine
              throughput table, with early stopping
+  chains     unfolding of a tree into its root-to-leaf chains
   attention  naive per-node attention in fp64 with explicit ancestor walks
   walk       greedy accept walk over the target's argmax
   commit     copy of the accepted chain into the persistent cache
@@ -44,5 +45,6 @@ from .expand import expand_candidates, expanded_rows, select_tree_expand  # noqa
 from .attention import attend_node, attend_request  # noqa: F401
 from .costfit import fit_cost  # noqa: F401
 from .global_budget import global_budget, global_order  # noqa: F401
+from .chains import unfold_chains  # noqa: F401
 from .walk import accept_walk, row_argmax  # noqa: F401
 from .commit import commit_path  # noqa: F401
