@@ -44,7 +44,8 @@ up to 20 % changes the adaptive budgets of workload 4.
     python bench.py --global-budget
 
 times select_global_budget (one budget across the batch) on workload 4's
-trees: 64 requests x 128 candidates against a linear-step-time table.
+trees: 64 requests x 128 candidates against a linear-step-time table, and
+unfold_chains on the same trees.
 """
 
 import argparse
@@ -321,6 +322,18 @@ def global_budget_bench(dev, K, W):
     dt = time.perf_counter() - t0
     if not np.array_equal(want, n):
         raise RuntimeError("oracle and GPU budgets differ")
+    # the same trees unfolded into their chains (per-round metadata)
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(W + K)]
+    for s in range(W + K):
+        evc[s][0].record(stream)
+        ch = tsv.unfold_chains(base, cfg.gamma)
+        evc[s][1].record(stream)
+    torch.cuda.synchronize()
+    tc = float(np.mean([a.elapsed_time(b) for a, b in evc[W:]])) * 1e3
+    print(json.dumps({"unfold_chains": f"{B} requests x {cfg.N_max} nodes (adaptive workload "
+                      "trees, fixed budget 128)", "calls": K, "us_per_call": round(tc, 2),
+                      "chains": int(ch["n_chains"].sum())}), flush=True)
     print(json.dumps({"global_budget": f"{B} requests x {cfg.N_max} candidates "
                       "(adaptive workload trees), engine step 1000 + 2 B us",
                       "calls": K, "us_per_call": round(t, 2), "admitted": int(n.sum()),

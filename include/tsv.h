@@ -196,6 +196,28 @@ int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, floa
                          long sps_len, void* stream);
 
 /*
+ * unfold_chains -- a draft tree as its root-to-leaf chains.
+ *
+ * [review] "How it works", step 4 (verify preprocess): the tree is unfolded
+ * into chains -- the toy's A-B, A-C, A-B-B becomes Chain1 = A-B-B and
+ * Chain2 = A-C -- so that the prefix's state is shared and everything after
+ * the branch point is kept per chain; step 6 commits only the accepted
+ * chain's state.
+ *
+ * A chain is the path from the root to one leaf (a node no node names as
+ * parent), root side first; chains are numbered by their leaf's index; the
+ * root (the last prefix token) is not part of a chain.
+ * Inputs (device): n_nodes int32 [B], parent int32 [B][N_max] as written by
+ * build_tree (parent values outside [-1, i) are read as -1, so a malformed
+ * tree stays memory-safe); N_max <= 128; 1 <= gamma <= 64 (maximum depth).
+ * Outputs (device): n_chains int32 [B]; chain_len int32 [B][N_max] (0 past
+ * the last chain; a chain deeper than gamma keeps its first gamma nodes);
+ * chain_nodes int32 [B][N_max][gamma], node indices, -1 past each chain.
+ */
+int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int gamma,
+                  int* n_chains, int* chain_len, int* chain_nodes, void* stream);
+
+/*
  * tree_verify_attn -- branch-aware tree attention over a shared prefix.
  *
  * [review] Difficulty 1 (paper section 3.1) and "How it works", step 3: each

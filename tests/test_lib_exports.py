@@ -23,7 +23,7 @@ def test_all_declared_symbols_exported():
     names = _declared()
     assert names == sorted(["build_tree", "build_tree_expand", "tree_verify_attn", "accept_walk",
                             "commit_path", "select_global_budget", "tsv_fit_cost",
-                            "tsv_workspace_size", "tsv_status_string"])
+                            "tsv_workspace_size", "tsv_status_string", "unfold_chains"])
     lib = ctypes.CDLL(tsv._lib.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -78,6 +78,9 @@ def test_host_validation_without_launch():
     assert L.tree_verify_attn(p, p, p, p, p, 1200, p, p, p, 1, 4, 10, 4, 2, 600, 64, 1, 0.1,
                               p, nul, p, 1 << 30, nul) == -2      # head dim > 576
     assert L.accept_walk(p, 1, 1, 4, 8, 65, p, p, p, p, p, p, p, 1 << 20, nul) == -2  # gamma
+    assert L.unfold_chains(p, p, 4, 8, 4, p, p, nul, nul) == -1                # null output
+    assert L.unfold_chains(p, p, 4, 129, 4, p, p, p, nul) == -1                # N_max > 128
+    assert L.unfold_chains(p, p, 4, 8, 65, p, p, p, nul) == -1                 # gamma > 64
     assert L.select_global_budget(p, p, p, p, p, p, 4, 8, nul, 10, nul) == -1   # null table
     assert L.select_global_budget(p, p, p, p, p, p, 4, 129, p, 10, nul) == -1   # N_max > 128
     assert L.select_global_budget(p, p, p, p, p, p, 65, 128, p, 10, nul) == -2  # 8320 candidates

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     select_global_budget,
     status_string,
     tree_verify_attn,
+    unfold_chains,
     workspace,
     workspace_size,
 )

@@ -54,6 +54,7 @@ _SIGS = {
                      ctypes.POINTER(ctypes.c_double), _I, ctypes.c_double,
                      ctypes.POINTER(tsv_cost)],
     "select_global_budget": [_P, _P, _P, _P, _P, _P, _I, _I, _P, _L, _P],
+    "unfold_chains": [_P, _P, _I, _I, _I, _P, _P, _P, _P],
     "tsv_workspace_size": [_I] * 12,
     "tsv_status_string": [_I],
 }
@@ -243,6 +244,23 @@ def select_global_budget(tree: dict, sps: torch.Tensor) -> dict:
         _stream(tree["n_nodes"].device))
     _check("select_global_budget", code)
     return tree
+
+
+def unfold_chains(tree: dict, gamma: int) -> dict:
+    """Root-to-leaf chains of build_tree's trees: n_chains [B], chain_len
+    [B, N_max], chain_nodes [B, N_max, gamma] (int32, device)."""
+    n_nodes = _dev(tree["n_nodes"], "n_nodes", torch.int32)
+    parent = _dev(tree["parent"], "parent", torch.int32)
+    B, N_max = parent.shape
+    dev = parent.device
+    out = dict(n_chains=torch.empty(B, dtype=torch.int32, device=dev),
+               chain_len=torch.empty(B, N_max, dtype=torch.int32, device=dev),
+               chain_nodes=torch.empty(B, N_max, gamma, dtype=torch.int32, device=dev))
+    code = lib().unfold_chains(_ptr(n_nodes), _ptr(parent), B, N_max, gamma,
+                               _ptr(out["n_chains"]), _ptr(out["chain_len"]),
+                               _ptr(out["chain_nodes"]), _stream(dev))
+    _check("unfold_chains", code)
+    return out
 
 
 def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -240,6 +240,22 @@ int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, floa
   return launch_status(launch_global_budget(a, static_cast<hipStream_t>(stream)));
 }
 
+int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int gamma,
+                  int* n_chains, int* chain_len, int* chain_nodes, void* stream) {
+  if (!n_nodes || !parent || !n_chains || !chain_len || !chain_nodes) return TSV_EINVAL;
+  if (B < 1 || N_max < 1 || N_max > kMaxNodes || gamma < 1 || gamma > kMaxGamma) return TSV_EINVAL;
+  ChainArgs a;
+  a.n_nodes = n_nodes;
+  a.parent = parent;
+  a.B = B;
+  a.N_max = N_max;
+  a.gamma = gamma;
+  a.n_chains = n_chains;
+  a.chain_len = chain_len;
+  a.chain_nodes = chain_nodes;
+  return launch_status(launch_unfold_chains(a, static_cast<hipStream_t>(stream)));
+}
+
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const void* k_tree, const void* v_tree, long kv_row_stride,
                      const int* prefix_len, const int* n_nodes,

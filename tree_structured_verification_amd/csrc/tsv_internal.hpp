@@ -60,6 +60,17 @@ struct GlobalBudgetArgs {
 };
 hipError_t launch_global_budget(const GlobalBudgetArgs& a, hipStream_t s);
 
+// ---- unfold_chains -------------------------------------------------------
+struct ChainArgs {
+  const int* n_nodes;
+  const int* parent;
+  int B, N_max, gamma;
+  int* n_chains;
+  int* chain_len;
+  int* chain_nodes;
+};
+hipError_t launch_unfold_chains(const ChainArgs& a, hipStream_t s);
+
 // ---- accept_walk -------------------------------------------------------
 struct ArgmaxPlan {
   int rows, V, nseg, seg_len;
