@@ -203,7 +203,7 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       n_par[m] = par;
       n_dep[m] = dep;
       n_rank[m] = rank;
-      n_row[m] = row;
+      if constexpr (PER_NODE) n_row[m] = row;
       n_sc[m] = sc;
     }
     drop_front();
@@ -225,7 +225,8 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   for (int i = lane; i < a.N_max; i += 64) {
     const bool v = i < n;
     a.parent[nb + i] = v ? n_par[i] : -1;
-    a.token[nb + i] = v ? s_i[n_row[i] * a.k + n_rank[i]] : -1;
+    const int trow = v ? (PER_NODE ? n_row[i] : n_dep[i] - 1) : 0;
+    a.token[nb + i] = v ? s_i[trow * a.k + n_rank[i]] : -1;
     a.depth[nb + i] = v ? n_dep[i] : -1;
     a.score[nb + i] = v ? n_sc[i] : 0.0f;
     uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
