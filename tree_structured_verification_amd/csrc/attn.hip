@@ -38,6 +38,10 @@ constexpr int kValuRows = 16;
 constexpr int kValuKeys = 16;
 constexpr int kValuMaxD = 576;
 constexpr float kLazy = 8.0f;  // lazy-rescale threshold, log2 units
+// grouped path: a split's published rows, 128 rows x 128 bf16, in floats
+constexpr size_t kGqaPartFloats = 128 * 128 / 2;
+// grouped path: at least one split per this many keys of a unit
+constexpr long long kSplitKeys = 4096;
 
 // Whether virtual key `key` is visible to a row whose node has ancestor words
 // w[0..3]: prefix keys always, scratch keys iff their bit is set, nothing at or
@@ -317,18 +321,22 @@ __device__ __forceinline__ void wait_later(int later) {
 // Work item of the one-kernel grouped-query path.  Workgroup ids are dealt to
 // the XCDs round robin (id % 8); consecutive ids on one XCD take the S splits
 // of one unit, so a unit's splits run side by side and share that XCD's L2,
-// where the last one to finish reads the others' partials.
+// where the last one to finish reads the others' partials.  A unit is (row
+// block, request, KV head), in that order of significance.
 __device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& unit) {
   const int id = static_cast<int>(blockIdx.x);
   const int slot = id >> 3;
   unit = (slot / a.S) * 8 + (id & 7);
   const int split = slot % a.S;
   if (unit >= a.units) return false;
-  const int per_b = a.Hkv * a.rbs;
-  c.b = unit / per_b;
-  const int rem = unit - c.b * per_b;
-  c.kvh = rem / a.rbs;
-  c.rowb = rem - c.kvh * a.rbs;
+  // units are numbered row block first: the first row block of every
+  // (request, KV head) comes before any second one, so the work of short
+  // trees (one row block) is spread over all XCDs and dispatched first
+  const int per_rb = a.B * a.Hkv;
+  c.rowb = unit / per_rb;
+  const int rem = unit - c.rowb * per_rb;
+  c.b = rem / a.Hkv;
+  c.kvh = rem - c.b * a.Hkv;
   c.n_b = clampi(a.n_nodes[c.b], 0, a.N_max);
   c.l_b = clampi(a.prefix_len[c.b], 0, a.L_cap);
   c.rows_b = c.n_b * a.G;
@@ -710,7 +718,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const int wr = wave * RG + rg;
-    uint64_t* pa = reinterpret_cast<uint64_t*>(a.part_acc + item * RB * D) + static_cast<size_t>(wr) * NDB * 64;
+    uint64_t* pa = reinterpret_cast<uint64_t*>(a.part_acc + item * kGqaPartFloats) + static_cast<size_t>(wr) * NDB * 64;
     const float lt = lacc[rg][0];
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
@@ -745,7 +753,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_pipe_kernel(AttnArgs a) {
            wr * 16 + lr;
   };
   auto rows_ptr = [&](int s2, int wr) {
-    return reinterpret_cast<const uint64_t*>(a.part_acc + (static_cast<size_t>(unit) * a.S + s2) * RB * D) +
+    return reinterpret_cast<const uint64_t*>(a.part_acc + (static_cast<size_t>(unit) * a.S + s2) * kGqaPartFloats) +
            static_cast<size_t>(wr) * NDB * 64 + lane;
   };
   // one split's term of the combined row, weighted by 2^(m - M) * l; the
@@ -1592,6 +1600,12 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
     if (c < p.min_chunk) c = p.min_chunk;
     c = (c + p.KT - 1) / p.KT * p.KT;
     p.S = static_cast<int>((keys_max + c - 1) / c);
+    // The capacity sizing above assumes every unit is busy.  When most are
+    // not (adaptive budgets leave many requests with few or no nodes, and a
+    // unit's rows past n_b * G are idle), the busy units still need their
+    // long prefixes cut: at least one split per kSplitKeys keys.
+    const long long s_len = (keys_max + kSplitKeys - 1) / kSplitKeys;
+    if (p.S < s_len) p.S = static_cast<int>(s_len);
     p.chunk = p.min_chunk;  // the device cuts each unit's actual keys into S chunks of at least this
     p.items_max = units_pad * p.S;
     size_t off = 0;
@@ -1601,7 +1615,8 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
     p.off_ml = off;
     off = align_up(off + static_cast<size_t>(p.items_max) * p.RB * 2 * sizeof(float));
     p.off_acc = off;
-    off = align_up(off + static_cast<size_t>(p.items_max) * p.RB * sh.d_v * sizeof(float));
+    // partial rows are published normalised, in bf16
+    off = align_up(off + static_cast<size_t>(p.items_max) * p.RB * sh.d_v * sizeof(uint16_t));
     p.bytes = off;
     return p;
   } else if (bf && aligned && shared_value && sh.d_qk == 576 && sh.d_v == 512) {
