@@ -1332,15 +1332,26 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   const T* kt = static_cast<const T*>(a.kt);
   const T* vt = static_cast<const T*>(a.vt);
 
-  for (int e = tid; e < R * DQ; e += 256) {
-    const int r = e / DQ, x = e % DQ;
-    const int rg = c.rowb * R + r;
-    float v = 0.f;
-    if (rg < c.rows_b) {
-      const int node = rg / a.G, h = c.kvh * a.G + rg % a.G;
-      v = ld_elem<T>(qp + ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * DQ + x);
+  for (int e0 = tid; e0 < R * DQ; e0 += 256 * 8) {
+    float qr[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 256 * u;
+      qr[u] = 0.f;
+      if (e < R * DQ) {
+        const int r = e / DQ, x = e % DQ;
+        const int rg = c.rowb * R + r;
+        if (rg < c.rows_b) {
+          const int node = rg / a.G, h = c.kvh * a.G + rg % a.G;
+          qr[u] = ld_elem<T>(qp + ((static_cast<size_t>(c.b) * a.N_max + node) * a.Hq + h) * DQ + x);
+        }
+      }
     }
-    sQ[r * DQ + x] = v;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 256 * u;
+      if (e < R * DQ) sQ[e] = qr[u];
+    }
   }
   if (tid < R * 4) {
     const int r = tid / 4, w = tid % 4;
@@ -1357,31 +1368,87 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < (DM + K - 1) / K; ++j) acc[j] = 0.f;
 
+  // A tile's K and V elements are loaded in chunks of CH per thread, every
+  // load of a chunk issued before any of its LDS stores.  When one chunk holds
+  // the whole tile (head dimensions up to 128), the next tile's loads are
+  // issued before this tile's arithmetic, so that their latency overlaps it;
+  // a thread's (key, column) pairs are then the same for every tile and are
+  // computed once.
+  constexpr int CH = 8;
+  const int kv_elems = K * (DQ > DVv ? DQ : DVv);
+  const bool pipe = kv_elems <= 256 * CH;
+  float kr[CH], vr[CH];
+  int kkey[CH], kx[CH], vkey[CH], vx[CH];
+  auto split_idx = [&](int e0) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int e = e0 + 256 * u;
+      kkey[u] = e < K * DQ ? e / DQ : -1;
+      kx[u] = e < K * DQ ? e % DQ : 0;
+      vkey[u] = e < K * DVv ? e / DVv : -1;
+      vx[u] = e < K * DVv ? e % DVv : 0;
+    }
+  };
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      kr[u] = 0.f;
+      vr[u] = 0.f;
+      if (kkey[u] >= 0 && t0 + kkey[u] < c.k_end) {
+        bool tr;
+        const long off = key_row(a, c, t0 + kkey[u], &tr) + static_cast<long>(c.kvh) * DQ + kx[u];
+        kr[u] = ld_elem<T>((tr ? kt : kc) + off);
+      }
+      if (vkey[u] >= 0 && t0 + vkey[u] < c.k_end) {
+        bool tr;
+        const long off = key_row(a, c, t0 + vkey[u], &tr) + static_cast<long>(c.kvh) * DVv + vx[u];
+        vr[u] = ld_elem<T>((tr ? vt : vc) + off);
+      }
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      if (kkey[u] >= 0) sK[kkey[u] * KS + kx[u]] = kr[u];
+      if (vkey[u] >= 0) sV[vkey[u] * DVv + vx[u]] = vr[u];
+    }
+  };
+  if (pipe) {
+    split_idx(tid);
+    if (c.k_beg < c.k_end) fetch(c.k_beg);
+  }
   for (int t0 = c.k_beg; t0 < c.k_end; t0 += K) {
     __syncthreads();
-    for (int e = tid; e < K * DQ; e += 256) {
-      const int key = e / DQ, x = e % DQ, kk = t0 + key;
-      float v = 0.f;
-      if (kk < c.k_end) {
-        bool tr;
-        const long off = key_row(a, c, kk, &tr) + static_cast<long>(c.kvh) * DQ + x;
-        v = ld_elem<T>((tr ? kt : kc) + off);
+    if (pipe) {
+      put();
+    } else {
+      for (int e0 = tid; e0 < kv_elems; e0 += 256 * CH) {
+        split_idx(e0);
+        fetch(t0);
+        put();
       }
-      sK[key * KS + x] = v;
-    }
-    for (int e = tid; e < K * DVv; e += 256) {
-      const int key = e / DVv, x = e % DVv, kk = t0 + key;
-      float v = 0.f;
-      if (kk < c.k_end) {
-        bool tr;
-        const long off = key_row(a, c, kk, &tr) + static_cast<long>(c.kvh) * DVv + x;
-        v = ld_elem<T>((tr ? vt : vc) + off);
-      }
-      sV[key * DVv + x] = v;
     }
     __syncthreads();
+    if (pipe && t0 + K < c.k_end) fetch(t0 + K);
+    // Scores: the dot product in the order x = 0, 1, ..., its LDS reads
+    // issued sixteen at a time ahead of their FMAs.
     float s = 0.f;
-    for (int x = 0; x < DQ; ++x) s = fmaf(sQ[row * DQ + x], sK[col * KS + x], s);
+    {
+      const float* qrow = sQ + row * DQ;
+      const float* krow = sK + col * KS;
+      int x = 0;
+      for (; x + 16 <= DQ; x += 16) {
+        float qv[16], kv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          qv[u] = qrow[x + u];
+          kv[u] = krow[x + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s = fmaf(qv[u], kv[u], s);
+      }
+      for (; x < DQ; ++x) s = fmaf(qrow[x], krow[x], s);
+    }
     const int key = t0 + col;
     const bool ok = row_ok && key_visible(sA[row], key, c.l_b, c.k_end);
     s = ok ? s * a.scale_log2 : -INFINITY;
@@ -1399,13 +1466,23 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     m_run = mnew;
     sP[row * (K + 1) + col] = p;
     __syncthreads();
+    // Values: column dv = col + K j of the row's output, the keys in order.
+    // The test on j is uniform; a lane past d_v reads a clamped column and
+    // its result is never stored, so the reads of a column are not split by
+    // a divergent branch and issue ahead of their FMAs.
+    float pr[K];
+#pragma unroll
+    for (int kk = 0; kk < K; ++kk) pr[kk] = sP[row * (K + 1) + kk];
 #pragma unroll
     for (int j = 0; j < (DM + K - 1) / K; ++j) {
-      const int dv = col + K * j;
-      if (dv < DVv) {
+      if (K * j < DVv) {
+        const int dv = min(col + K * j, DVv - 1);
+        float vv[K];
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) vv[kk] = sV[kk * DVv + dv];
         float v = acc[j] * alpha;
 #pragma unroll
-        for (int kk = 0; kk < K; ++kk) v = fmaf(sP[row * (K + 1) + kk], sV[kk * DVv + dv], v);
+        for (int kk = 0; kk < K; ++kk) v = fmaf(pr[kk], vv[kk], v);
         acc[j] = v;
       }
     }
@@ -1629,7 +1706,8 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
     p.path = kPathValu;
     p.RB = kValuRows;
     p.KT = kValuKeys;
-    p.min_chunk = 256;
+    // small problems are latency-bound: down to one key tile per workgroup
+    p.min_chunk = kValuKeys;
     p.target_items = 1024;
   }
   const int G = sh.Hq / sh.Hkv;
