@@ -48,3 +48,4 @@ from .global_budget import global_budget, global_order  # noqa: F401
 from .chains import unfold_chains  # noqa: F401
 from .walk import accept_walk, row_argmax  # noqa: F401
 from .commit import commit_path  # noqa: F401
+from .compress import block_state, chain_entries, compress_chains, refresh_compressed  # noqa: F401
