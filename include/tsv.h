@@ -16,6 +16,8 @@
  *   tree_verify_attn  branch-aware attention of every tree node
  *   accept_walk       target argmax -> longest accepted root-to-node path
  *   commit_path       accepted scratch KV -> persistent cache
+ * (unfold_chains, compress_chains and refresh_compressed keep a per-chain
+ * compressed state beside the KV and commit the accepted chain's part),
  * and, once per deployment, tsv_fit_cost: measured latencies -> the cost
  * model build_tree's adaptive budget uses.
  *
@@ -216,6 +218,70 @@ int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, floa
  */
 int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int gamma,
                   int* n_chains, int* chain_len, int* chain_nodes, void* stream);
+
+/*
+ * compress_chains -- every chain's compressed state (verify preprocess).
+ *
+ * [review] "How it works", steps 4 and 6, and "Secret weapon" (paper
+ * sections 4.1-4.2 as summarised there): the prefix's compressed state is
+ * reused, compression after the branch point is done per chain (one
+ * compression over two chains would mix exclusive histories), and the
+ * chains' temporary compressed tokens and intermediate buffers stay in a
+ * scratch pad.  The pages give no formula for DeepSeek-V4's C4 / C128
+ * compression; this library uses the block mean as a stand-in: entry j of a
+ * token sequence is the mean of the rows of positions j*c .. j*c + c - 1,
+ * and the intermediate buffer ("tail") is the fp32 sum of the rows of the
+ * incomplete last block.
+ *
+ * For request b (prefix length l_b) and chain q < n_chains[b]: s = tail[b];
+ * for t = 0 .. chain_len - 1, s += the scratch row of chain node t; when
+ * l_b + t + 1 is a multiple of c, entry s / c is written and s restarts at
+ * zero.  Each column is summed in that order in fp32.
+ *   rows        dtype [B][N_max] rows of row_stride elements (the scratch
+ *               keys or values, e.g. k_tree with E = Hkv*d_k); the first E
+ *               columns are compressed
+ *   tail        fp32 [B][E]; prefix_len int32 [B]
+ *   n_chains, chain_len, chain_nodes  as written by unfold_chains (gamma)
+ * Outputs (device): entries fp32 [B][N_max][M][E], M = (c - 1 + gamma) / c,
+ * entries past each chain's count untouched; n_entries int32 [B][N_max]:
+ * the count written, 0 past the last chain, -1 for a chain that cannot be
+ * read (negative prefix length or a node index outside [0, N_max); nothing
+ * written for it).
+ * Requirements: c >= 1 (4 and 128 for C4 / C128); row_stride >= E >= 1,
+ * E <= 2^24; N_max <= 128; 1 <= gamma <= 64.
+ */
+int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
+                    const float* tail, const int* prefix_len, const int* n_chains,
+                    const int* chain_len, const int* chain_nodes, int B, int N_max,
+                    int gamma, float* entries, int* n_entries, void* stream);
+
+/*
+ * refresh_compressed -- commit the accepted chain's compressed state.
+ *
+ * [review] "How it works", step 6: when a path is accepted only its chain's
+ * KV and compressed state reach the persistent cache; the other chains'
+ * temporary compressed tokens and buffers are dropped.  Call it after
+ * accept_walk and before commit_path (prefix_len is the length before the
+ * round's commit).
+ *
+ * For request b with m = accept_len[b]: q = the lowest-numbered chain whose
+ * node m - 1 is accept_nodes[b][m-1] (any chain through it gives the same
+ * result); the e = (l_b % c + m) / c blocks closed by the accepted tokens
+ * are copied from entries[b][q] to comp[b][l_b / c ...]; tail[b] becomes
+ * tail[b] plus the accepted rows when e == 0, else the sum of the accepted
+ * rows after the last closed block (in sequence order, fp32).
+ *   entries     as compress_chains wrote them for the same prefix lengths
+ *   comp        fp32 [B][Lc_cap][E] persistent compressed entries (in/out)
+ *   tail        fp32 [B][E] (in/out)
+ * status int32 [B]: 0 done (m == 0 changes nothing); 1 l_b / c + e > Lc_cap
+ * (nothing written); 2 m outside [0, gamma], l_b < 0, an accepted node
+ * outside [0, N_max) or no chain holding the path (nothing written).
+ */
+int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int c,
+                       const int* prefix_len, const int* accept_len, const int* accept_nodes,
+                       const int* n_chains, const int* chain_len, const int* chain_nodes,
+                       const float* entries, int B, int N_max, int gamma, float* comp,
+                       int Lc_cap, float* tail, int* status, void* stream);
 
 /*
  * tree_verify_attn -- branch-aware tree attention over a shared prefix.

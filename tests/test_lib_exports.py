@@ -23,7 +23,8 @@ def test_all_declared_symbols_exported():
     names = _declared()
     assert names == sorted(["build_tree", "build_tree_expand", "tree_verify_attn", "accept_walk",
                             "commit_path", "select_global_budget", "tsv_fit_cost",
-                            "tsv_workspace_size", "tsv_status_string", "unfold_chains"])
+                            "tsv_workspace_size", "tsv_status_string", "unfold_chains",
+                            "compress_chains", "refresh_compressed"])
     lib = ctypes.CDLL(tsv._lib.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -96,6 +97,21 @@ def test_host_validation_without_launch():
     assert L.build_tree_expand(p, 1, 3, 8, 2, 9, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
                                1 << 20, nul) == -1                # budget > N_max
     assert L.commit_path(p, nul, p, p, p, 64, p, p, 1, 4, 8, 1, 64, 64, 2, 1, p, nul) == -1
+    # compress_chains(rows, dtype, stride, E, c, tail, pl, nc, cl, cn, B, N, gamma, ent, n_ent, s)
+    assert L.compress_chains(p, 1, 64, 64, 4, p, p, p, p, p, 2, 8, 4, p, nul, nul) == -1  # null
+    assert L.compress_chains(p, 1, 32, 64, 4, p, p, p, p, p, 2, 8, 4, p, p, nul) == -1   # stride < E
+    assert L.compress_chains(p, 1, 64, 64, 0, p, p, p, p, p, 2, 8, 4, p, p, nul) == -1   # c < 1
+    assert L.compress_chains(p, 1, 64, 64, 4, p, p, p, p, p, 2, 129, 4, p, p, nul) == -1  # N_max
+    assert L.compress_chains(p, 1, 1 << 25, 1 << 25, 4, p, p, p, p, p, 2, 8, 4, p, p,
+                             nul) == -2                                                 # E > 2^24
+    # refresh_compressed(rows, dtype, stride, E, c, pl, al, an, nc, cl, cn, ent, B, N, gamma,
+    #                    comp, Lc_cap, tail, status, s)
+    assert L.refresh_compressed(p, 1, 64, 64, 4, p, p, p, p, p, p, p, 2, 8, 4, p, 8, p, nul,
+                                nul) == -1                                              # null status
+    assert L.refresh_compressed(p, 1, 64, 64, 4, p, p, p, p, p, p, p, 2, 8, 4, p, -1, p, p,
+                                nul) == -1                                              # Lc_cap < 0
+    assert L.refresh_compressed(p, 1, 64, 64, 4, p, p, p, p, p, p, p, 2, 8, 65, p, 8, p, p,
+                                nul) == -1                                              # gamma > 64
 
 
 def test_binding_requires_device_tensors():

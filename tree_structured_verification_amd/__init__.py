@@ -16,7 +16,9 @@ from ._lib import (  # noqa: F401
     expanded_rows,
     fit_cost,
     commit_path,
+    compress_chains,
     lib,
+    refresh_compressed,
     select_global_budget,
     status_string,
     tree_verify_attn,

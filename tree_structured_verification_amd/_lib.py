@@ -55,6 +55,9 @@ _SIGS = {
                      ctypes.POINTER(tsv_cost)],
     "select_global_budget": [_P, _P, _P, _P, _P, _P, _I, _I, _P, _L, _P],
     "unfold_chains": [_P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "compress_chains": [_P, _I, _L, _L, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P],
+    "refresh_compressed": [_P, _I, _L, _L, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P,
+                           _I, _P, _P, _P],
     "tsv_workspace_size": [_I] * 12,
     "tsv_status_string": [_I],
 }
@@ -261,6 +264,72 @@ def unfold_chains(tree: dict, gamma: int) -> dict:
                                _ptr(out["chain_nodes"]), _stream(dev))
     _check("unfold_chains", code)
     return out
+
+
+def _rows2d(rows: torch.Tensor, E: Optional[int]):
+    """Scratch rows [B, N_max, ...] viewed as rows of row_stride elements."""
+    _dev(rows, "rows")
+    if rows.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("rows must be bfloat16 or float32")
+    B, N_max = rows.shape[0], rows.shape[1]
+    stride = rows[0, 0].numel()
+    return B, N_max, stride, (stride if E is None else int(E))
+
+
+def compress_chains(rows: torch.Tensor, c: int, tail: torch.Tensor, prefix_len: torch.Tensor,
+                    chains: dict, gamma: int, E: Optional[int] = None,
+                    entries: Optional[torch.Tensor] = None,
+                    n_entries: Optional[torch.Tensor] = None):
+    """Every chain's compressed entries (block means of c tokens) from the
+    scratch rows [B, N_max, ...] (first E columns of a row, default all),
+    the prefix's tail sums fp32 [B, E] and unfold_chains' output.
+    Returns (entries fp32 [B, N_max, (c-1+gamma)//c, E], n_entries int32
+    [B, N_max])."""
+    B, N_max, stride, E = _rows2d(rows, E)
+    dev = rows.device
+    _dev(tail, "tail", torch.float32)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    nc = _dev(chains["n_chains"], "n_chains", torch.int32)
+    cl = _dev(chains["chain_len"], "chain_len", torch.int32)
+    cn = _dev(chains["chain_nodes"], "chain_nodes", torch.int32)
+    M = (c - 1 + gamma) // c
+    if entries is None:
+        entries = torch.zeros(B, N_max, M, E, dtype=torch.float32, device=dev)
+    if n_entries is None:
+        n_entries = torch.empty(B, N_max, dtype=torch.int32, device=dev)
+    code = lib().compress_chains(_ptr(rows), dtype_code(rows.dtype), stride, E, int(c), _ptr(tail),
+                                 _ptr(prefix_len), _ptr(nc), _ptr(cl), _ptr(cn), B, N_max, gamma,
+                                 _ptr(entries), _ptr(n_entries), _stream(dev))
+    _check("compress_chains", code)
+    return entries, n_entries
+
+
+def refresh_compressed(rows: torch.Tensor, c: int, prefix_len: torch.Tensor, walk: dict,
+                       chains: dict, entries: torch.Tensor, comp: torch.Tensor,
+                       tail: torch.Tensor, gamma: int, E: Optional[int] = None,
+                       status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Commit the accepted chain's compressed state into comp fp32 [B, Lc_cap,
+    E] and tail fp32 [B, E] (both updated in place); walk is accept_walk's
+    output.  Call before commit_path.  Returns status int32 [B]."""
+    B, N_max, stride, E = _rows2d(rows, E)
+    dev = rows.device
+    _dev(prefix_len, "prefix_len", torch.int32)
+    al = _dev(walk["accept_len"], "accept_len", torch.int32)
+    an = _dev(walk["accept_nodes"], "accept_nodes", torch.int32)
+    nc = _dev(chains["n_chains"], "n_chains", torch.int32)
+    cl = _dev(chains["chain_len"], "chain_len", torch.int32)
+    cn = _dev(chains["chain_nodes"], "chain_nodes", torch.int32)
+    _dev(entries, "entries", torch.float32)
+    _dev(comp, "comp", torch.float32)
+    _dev(tail, "tail", torch.float32)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    code = lib().refresh_compressed(_ptr(rows), dtype_code(rows.dtype), stride, E, int(c),
+                                    _ptr(prefix_len), _ptr(al), _ptr(an), _ptr(nc), _ptr(cl),
+                                    _ptr(cn), _ptr(entries), B, N_max, gamma, _ptr(comp),
+                                    comp.shape[1], _ptr(tail), _ptr(status), _stream(dev))
+    _check("refresh_compressed", code)
+    return status
 
 
 def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtsv.so")
-SOURCES = ["api.hip", "topk.hip", "tree.hip", "attn.hip", "walk.hip", "commit.hip", "fit.hip", "budget.hip", "chains.hip"]
+SOURCES = ["api.hip", "topk.hip", "tree.hip", "attn.hip", "walk.hip", "commit.hip", "fit.hip", "budget.hip", "chains.hip", "compress.hip"]
 ARCH = os.environ.get("TSV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -12,6 +12,8 @@ namespace {
 
 constexpr int kMaxNodes = 128;
 constexpr int kMaxGamma = 64;
+// columns of a compressed row (grid y = columns / 1024 stays far below its limit)
+constexpr long kMaxCompressCols = 1L << 24;
 constexpr int kMaxTopk = 128;
 constexpr int kMaxTopkTable = 4096;  // gamma * top_k staged in LDS by the tree kernel
 constexpr int kMaxHeadDim = 576;
@@ -254,6 +256,67 @@ int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int g
   a.chain_len = chain_len;
   a.chain_nodes = chain_nodes;
   return launch_status(launch_unfold_chains(a, static_cast<hipStream_t>(stream)));
+}
+
+int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
+                    const float* tail, const int* prefix_len, const int* n_chains,
+                    const int* chain_len, const int* chain_nodes, int B, int N_max,
+                    int gamma, float* entries, int* n_entries, void* stream) {
+  if (!rows || !tail || !prefix_len || !n_chains || !chain_len || !chain_nodes || !entries ||
+      !n_entries)
+    return TSV_EINVAL;
+  if (!dtype_ok(dtype) || E < 1 || row_stride < E || c < 1) return TSV_EINVAL;
+  if (B < 1 || N_max < 1 || N_max > kMaxNodes || gamma < 1 || gamma > kMaxGamma) return TSV_EINVAL;
+  if (E > kMaxCompressCols || static_cast<long long>(B) * N_max > 0x7fffffffLL) return TSV_EUNSUPPORTED;
+  CompressArgs a;
+  a.rows = rows;
+  a.row_stride = row_stride;
+  a.E = E;
+  a.c = c;
+  a.tail = tail;
+  a.prefix_len = prefix_len;
+  a.n_chains = n_chains;
+  a.chain_len = chain_len;
+  a.chain_nodes = chain_nodes;
+  a.B = B;
+  a.N_max = N_max;
+  a.gamma = gamma;
+  a.entries = entries;
+  a.n_entries = n_entries;
+  return launch_status(launch_compress_chains(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int c,
+                       const int* prefix_len, const int* accept_len, const int* accept_nodes,
+                       const int* n_chains, const int* chain_len, const int* chain_nodes,
+                       const float* entries, int B, int N_max, int gamma, float* comp,
+                       int Lc_cap, float* tail, int* status, void* stream) {
+  if (!rows || !prefix_len || !accept_len || !accept_nodes || !n_chains || !chain_len ||
+      !chain_nodes || !entries || !comp || !tail || !status)
+    return TSV_EINVAL;
+  if (!dtype_ok(dtype) || E < 1 || row_stride < E || c < 1 || Lc_cap < 0) return TSV_EINVAL;
+  if (B < 1 || N_max < 1 || N_max > kMaxNodes || gamma < 1 || gamma > kMaxGamma) return TSV_EINVAL;
+  if (E > kMaxCompressCols) return TSV_EUNSUPPORTED;
+  RefreshArgs a;
+  a.rows = rows;
+  a.row_stride = row_stride;
+  a.E = E;
+  a.c = c;
+  a.prefix_len = prefix_len;
+  a.accept_len = accept_len;
+  a.accept_nodes = accept_nodes;
+  a.n_chains = n_chains;
+  a.chain_len = chain_len;
+  a.chain_nodes = chain_nodes;
+  a.entries = entries;
+  a.B = B;
+  a.N_max = N_max;
+  a.gamma = gamma;
+  a.comp = comp;
+  a.Lc_cap = Lc_cap;
+  a.tail = tail;
+  a.status = status;
+  return launch_status(launch_refresh_compressed(a, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -71,6 +71,41 @@ struct ChainArgs {
 };
 hipError_t launch_unfold_chains(const ChainArgs& a, hipStream_t s);
 
+// ---- compress_chains / refresh_compressed --------------------------------
+struct CompressArgs {
+  const void* rows;        // scratch rows [B][N_max], row_stride elements each
+  long row_stride, E;
+  int c;
+  const float* tail;       // [B][E]
+  const int* prefix_len;   // [B]
+  const int* n_chains;     // [B]
+  const int* chain_len;    // [B][N_max]
+  const int* chain_nodes;  // [B][N_max][gamma]
+  int B, N_max, gamma;
+  float* entries;          // [B][N_max][(c - 1 + gamma) / c][E]
+  int* n_entries;          // [B][N_max]
+};
+hipError_t launch_compress_chains(const CompressArgs& a, int dtype, hipStream_t s);
+
+struct RefreshArgs {
+  const void* rows;
+  long row_stride, E;
+  int c;
+  const int* prefix_len;
+  const int* accept_len;   // [B]
+  const int* accept_nodes; // [B][gamma]
+  const int* n_chains;
+  const int* chain_len;
+  const int* chain_nodes;
+  const float* entries;
+  int B, N_max, gamma;
+  float* comp;             // [B][Lc_cap][E]
+  int Lc_cap;
+  float* tail;             // [B][E]
+  int* status;             // [B]
+};
+hipError_t launch_refresh_compressed(const RefreshArgs& a, int dtype, hipStream_t s);
+
 // ---- accept_walk -------------------------------------------------------
 struct ArgmaxPlan {
   int rows, V, nseg, seg_len;
