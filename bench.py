@@ -48,6 +48,12 @@ up to 20 % changes the adaptive budgets of workload 4.
 times select_global_budget (one budget across the batch) on workload 4's
 trees: 64 requests x 128 candidates against a linear-step-time table, and
 unfold_chains on the same trees.
+
+    python bench.py --compressed-state
+
+times compress_chains and refresh_compressed (the per-chain compressed state,
+block means of 4 and of 128 tokens) on workload 4's trees over scratch keys
+and values of 8 KV heads x 128 (bf16).
 """
 
 import argparse
@@ -66,7 +72,7 @@ if ROOT not in sys.path:
 
 import tree_structured_verification_amd as tsv  # noqa: E402
 from tree_structured_verification_amd import _lib  # noqa: E402
-from workloads import Cost, attention_inputs, config, marginals, target_logits  # noqa: E402
+from workloads import Cost, attention_inputs, config, marginals, prefix_lengths, target_logits  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = 2
@@ -292,6 +298,81 @@ def cost_profile(dev, perturbations=20):
         "grid": [[float(x), float(y), round(float(z), 3)] for x, y, z in zip(n, l, t)]}), flush=True)
 
 
+def compressed_state_bench(dev, K, W):
+    """compress_chains (keys and values) and refresh_compressed on the
+    adaptive workload's trees (64 requests x 128 best-first nodes, prefix
+    lengths 1024-32768) with scratch rows of 8 KV heads x 128 in bf16, for
+    blocks of 4 and of 128 tokens.  The accepted path of a request is the
+    first min(4, length) nodes of its first chain.  One JSON line per block
+    size; algorithmic bytes = every scratch row read once, the tails read,
+    the entries written (compress) or copied, the tails rewritten and the
+    accepted rows read (refresh)."""
+    import oracle
+    cfg = config(4)
+    tree = tsv.build_tree(marginals(cfg, 0, dev), cfg.top_k, cfg.N_max, cfg.N_max)
+    ch = tsv.unfold_chains(tree, cfg.gamma)
+    B, N, G, E = cfg.B, cfg.N_max, cfg.gamma, cfg.Hkv * cfg.d_qk
+    gen = torch.Generator(device=dev).manual_seed(7)
+    rows = [torch.randn(B, N, cfg.kv_stride, generator=gen, device=dev).to(torch.bfloat16)
+            for _ in range(2)]
+    pl_np = prefix_lengths(cfg, 0)
+    pl = torch.from_numpy(pl_np).to(dev)
+    tails = [torch.randn(B, E, generator=gen, device=dev) for _ in range(2)]
+    chn = {k: v.cpu().numpy() for k, v in ch.items()}
+    m = np.minimum(chn["chain_len"][:, 0], 4).astype(np.int32)
+    acc = np.full((B, G), -1, dtype=np.int32)
+    for b in range(B):
+        acc[b, :m[b]] = chn["chain_nodes"][b, 0, :m[b]]
+    walk = dict(accept_len=torch.from_numpy(m).to(dev), accept_nodes=torch.from_numpy(acc).to(dev))
+    n_rows = int(tree["n_nodes"].sum())
+    stream = torch.cuda.current_stream(dev)
+    for c in (4, 128):
+        M = (c - 1 + G) // c
+        ent = [torch.zeros(B, N, M, E, dtype=torch.float32, device=dev) for _ in range(2)]
+        n_ent = [torch.empty(B, N, dtype=torch.int32, device=dev) for _ in range(2)]
+        Lc = int(pl_np.max()) // c + G + 1
+        comp = [torch.zeros(B, Lc, E, dtype=torch.float32, device=dev) for _ in range(2)]
+        work_tail = [t.clone() for t in tails]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(W + K)]
+        for s in range(W + K):
+            for i in range(2):
+                work_tail[i].copy_(tails[i])
+            ev[s][0].record(stream)
+            for i in range(2):
+                tsv.compress_chains(rows[i], c, work_tail[i], pl, ch, G, E=E, entries=ent[i],
+                                    n_entries=n_ent[i])
+            ev[s][1].record(stream)
+            for i in range(2):
+                tsv.refresh_compressed(rows[i], c, pl, walk, ch, ent[i], comp[i], work_tail[i], G, E=E)
+            ev[s][2].record(stream)
+        torch.cuda.synchronize()
+        t_c = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[W:]])) * 1e3
+        t_r = float(np.mean([e[1].elapsed_time(e[2]) for e in ev[W:]])) * 1e3
+        ne = n_ent[0].cpu().numpy()
+        n_entries = int(ne[ne > 0].sum())
+        e_acc = int(np.sum((pl_np % c + m) // c))
+        bytes_c = 2 * (n_rows * E * 2 + B * E * 4 + n_entries * E * 4)
+        bytes_r = 2 * (2 * e_acc * E * 4 + 2 * B * E * 4 + int(m.sum()) * E * 2)
+        # the oracle on a sample of 4 requests (keys only), for the CPU baseline
+        smp = 4
+        rows_np = rows[0][:smp].float().cpu().numpy()[:, :, :E].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.compress_chains(rows_np, tails[0][:smp].cpu().numpy(), pl_np[:smp],
+                               chn["n_chains"][:smp], chn["chain_len"][:smp],
+                               chn["chain_nodes"][:smp], c, G)
+        dt = time.perf_counter() - t0
+        print(json.dumps({
+            "compressed_state": f"C{c}: {B} requests x {N} nodes, {int(chn['n_chains'].sum())} chains, "
+                                f"keys and values of {cfg.Hkv} heads x {cfg.d_qk} (bf16)",
+            "calls": K, "compress_us": round(t_c, 2), "refresh_us": round(t_r, 2),
+            "entries_per_call": 2 * n_entries,
+            "compress_gbs": round(bytes_c / t_c / 1e3, 1), "compress_hbm_frac": round(bytes_c / t_c / 1e3 / 8000.0, 4),
+            "compress_algorithmic_bytes": bytes_c, "refresh_algorithmic_bytes": bytes_r,
+            "cpu_baseline": {"value_us": round(dt * 1e6, 1), "cores": 1, "kind": "oracle",
+                             "sample": f"compress_chains of the keys of {smp} of the {B} requests"}}),
+            flush=True)
+
+
 def global_budget_bench(dev, K, W):
     """Time select_global_budget on the adaptive workload's trees (64
     requests, 128 best-first nodes each: the largest batch of one sort),
@@ -362,6 +443,8 @@ def main():
                          "(101..104 of workloads/gen.py)")
     ap.add_argument("--global-budget", action="store_true",
                     help="time select_global_budget on the adaptive workload's trees")
+    ap.add_argument("--compressed-state", action="store_true",
+                    help="time compress_chains and refresh_compressed on the adaptive workload's trees")
     ap.add_argument("--cost-profile", action="store_true",
                     help="measure and fit the verification cost C_v(n; l) and test the "
                          "adaptive budget's robustness to perturbed coefficients")
@@ -390,6 +473,9 @@ def main():
         return
     if args.global_budget:
         global_budget_bench(dev, args.steps, args.warmup)
+        return
+    if args.compressed_state:
+        compressed_state_bench(dev, args.steps, args.warmup)
         return
     if args.expand_workload:
         expand_only(args.expand_workload, args.steps, args.warmup, dev, args.cpu_requests)

@@ -283,7 +283,11 @@ int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
   a.gamma = gamma;
   a.entries = entries;
   a.n_entries = n_entries;
-  return launch_status(launch_compress_chains(a, dtype, static_cast<hipStream_t>(stream)));
+  // adjacent columns per thread: whole 4-column groups, rows and entries aligned
+  const int es = esize(dtype);
+  const bool vec = E % 4 == 0 && (row_stride * es) % (4 * es) == 0 && aligned_to(rows, 4 * es) &&
+                   aligned_to(tail, 16) && aligned_to(entries, 16);
+  return launch_status(launch_compress_chains(a, dtype, vec, static_cast<hipStream_t>(stream)));
 }
 
 int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int c,

@@ -11,10 +11,13 @@
 // the rows of positions j*c .. j*c + c - 1; the intermediate buffer is the
 // fp32 sum of the rows of the incomplete last block.
 //
-// Both kernels give every thread four columns of the rows (coalesced across
-// the workgroup) and walk the tokens in sequence order, so each column is
-// accumulated in exactly the order of the definition; a chain's rows are
-// loaded eight tokens ahead of their additions.
+// Both kernels give every thread four columns of the rows and walk the
+// tokens in sequence order, so each column is accumulated in exactly the
+// order of the definition; a chain's rows are loaded eight tokens ahead of
+// their additions.  When columns, row stride and buffers allow it, a
+// thread's four columns are adjacent and move as one 8-byte (bf16) or
+// 16-byte (fp32) load and one 16-byte store; otherwise they are strided by
+// the workgroup size.
 
 #include "tsv_device.hpp"
 #include "tsv_internal.hpp"
@@ -34,8 +37,28 @@ __device__ __forceinline__ float load_col<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load_col<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
+// four adjacent columns starting at p (vector path)
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+__device__ __forceinline__ void load4(const uint16_t* p, float (&v)[4]) {
+  const uint2 x = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(x.x << 16);
+  v[1] = __uint_as_float(x.x & 0xffff0000u);
+  v[2] = __uint_as_float(x.y << 16);
+  v[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
+// column k of this thread: adjacent (VEC) or strided by the workgroup size
+template <bool VEC>
+__device__ __forceinline__ long col_of(int k) {
+  return VEC ? static_cast<long>(blockIdx.y) * kCmpSlice + threadIdx.x * kCmpCols + k
+             : static_cast<long>(blockIdx.y) * kCmpSlice + threadIdx.x + k * kCmpThreads;
+}
+
 // Grid (B * N_max chain slots, column slices).
-template <typename T>
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kCmpThreads) void compress_chains_kernel(CompressArgs a) {
   const int N = a.N_max, G = a.gamma;
   const int b = blockIdx.x / N, q = blockIdx.x % N;
@@ -64,9 +87,11 @@ __global__ __launch_bounds__(kCmpThreads) void compress_chains_kernel(CompressAr
   float s[kCmpCols];
 #pragma unroll
   for (int k = 0; k < kCmpCols; ++k) {
-    col[k] = static_cast<long>(blockIdx.y) * kCmpSlice + threadIdx.x + k * kCmpThreads;
+    col[k] = col_of<VEC>(k);
     s[k] = col[k] < E ? a.tail[static_cast<size_t>(b) * E + col[k]] : 0.f;
   }
+  // vector path: E is a multiple of 4, so a thread's columns are all in or all out
+  const bool live = col[0] < E;
   const int M = (a.c - 1 + G) / a.c;
   float* out = a.entries + slot * M * E;
   const long long phase = l % a.c;   // tokens already in the prefix's open block
@@ -77,8 +102,17 @@ __global__ __launch_bounds__(kCmpThreads) void compress_chains_kernel(CompressAr
     for (int u = 0; u < kCmpAhead; ++u) {
       const int t = t0 + u;
       const T* r = rows + (static_cast<size_t>(b) * N + (t < len ? nodes[t] : 0)) * a.row_stride;
+      if constexpr (VEC) {
+        if (t < len && live) {
+          load4(r + col[0], v[u]);
+        } else {
 #pragma unroll
-      for (int k = 0; k < kCmpCols; ++k) v[u][k] = (t < len && col[k] < E) ? load_col<T>(r + col[k]) : 0.f;
+          for (int k = 0; k < kCmpCols; ++k) v[u][k] = 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kCmpCols; ++k) v[u][k] = (t < len && col[k] < E) ? load_col<T>(r + col[k]) : 0.f;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kCmpAhead; ++u) {
@@ -87,10 +121,19 @@ __global__ __launch_bounds__(kCmpThreads) void compress_chains_kernel(CompressAr
 #pragma unroll
       for (int k = 0; k < kCmpCols; ++k) s[k] += v[u][k];
       if ((phase + t + 1) % a.c == 0) {
+        float w[kCmpCols];
 #pragma unroll
         for (int k = 0; k < kCmpCols; ++k) {
-          if (col[k] < E) out[static_cast<size_t>(j) * E + col[k]] = s[k] / static_cast<float>(a.c);
+          w[k] = s[k] / static_cast<float>(a.c);
           s[k] = 0.f;
+        }
+        if constexpr (VEC) {
+          if (live)
+            *reinterpret_cast<float4*>(out + static_cast<size_t>(j) * E + col[0]) = make_float4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < kCmpCols; ++k)
+            if (col[k] < E) out[static_cast<size_t>(j) * E + col[k]] = w[k];
         }
         ++j;
       }
@@ -155,13 +198,16 @@ __global__ __launch_bounds__(kCmpThreads) void refresh_compressed_kernel(Refresh
 
 }  // namespace
 
-hipError_t launch_compress_chains(const CompressArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_compress_chains(const CompressArgs& a, int dtype, bool vec, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B) * a.N_max,
                   static_cast<unsigned>((a.E + kCmpSlice - 1) / kCmpSlice));
-  if (dtype == TSV_F32)
-    compress_chains_kernel<float><<<grid, dim3(kCmpThreads), 0, s>>>(a);
-  else
-    compress_chains_kernel<uint16_t><<<grid, dim3(kCmpThreads), 0, s>>>(a);
+  if (dtype == TSV_F32) {
+    if (vec) compress_chains_kernel<float, true><<<grid, dim3(kCmpThreads), 0, s>>>(a);
+    else compress_chains_kernel<float, false><<<grid, dim3(kCmpThreads), 0, s>>>(a);
+  } else {
+    if (vec) compress_chains_kernel<uint16_t, true><<<grid, dim3(kCmpThreads), 0, s>>>(a);
+    else compress_chains_kernel<uint16_t, false><<<grid, dim3(kCmpThreads), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -85,7 +85,7 @@ struct CompressArgs {
   float* entries;          // [B][N_max][(c - 1 + gamma) / c][E]
   int* n_entries;          // [B][N_max]
 };
-hipError_t launch_compress_chains(const CompressArgs& a, int dtype, hipStream_t s);
+hipError_t launch_compress_chains(const CompressArgs& a, int dtype, bool vec, hipStream_t s);
 
 struct RefreshArgs {
   const void* rows;
