@@ -247,7 +247,7 @@ int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int g
  * the count written, 0 past the last chain, -1 for a chain that cannot be
  * read (negative prefix length or a node index outside [0, N_max); nothing
  * written for it).
- * Requirements: c >= 1 (4 and 128 for C4 / C128); row_stride >= E >= 1,
+ * Requirements: 1 <= c <= 65536 (4 and 128 for C4 / C128); row_stride >= E >= 1,
  * E <= 2^24; N_max <= 128; 1 <= gamma <= 64.
  */
 int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
@@ -276,6 +276,7 @@ int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
  * status int32 [B]: 0 done (m == 0 changes nothing); 1 l_b / c + e > Lc_cap
  * (nothing written); 2 m outside [0, gamma], l_b < 0, an accepted node
  * outside [0, N_max) or no chain holding the path (nothing written).
+ * Requirements as for compress_chains; Lc_cap >= 0.
  */
 int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int c,
                        const int* prefix_len, const int* accept_len, const int* accept_nodes,

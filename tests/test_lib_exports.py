@@ -101,6 +101,7 @@ def test_host_validation_without_launch():
     assert L.compress_chains(p, 1, 64, 64, 4, p, p, p, p, p, 2, 8, 4, p, nul, nul) == -1  # null
     assert L.compress_chains(p, 1, 32, 64, 4, p, p, p, p, p, 2, 8, 4, p, p, nul) == -1   # stride < E
     assert L.compress_chains(p, 1, 64, 64, 0, p, p, p, p, p, 2, 8, 4, p, p, nul) == -1   # c < 1
+    assert L.compress_chains(p, 1, 64, 64, 1 << 17, p, p, p, p, p, 2, 8, 4, p, p, nul) == -1  # c
     assert L.compress_chains(p, 1, 64, 64, 4, p, p, p, p, p, 2, 129, 4, p, p, nul) == -1  # N_max
     assert L.compress_chains(p, 1, 1 << 25, 1 << 25, 4, p, p, p, p, p, 2, 8, 4, p, p,
                              nul) == -2                                                 # E > 2^24

@@ -14,6 +14,8 @@ constexpr int kMaxNodes = 128;
 constexpr int kMaxGamma = 64;
 // columns of a compressed row (grid y = columns / 1024 stays far below its limit)
 constexpr long kMaxCompressCols = 1L << 24;
+// tokens per compressed block
+constexpr int kMaxBlock = 1 << 16;
 constexpr int kMaxTopk = 128;
 constexpr int kMaxTopkTable = 4096;  // gamma * top_k staged in LDS by the tree kernel
 constexpr int kMaxHeadDim = 576;
@@ -265,7 +267,7 @@ int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
   if (!rows || !tail || !prefix_len || !n_chains || !chain_len || !chain_nodes || !entries ||
       !n_entries)
     return TSV_EINVAL;
-  if (!dtype_ok(dtype) || E < 1 || row_stride < E || c < 1) return TSV_EINVAL;
+  if (!dtype_ok(dtype) || E < 1 || row_stride < E || c < 1 || c > kMaxBlock) return TSV_EINVAL;
   if (B < 1 || N_max < 1 || N_max > kMaxNodes || gamma < 1 || gamma > kMaxGamma) return TSV_EINVAL;
   if (E > kMaxCompressCols || static_cast<long long>(B) * N_max > 0x7fffffffLL) return TSV_EUNSUPPORTED;
   CompressArgs a;
@@ -298,7 +300,7 @@ int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int
   if (!rows || !prefix_len || !accept_len || !accept_nodes || !n_chains || !chain_len ||
       !chain_nodes || !entries || !comp || !tail || !status)
     return TSV_EINVAL;
-  if (!dtype_ok(dtype) || E < 1 || row_stride < E || c < 1 || Lc_cap < 0) return TSV_EINVAL;
+  if (!dtype_ok(dtype) || E < 1 || row_stride < E || c < 1 || c > kMaxBlock || Lc_cap < 0) return TSV_EINVAL;
   if (B < 1 || N_max < 1 || N_max > kMaxNodes || gamma < 1 || gamma > kMaxGamma) return TSV_EINVAL;
   if (E > kMaxCompressCols) return TSV_EUNSUPPORTED;
   RefreshArgs a;
