@@ -236,3 +236,18 @@ def test_rounds_match_from_scratch():
         # every entry and the tail are sums of at most c + 1 fp32 terms
         assert np.all(np.abs(cn[b, :len(ent)] - ent) <= bound(a_ent, c + 2)), b
         assert np.all(np.abs(tn[b] - t) <= bound(a_t * 1.0, gamma + c + 2)), b
+
+
+@pytest.mark.parametrize("c", [4, 128])
+def test_bench_configuration(c):
+    """The configuration bench.py --compressed-state times: the adaptive
+    workload's trees at a fixed budget of 128 (64 requests, 7699 chains),
+    its prefix lengths, 1024 bf16 columns per row."""
+    from workloads import prefix_lengths
+    cfg = config(4)
+    tree = tsv.build_tree(marginals(cfg, 0, DEV), cfg.top_k, cfg.N_max, cfg.N_max)
+    n = tree["n_nodes"].cpu().numpy()
+    parent = tree["parent"].cpu().numpy()
+    rng = np.random.default_rng(100 + c)
+    run_case(rng, B=cfg.B, N=cfg.N_max, E=cfg.Hkv * cfg.d_qk, stride=cfg.kv_stride, gamma=cfg.gamma,
+             c=c, dtype=torch.bfloat16, sizes=n, parent=parent, l=prefix_lengths(cfg, 0))
