@@ -72,6 +72,8 @@ CASES = [
     ("bf16_latent_long", 1, 16, 128, 1, 576, 512, torch.bfloat16, [5000], [16], True),
     ("bf16_valu_d64", 2, 12, 6, 3, 64, 64, torch.bfloat16, [500, 9], [12, 7], False),
     ("bf16_n128_prefix0", 1, 128, 4, 1, 128, 128, torch.bfloat16, [0], [128], False),
+    # ~313 splits of 16 keys: several groups of 64 in the combine, two column passes of d_v 72
+    ("fp32_dv72_many_splits", 1, 8, 2, 2, 72, 72, torch.float32, [5000], [8], False),
 ]
 
 

@@ -1639,14 +1639,40 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const float inv = 1.0f / L;
   const size_t orow = (static_cast<size_t>(b) * a.N_max + i) * a.Hq + h;
   T* op = static_cast<T*>(a.out) + orow * a.d_v;
-  for (int dv = lane; dv < a.d_v; dv += 64) {
+  // Split s's weight is held by lane s % 64 of its group of 64 splits and
+  // read back by lane index; the partial rows of eight splits are loaded
+  // ahead of their FMAs.  The sum runs over s = 0, 1, ... as in the plain
+  // loop.
+  const float* pa = a.part_acc + (item0 * a.RB + r_loc) * a.d_v;
+  const size_t sstride = static_cast<size_t>(a.RB) * a.d_v;
+  auto weight = [&](int s) {
+    if (s >= splits) return 0.f;
+    const float ms = ml(s, 0);
+    return ms == -INFINITY ? 0.f : exp2f(ms - M);
+  };
+  const float w0 = weight(lane);   // the first group, shared by every column pass
+  // every lane stays in the column loop (a lane past d_v reads a clamped
+  // column and stores nothing), so the weights a lane reads back are always
+  // those of the current group
+  for (int dv0 = 0; dv0 < a.d_v; dv0 += 64) {
+    const int dv = min(dv0 + lane, a.d_v - 1);
     float acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float ms = ml(s, 0);
-      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      acc = fmaf(w, a.part_acc[((item0 + s) * a.RB + r_loc) * a.d_v + dv], acc);
+    for (int s0 = 0; s0 < splits; s0 += 64) {
+      const float wl = s0 == 0 ? w0 : weight(s0 + lane);
+      const int ns = min(64, splits - s0);
+      int t = 0;
+      for (; t + 8 <= ns; t += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = pa[(s0 + t + u) * sstride + dv];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), t + u)), x[u], acc);
+      }
+      for (; t < ns; ++t)
+        acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), t)), pa[(s0 + t) * sstride + dv], acc);
     }
-    st_elem<T>(op + dv, acc * inv);
+    if (dv0 + lane < a.d_v) st_elem<T>(op + dv, acc * inv);
   }
   if (lane == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * kLn2;
 }
