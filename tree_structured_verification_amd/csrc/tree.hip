@@ -39,6 +39,12 @@ __device__ __forceinline__ uint64_t frontier_key(float score, int depth, int par
          static_cast<uint64_t>(127 - rank);
 }
 
+// the exact score a frontier key was built from (inverse of ord_f32)
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t o = static_cast<uint32_t>(key >> 21);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 __device__ __forceinline__ double round_cost(const tsv_cost& c, int n, double l) {
   double m = static_cast<double>(n);
   double v = __dadd_rn(c.a, __dmul_rn(c.b, m));
@@ -107,40 +113,30 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   const float q_first = (!PER_NODE && lane < a.gamma) ? a.tk_p[tbase + static_cast<size_t>(lane) * a.k] : 0.f;
   __syncthreads();
 
-  // entry = order key (0 = empty), its exact score, its parent's score and
-  // (per node) the list its token comes from
+  // entry = order key (0 = empty; it holds the node's exact score) and (per
+  // node) the list its token comes from; the parent's score is read from
+  // the popped nodes' record when the entry is popped
   uint64_t fk[SL];
-  float fsc[SL], fps[SL];
   int frw[SL];
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
     fk[s] = 0;
-    fsc[s] = 0.f;
-    fps[s] = 0.f;
     frw[s] = 0;
   }
-  auto insert = [&](uint64_t x, float xs, float xp, int xr) {
+  auto insert = [&](uint64_t x, int xr) {
     int pos = 0;
 #pragma unroll
     for (int s = 0; s < SL; ++s) pos += __popcll(__ballot(fk[s] > x));
     uint64_t ck = 0;
-    float cs = 0.f, cp = 0.f;
     int cr = 0;
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const uint64_t k63 = readlane_u64(fk[s], 63);
-      const float s63 = readlane_f32(fsc[s], 63), p63 = readlane_f32(fps[s], 63);
       const uint64_t shk = wave_shift_u64<kShr1>(fk[s], ck);
-      const float shs = __uint_as_float(wave_shift_u32<kShr1>(__float_as_uint(fsc[s]), __float_as_uint(cs)));
-      const float shp = __uint_as_float(wave_shift_u32<kShr1>(__float_as_uint(fps[s]), __float_as_uint(cp)));
       const int P = s * 64 + lane;
       const bool keep = P < pos, here = P == pos;
       fk[s] = keep ? fk[s] : (here ? x : shk);
-      fsc[s] = keep ? fsc[s] : (here ? xs : shs);
-      fps[s] = keep ? fps[s] : (here ? xp : shp);
       ck = k63;
-      cs = s63;
-      cp = p63;
       if constexpr (PER_NODE) {
         const int r63 = __builtin_amdgcn_readlane(frw[s], 63);
         const int shr = static_cast<int>(wave_shift_u32<kShr1>(static_cast<uint32_t>(frw[s]), static_cast<uint32_t>(cr)));
@@ -153,11 +149,7 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const uint64_t nk = s + 1 < SL ? readlane_u64(fk[s + 1 < SL ? s + 1 : s], 0) : 0;
-      const float ns = s + 1 < SL ? readlane_f32(fsc[s + 1 < SL ? s + 1 : s], 0) : 0.f;
-      const float np = s + 1 < SL ? readlane_f32(fps[s + 1 < SL ? s + 1 : s], 0) : 0.f;
       fk[s] = wave_shift_u64<kShl1>(fk[s], nk);
-      fsc[s] = __uint_as_float(wave_shift_u32<kShl1>(__float_as_uint(fsc[s]), __float_as_uint(ns)));
-      fps[s] = __uint_as_float(wave_shift_u32<kShl1>(__float_as_uint(fps[s]), __float_as_uint(np)));
       if constexpr (PER_NODE) {
         const int nr = s + 1 < SL ? __builtin_amdgcn_readlane(frw[s + 1 < SL ? s + 1 : s], 0) : 0;
         frw[s] = static_cast<int>(wave_shift_u32<kShl1>(static_cast<uint32_t>(frw[s]), static_cast<uint32_t>(nr)));
@@ -168,7 +160,7 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   // the root's best child: score 1 * q, depth 1, rank 0
   {
     const float r0 = __fmul_rn(1.0f, s_p[0]);
-    insert(frontier_key(r0, 1, -1, 0), r0, 1.0f, 0);
+    insert(frontier_key(r0, 1, -1, 0), 0);
   }
 
   const double l = a.adaptive ? static_cast<double>(a.prefix_len[b]) : 0.0;
@@ -183,8 +175,8 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     const int rank = 127 - static_cast<int>(wl & 127);
     const int par = 255 - static_cast<int>((wl >> 7) & 255) - 1;
     const int dep = 63 - static_cast<int>((wl >> 15) & 63) + 1;
-    const float sc = readlane_f32(fsc[0], 0);
-    const float ps = readlane_f32(fps[0], 0);
+    const float sc = key_score(hk);
+    const float ps = par >= 0 ? n_sc[par] : 1.0f;   // the parent was popped earlier
     // list of the popped node's token (shared with its siblings) and the
     // list its children come from
     const int row = PER_NODE ? __builtin_amdgcn_readlane(frw[0], 0) : dep - 1;
@@ -209,11 +201,11 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     drop_front();
     if (rank + 1 < a.k) {
       const float v = __fmul_rn(ps, q_sib);
-      insert(frontier_key(v, dep, par, rank + 1), v, ps, row);
+      insert(frontier_key(v, dep, par, rank + 1), row);
     }
     if (dep < a.gamma) {
       const float v = __fmul_rn(sc, q_kid);
-      insert(frontier_key(v, dep + 1, m, 0), v, sc, kid_row);
+      insert(frontier_key(v, dep + 1, m, 0), kid_row);
     }
     ++m;
   }
