@@ -293,14 +293,18 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
         sel.offer(ok ? sel_key(v[u].w, e + 3) : 0);
       }
     };
+    // The next block's loads are issued without a condition (past the end
+    // they are clamped re-reads, never processed): behind a branch, the wait
+    // before the current block's last use would also cover them, and the
+    // two blocks would no longer overlap.
     float4 b0[8], b1[8];
     const int first = beg + 1024;
-    if (first < end) load_block(b0, first);
+    load_block(b0, first);
     for (int base = first; base < end; base += 4096) {
-      if (base + 2048 < end) load_block(b1, base + 2048);
+      load_block(b1, base + 2048);
       process(b0, base);
       if (base + 2048 >= end) break;
-      if (base + 4096 < end) load_block(b0, base + 4096);
+      load_block(b0, base + 4096);
       process(b1, base + 2048);
     }
   } else {
