@@ -217,8 +217,9 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
   const int row = blockIdx.x;
   if (threadIdx.x < kMaxSegments) published[threadIdx.x] = 0;
   __syncthreads();
-  const int beg = wave * seg_len;
-  const int end = min(V, beg + seg_len);
+  // wave-uniform, so that a block's buffer resource lives in scalar registers
+  const int beg = __builtin_amdgcn_readfirstlane(wave * seg_len);
+  const int end = __builtin_amdgcn_readfirstlane(min(V, beg + seg_len));
   const float* p = x + static_cast<size_t>(row) * V;
 
   WaveSelect<SLOTS> sel;
@@ -264,11 +265,20 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
     // re-reads the slice's last group and is ignored, so loads are
     // unconditional; two blocks alternate so that one is in flight while the
     // other is scanned
+    // A block is read through a buffer resource over [base, end) of the row
+    // (stride 0, dword 3 = 0x00020000, the raw 32-bit format of the CDNA
+    // buffer descriptor): loads past its end return zeros without touching
+    // memory and are never processed, so no address is clamped and the lane
+    // offsets stay constant registers.
     auto load_block = [&](float4 (&raw)[8], int base) {
+      const int avail = base < end ? end - base : 0;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(p) + (base < end ? base : 0), 0, avail * 4, 0x00020000);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int e = min(base + u * 256 + lane * 4, end - 4);
-        raw[u] = *reinterpret_cast<const float4*>(p + e);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (u * 256 + lane * 4) * 4, 0, 0);
+        raw[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                             __uint_as_float(v[3]));
       }
     };
     auto process = [&](const float4 (&v)[8], int base) {
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
       }
     };
     // The next block's loads are issued without a condition (past the end
-    // they are clamped re-reads, never processed): behind a branch, the wait
+    // they return zeros, never processed): behind a branch, the wait
     // before the current block's last use would also cover them, and the
     // two blocks would no longer overlap.
     float4 b0[8], b1[8];
