@@ -297,10 +297,34 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
         const int e = base + u * 256 + lane * 4;
         const bool ok = e < end;
         if (__ballot(ok && m4[u] >= thr) == 0) continue;
-        sel.offer(ok ? sel_key(v[u].x, e) : 0);
-        sel.offer(ok ? sel_key(v[u].y, e + 1) : 0);
-        sel.offer(ok ? sel_key(v[u].z, e + 2) : 0);
-        sel.offer(ok ? sel_key(v[u].w, e + 3) : 0);
+        // The lane's elements at or above the filter become keys (0 for the
+        // others), sorted descending by a five-step network; they are offered
+        // only while some lane still has one, so a group usually costs one
+        // or two offers instead of four.  The list's final contents do not
+        // depend on the order of the offers.  (Indices stay static: a loop
+        // over a lane's pending elements moved the block to scratch memory.)
+        uint64_t k0 = ok && v[u].x >= thr ? sel_key(v[u].x, e) : 0;
+        uint64_t k1 = ok && v[u].y >= thr ? sel_key(v[u].y, e + 1) : 0;
+        uint64_t k2 = ok && v[u].z >= thr ? sel_key(v[u].z, e + 2) : 0;
+        uint64_t k3 = ok && v[u].w >= thr ? sel_key(v[u].w, e + 3) : 0;
+        auto order = [](uint64_t& a, uint64_t& b) {
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          a = hi;
+          b = lo;
+        };
+        order(k0, k1);
+        order(k2, k3);
+        order(k0, k2);
+        order(k1, k3);
+        order(k1, k2);
+        sel.offer(k0);
+        if (__ballot(k1 != 0) != 0) {
+          sel.offer(k1);
+          if (__ballot(k2 != 0) != 0) {
+            sel.offer(k2);
+            if (__ballot(k3 != 0) != 0) sel.offer(k3);
+          }
+        }
       }
     };
     // The next block's loads are issued without a condition (past the end
