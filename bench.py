@@ -1,26 +1,32 @@
 """Throughput of one tree-structured verification round on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+                    [--no-cpu-baseline] [--no-per-workload]
 
 A step is one round of the whole hot path -- build_tree, tree_verify_attn,
-accept_walk, commit_path (one attention layer) -- over one batch of the
-grouped-query bf16 workload: 16 requests, 32 query / 8 KV heads x 128,
-prefix 4096, 16 drafter positions over a 151936-token vocabulary, top-32,
-fixed budget 32 (synthetic, seeded; see workloads/gen.py).  Inputs are
-resident in HBM before timing; three copies of every large input rotate
-across steps so the 256 MB last-level cache cannot serve a step from the
-previous one.  Each step commits into its own copy of the prefix lengths, so
-every step does identical work.
+accept_walk, commit_path (one attention layer) -- over one batch of a
+workload of workloads/gen.py.  The headline (`value`) is workload 2, the
+grouped-query bf16 batch: 16 requests, 32 query / 8 KV heads x 128, prefix
+4096, 16 drafter positions over a 151936-token vocabulary, top-32, fixed
+budget 32 (synthetic, seeded).  Inputs are resident in HBM before timing;
+three copies of every large input rotate across steps so the 256 MB
+last-level cache cannot serve a step from the previous one (one copy when a
+copy is several GB).  Each step commits into its own copy of the prefix
+lengths, so every step does identical work.
 
 Reported: verified tree tokens/s = sum_b n_b * K / wall time of K steps
-(bracketed by device synchronisation), the attention entry point's achieved
-HBM bandwidth on its algorithmic bytes (HIP events around each call on the
-launch stream, the only events in the timed steps; the entry point is a
-single kernel), the other calls' durations from an untimed pass with events
-between all calls, the HBM bytes one such
-launch actually moves (from the committed counter summary, when it was taken
-on the current kernel source), and the CPU oracle timed on the same
-workload on this host's cores.
+(bracketed by device synchronisation) and accepted tokens/s; the attention
+entry point's roofline (HBM bandwidth on its algorithmic bytes for grouped
+heads, bf16 matrix throughput on its algorithmic flops for latent heads;
+HIP events around each call on the launch stream, the only events in the
+timed steps), against the MI355X peak and against the peaks measured in the
+same run (a 1 GiB device copy, an 8192^3 bf16 GEMM); the other calls'
+durations from an untimed pass with events between all calls; the HBM bytes
+one attention launch actually moves (from the committed counter summary,
+when it was taken on the current kernel source); and the CPU oracle on this
+host's cores (all of them, and one thread) on a sample of the same round,
+each step scaled to the whole batch by its own unit.  `per_workload` repeats
+all of it for workloads 1-5 (fewer steps for the large ones).
 
     python bench.py --attention-only --copy-calibration 256 --steps 10 --warmup 2
 
@@ -75,6 +81,7 @@ from tree_structured_verification_amd import _lib  # noqa: E402
 from workloads import Cost, attention_inputs, config, marginals, prefix_lengths, target_logits  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak
 WORKLOAD = 2
 ROTATE = 3
 ATTN_SOURCE = os.path.join(ROOT, "tree_structured_verification_amd", "csrc", "attn.hip")
@@ -256,7 +263,7 @@ def cost_profile(dev, perturbations=20):
     pl = torch.from_numpy(pl_np).to(dev)
 
     def run(c):
-        g = tsv.build_tree(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=c, prefix_len=pl)
+        g = tsv.build_tree_fitted(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=c, prefix_len=pl)
         torch.cuda.synchronize()
         return g["n_nodes"].cpu().numpy(), g["score"].cpu().numpy()
 
@@ -426,122 +433,134 @@ def global_budget_bench(dev, K, W):
           flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=16,
-                    help="requests of the workload the CPU oracle runs")
-    ap.add_argument("--attention-only", action="store_true",
-                    help="run only the tree_verify_attn calls of the steps (for counter runs)")
-    ap.add_argument("--attention-workload", type=int, default=0, metavar="N",
-                    help="time only tree_verify_attn on workload N (implies --attention-only)")
-    ap.add_argument("--expand-workload", type=int, default=0, metavar="N",
-                    help="time only build_tree_expand on expansion workload N "
-                         "(101..104 of workloads/gen.py)")
-    ap.add_argument("--global-budget", action="store_true",
-                    help="time select_global_budget on the adaptive workload's trees")
-    ap.add_argument("--compressed-state", action="store_true",
-                    help="time compress_chains and refresh_compressed on the adaptive workload's trees")
-    ap.add_argument("--cost-profile", action="store_true",
-                    help="measure and fit the verification cost C_v(n; l) and test the "
-                         "adaptive budget's robustness to perturbed coefficients")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="first copy MIB MiB three times between device buffers, so that "
-                         "byte counters can be scaled by a kernel of known traffic")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
+def copy_peak_gbs(dev, mib=1024, reps=8):
+    """Measured device-to-device copy bandwidth (read + write bytes per
+    second) of torch's copy kernel on two buffers of `mib` MiB, far larger
+    than the 256 MB last-level cache; the best of `reps` copies."""
+    nb = mib << 20
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    stream = torch.cuda.current_stream(dev)
+    for a, b in ev:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    best = min(a.elapsed_time(b) for a, b in ev) / 1e3
+    del src, dst
+    return 2.0 * nb / best / 1e9
 
-    dev = torch.device("cuda:0")
-    if args.copy_calibration > 0:
-        nb = args.copy_calibration << 20
-        bufs = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(6)]
-        for i in range(3):
-            bufs[2 * i + 1].copy_(bufs[2 * i])
-        torch.cuda.synchronize()
-        del bufs
-    if args.attention_workload:
-        attention_only(args.attention_workload, args.steps, args.warmup, dev)
-        return
-    if args.cost_profile:
-        cost_profile(dev)
-        return
-    if args.global_budget:
-        global_budget_bench(dev, args.steps, args.warmup)
-        return
-    if args.compressed_state:
-        compressed_state_bench(dev, args.steps, args.warmup)
-        return
-    if args.expand_workload:
-        expand_only(args.expand_workload, args.steps, args.warmup, dev, args.cpu_requests)
-        return
-    cfg = config(WORKLOAD)
-    print(f"[bench] generating workload {cfg.name} on {torch.cuda.get_device_name(dev)}",
-          file=sys.stderr, flush=True)
+
+def gemm_peak_tflops(dev, n=8192, reps=5):
+    """Measured dense bf16 matrix throughput of the vendor GEMM (torch.matmul,
+    n x n x n), the best of `reps` calls."""
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    c = a @ b
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    stream = torch.cuda.current_stream(dev)
+    for e0, e1 in ev:
+        e0.record(stream)
+        torch.matmul(a, b, out=c)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    best = min(e0.elapsed_time(e1) for e0, e1 in ev) / 1e3
+    del a, b, c
+    return 2.0 * n ** 3 / best / 1e12
+
+
+def attention_flops(cfg, n, depth, prefix):
+    """Algorithmic matrix flops of one attention launch: every tree node
+    attends to its request's prefix and to its ancestors and itself (depth of
+    them), for every query head, scores and weighted values."""
+    pairs = sum(int(n[b]) * int(prefix[b]) + int(depth[b, :n[b]].sum()) for b in range(cfg.B))
+    return 2.0 * pairs * cfg.Hq * (cfg.d_qk + cfg.d_v)
+
+
+def round_bench(wid, K, W, dev):
+    """K timed rounds (after W) of workload wid: build_tree, tree_verify_attn,
+    accept_walk and commit_path on inputs resident in HBM.  Returns a dict of
+    measurements and host copies the CPU baseline needs."""
+    cfg = config(wid)
     L = _lib.lib()
+    dt = tsv.TSV_F32 if cfg.dtype == "f32" else tsv.TSV_BF16
+    adaptive = cfg.cost is not None
+    print(f"[bench] generating workload {cfg.name}", file=sys.stderr, flush=True)
     marg0 = marginals(cfg, 0, dev)
     ins0 = attention_inputs(cfg, 0, dev)
     prefix0 = ins0["prefix_len"].clone()
-    # tree of the workload (deterministic), used to lay out the target rows
-    tree0 = tsv.build_tree(marg0, cfg.top_k, cfg.n_budget, cfg.N_max)
+    # the workload's tree (deterministic) lays out the target rows
+    tree0 = tsv.build_tree(marg0, cfg.top_k, cfg.n_budget, cfg.N_max, cost=cfg.cost,
+                           prefix_len=prefix0 if adaptive else None)
     torch.cuda.synchronize()
     depth0 = tree0["depth"].cpu().numpy()
     n0 = tree0["n_nodes"].cpu().numpy()
     tl0 = target_logits(cfg, 0, depth0, n0, dev)
-
+    big = [marg0, ins0["q"], ins0["k_cache"], ins0["k_tree"], tl0]
+    if not cfg.mla:
+        big += [ins0["v_cache"], ins0["v_tree"]]
+    per_copy = sum(t.numel() * t.element_size() for t in big)
+    # rotating copies keep the 256 MB last-level cache from serving a step
+    # from the previous one; one copy of several GB already does that
+    copies = ROTATE if per_copy < (4 << 30) else 1
     sets = []
-    for r in range(ROTATE):
-        c = lambda t: t if r == 0 else t.clone()
-        sets.append(dict(marg=c(marg0), q=c(ins0["q"]), kc=c(ins0["k_cache"]),
-                         vc=c(ins0["v_cache"]), kt=c(ins0["k_tree"]), vt=c(ins0["v_tree"]),
-                         tl=c(tl0)))
-    K, W = args.steps, args.warmup
+    for r in range(copies):
+        c = (lambda t: t) if r == 0 else (lambda t: t.clone())
+        st = dict(marg=c(marg0), q=c(ins0["q"]), kc=c(ins0["k_cache"]), kt=c(ins0["k_tree"]),
+                  tl=c(tl0))
+        st["vc"] = st["kc"] if cfg.mla else c(ins0["v_cache"])
+        st["vt"] = st["kt"] if cfg.mla else c(ins0["v_tree"])
+        sets.append(st)
     prefixes = [prefix0.clone() for _ in range(K + W)]
 
-    # outputs and workspaces, allocated once
     B, N, Wd = cfg.B, cfg.N_max, (cfg.N_max + 31) // 32
     i32 = dict(dtype=torch.int32, device=dev)
     tr = dict(n_nodes=torch.empty(B, **i32), parent=torch.empty(B, N, **i32),
               token=torch.empty(B, N, **i32), depth=torch.empty(B, N, **i32),
               score=torch.empty(B, N, dtype=torch.float32, device=dev),
               anc_bits=torch.empty(B, N, Wd, **i32))
-    out = torch.empty(B, N, cfg.Hq, cfg.d_v, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(B, N, cfg.Hq, cfg.d_v, dtype=cfg.torch_dtype, device=dev)
     lse = torch.empty(B, N, cfg.Hq, dtype=torch.float32, device=dev)
     wk = dict(accept_len=torch.empty(B, **i32), accept_nodes=torch.empty(B, cfg.gamma, **i32),
               out_tokens=torch.empty(B, cfg.gamma + 1, **i32))
     status = torch.empty(B, **i32)
     ws_b = tsv.workspace(tsv.workspace_size(0, B, cfg.gamma, cfg.V, cfg.top_k, N), dev)
     ws_a = tsv.workspace(tsv.workspace_size(1, B, 1, 1, 1, N, cfg.L_cap, cfg.Hq, cfg.Hkv,
-                                            cfg.d_qk, cfg.d_v, tsv.TSV_BF16), dev)
-    ws_w = tsv.workspace(tsv.workspace_size(2, B, cfg.gamma, cfg.V, 1, N, dtype=tsv.TSV_BF16), dev)
+                                            cfg.d_qk, cfg.d_v, dt), dev)
+    ws_w = tsv.workspace(tsv.workspace_size(2, B, cfg.gamma, cfg.V, 1, N, dtype=dt), dev)
+    cost = None
+    if adaptive:
+        cost = tsv.tsv_cost(cfg.cost.a, cfg.cost.b, cfg.cost.c, cfg.cost.e, cfg.cost.c_d)
 
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     stride = cfg.kv_stride
 
     # pre-marshalled argument tuples: the timed loop only calls the library
     def step_args(s):
-        st = sets[s % ROTATE]
+        st = sets[s % copies]
         pl = prefixes[s]
-        a_build = (P(st["marg"]), B, cfg.gamma, cfg.V, cfg.top_k, cfg.n_budget, None, None, N,
+        a_build = (P(st["marg"]), B, cfg.gamma, cfg.V, cfg.top_k, cfg.n_budget,
+                   ctypes.byref(cost) if adaptive else None, P(pl) if adaptive else None, N,
                    P(tr["n_nodes"]), P(tr["parent"]), P(tr["token"]), P(tr["depth"]),
-                   P(tr["score"]), P(tr["anc_bits"]), None, None, P(ws_b), ws_b.numel(), sp)
+                   P(tr["score"]), P(tr["anc_bits"]), P(ws_b), ws_b.numel(), sp)
         a_attn = (P(st["q"]), P(st["kc"]), P(st["vc"]), P(st["kt"]), P(st["vt"]), stride,
                   P(pl), P(tr["n_nodes"]), P(tr["anc_bits"]), B, N, cfg.L_cap, cfg.Hq, cfg.Hkv,
-                  cfg.d_qk, cfg.d_v, tsv.TSV_BF16, ctypes.c_float(cfg.sm_scale), P(out), P(lse),
+                  cfg.d_qk, cfg.d_v, dt, ctypes.c_float(cfg.sm_scale), P(out), P(lse),
                   P(ws_a), ws_a.numel(), sp)
-        a_walk = (P(st["tl"]), tsv.TSV_BF16, B, N, cfg.V, cfg.gamma, P(tr["n_nodes"]),
+        a_walk = (P(st["tl"]), dt, B, N, cfg.V, cfg.gamma, P(tr["n_nodes"]),
                   P(tr["parent"]), P(tr["token"]), P(wk["accept_len"]), P(wk["accept_nodes"]),
                   P(wk["out_tokens"]), P(ws_w), ws_w.numel(), sp)
-        a_commit = (P(st["kc"]), P(st["vc"]), P(pl), P(st["kt"]), P(st["vt"]), stride,
-                    P(wk["accept_len"]), P(wk["accept_nodes"]), B, N, cfg.L_cap, cfg.Hkv,
-                    cfg.d_qk, cfg.d_v, cfg.gamma, tsv.TSV_BF16, P(status), sp)
+        # a latent cache commits its rows once (no separate value rows)
+        a_commit = (P(st["kc"]), None if cfg.mla else P(st["vc"]), P(pl), P(st["kt"]),
+                    None if cfg.mla else P(st["vt"]), stride, P(wk["accept_len"]),
+                    P(wk["accept_nodes"]), B, N, cfg.L_cap, cfg.Hkv, cfg.d_qk, cfg.d_v,
+                    cfg.gamma, dt, P(status), sp)
         return a_build, a_attn, a_walk, a_commit
 
     all_args = [step_args(s) for s in range(K + W)]
@@ -567,22 +586,12 @@ def main():
             e[4].record(stream)
         return rc
 
-    if args.attention_only:
-        if L.build_tree(*all_args[0][0]) != 0:   # the trees the attention reads
-            raise RuntimeError("build_tree failed")
-        for s in range(W + K):
-            if L.tree_verify_attn(*all_args[s][1]) != 0:
-                raise RuntimeError("tree_verify_attn failed")
-        torch.cuda.synchronize()
-        print(json.dumps({"attention_only_calls": W + K}), flush=True)
-        return
-
-    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: warmup {W} steps", file=sys.stderr, flush=True)
     for s in range(W):
         if run(s) != 0:
             raise RuntimeError("library call failed during warmup")
     torch.cuda.synchronize()
-    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: timing {K} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     rc = 0
     for s in range(W, W + K):
@@ -599,94 +608,315 @@ def main():
     # per-call durations of the other entry points: an untimed pass of a few
     # steps with an event between every call (the steps' inputs are reused;
     # their prefix-length copies are restored first)
-    P = list(range(W, W + min(K, 20)))
-    for s in P:
+    Pp = list(range(W, W + min(K, 20)))
+    for s in Pp:
         prefixes[s].copy_(prefix0)
     torch.cuda.synchronize()
-    for s in P:
+    for s in Pp:
         if run(s, all_events=True) != 0:
             raise RuntimeError("library call failed in the per-call timing pass")
     torch.cuda.synchronize()
-    t_build, t_walk, t_commit = ms(0, 1, P), ms(2, 3, P), ms(3, 4, P)
+    t_build, t_walk, t_commit = ms(0, 1, Pp), ms(2, 3, Pp), ms(3, 4, Pp)
     n_np = tr["n_nodes"].cpu().numpy()
-    prefix_np = prefix0.cpu().numpy()
+    if not np.array_equal(n_np, n0):
+        raise RuntimeError("the timed rounds built other trees than the workload's")
+    prefix_np = prefix0.cpu().numpy().astype(np.int64)
+    depth_np = tr["depth"].cpu().numpy()
     tokens = int(n_np.sum())
     accepted = int(wk["accept_len"].cpu().numpy().sum()) + B
-    value = tokens * K / wall
-    attn_bytes = attention_bytes(cfg, prefix_np, n_np)
     attn_s = float(np.mean(t_attn)) / 1e3
-    achieved = attn_bytes / attn_s / 1e9
+    res = dict(cfg=cfg, K=K, W=W, wall=wall, tokens=tokens, accepted=accepted,
+               value=tokens * K / wall, accepted_per_s=accepted * K / wall,
+               round_us=wall / K * 1e6, copies=copies,
+               kernel_ms={"build_tree": float(np.mean(t_build)),
+                          "tree_verify_attn": float(np.mean(t_attn)),
+                          "accept_walk": float(np.mean(t_walk)),
+                          "commit_path": float(np.mean(t_commit))},
+               attn_s=attn_s, attn_bytes=attention_bytes(cfg, prefix_np, n_np),
+               attn_flops=attention_flops(cfg, n_np, depth_np, prefix_np),
+               n=n_np, prefix=prefix_np, depth=depth_np)
+    res["sets0"] = sets[0]
+    res["marg0"] = marg0
+    return res
 
+
+def host_sample(res, reqs):
+    """Host copies of the inputs of requests `reqs` (first rotating copy)."""
+    cfg, st = res["cfg"], res["sets0"]
+    f32 = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+    lmax = int(res["prefix"][reqs].max()) + cfg.gamma
+    h = dict(marg=res["marg0"][reqs].cpu().numpy(), q=f32(st["q"][reqs]),
+             kc=f32(st["kc"][reqs, :lmax]), kt=f32(st["kt"][reqs]), tl=f32(st["tl"][reqs]))
+    h["vc"] = None if cfg.mla else f32(st["vc"][reqs, :lmax])
+    h["vt"] = None if cfg.mla else f32(st["vt"][reqs])
+    return h
+
+
+def oracle_round(cfg, h, prefix_np, n_gpu, depth_gpu, reqs, node_cap, threads):
+    """One round of the oracle over requests `reqs` of the workload (host
+    copies h), with attention on the first node_cap nodes of each, BLAS on
+    `threads` threads.  Every step is timed and scaled to the whole batch by
+    its own unit (marginal rows, requests, node x key pairs, verified rows,
+    requests); returns (tokens/s of the whole round, sample description)."""
+    import oracle
+    from oracle.attention import latent_as_heads
+    from threadpoolctl import threadpool_limits
+
+    r = len(reqs)
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        idx, p = oracle.topk_per_position(h["marg"], cfg.top_k)
+        t_topk = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        trees = [oracle.select_tree(idx[j], p[j], cfg.n_budget, cfg.N_max, cfg.cost,
+                                    int(prefix_np[b])) for j, b in enumerate(reqs)]
+        t_tree = time.perf_counter() - t0
+        if [t.n for t in trees] != [int(n_gpu[b]) for b in reqs]:
+            raise RuntimeError("oracle and GPU trees differ in size")
+        pairs_s = 0
+        t0 = time.perf_counter()
+        for j, b in enumerate(reqs):
+            t = trees[j]
+            lb = int(prefix_np[b])
+            nodes = list(range(min(t.n, node_cap)))
+            if not nodes:
+                continue
+            if cfg.mla:
+                Kc, Vc = latent_as_heads(h["kc"][j, :lb], cfg.d_v)
+                Kt, Vt = latent_as_heads(h["kt"][j], cfg.d_v)
+            else:
+                Kc, Vc, Kt, Vt = h["kc"][j, :lb], h["vc"][j, :lb], h["kt"][j], h["vt"][j]
+            oracle.attend_request(h["q"][j], Kc, Vc, Kt, Vt, lb, t.n, t.parent, cfg.sm_scale,
+                                  nodes=nodes)
+            pairs_s += sum(lb + int(t.depth[i]) for i in nodes)
+        t_attn = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        alen = np.zeros(r, np.int32)
+        anodes = np.full((r, cfg.gamma), -1, np.int32)
+        for j, t in enumerate(trees):
+            m, nodes, _ = oracle.accept_walk(h["tl"][j], t.n, t.parent, t.token, cfg.gamma)
+            alen[j], anodes[j] = m, nodes
+        t_walk = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        pl = prefix_np[reqs].copy()
+        oracle.commit_path(h["kc"], h["vc"], pl, h["kt"], h["vt"], alen, anodes, cfg.gamma)
+        t_commit = time.perf_counter() - t0
+    B = cfg.B
+    pairs_all = int(sum(int(n_gpu[b]) * int(prefix_np[b]) + int(depth_gpu[b, :n_gpu[b]].sum())
+                        for b in range(B)))
+    rows_s = sum(1 + t.n for t in trees)
+    rows_all = int(np.sum(1 + n_gpu))
+    est = (t_topk * B / r + t_tree * B / r
+           + (t_attn * pairs_all / pairs_s if pairs_s else 0.0)
+           + t_walk * rows_all / rows_s + t_commit * B / r)
+    spent = t_topk + t_tree + t_attn + t_walk + t_commit
+    desc = (f"top-k, tree, walk and commit of {r} of the {B} requests, attention of "
+            f"{'all' if node_cap >= cfg.N_max else f'at most {node_cap}'} nodes of each "
+            f"({pairs_s} node x key pairs of {pairs_all}); {spent:.1f} s measured, each step "
+            f"scaled to the batch by its unit (rows, requests, node x key pairs, verified rows)")
+    return int(n_gpu.sum()) / est, desc
+
+
+# per workload: requests the oracle runs and the attention nodes per request
+# (bounded so the sample costs seconds, not minutes), and timed steps
+CPU_SAMPLE = {1: ([0], 8), 2: (list(range(8)), 32), 3: ([0, 1], 4), 4: (None, 3), 5: ([0], 2)}
+PER_WORKLOAD_STEPS = {1: (50, 10), 2: (20, 5), 3: (10, 3), 4: (10, 3), 5: (5, 2)}
+
+
+def cpu_cores():
+    """Host cores the oracle may use: this process's affinity set, within the
+    thread count the environment grants (OMP_NUM_THREADS)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
+
+
+def cpu_baseline(res, cores, one_thread=True):
+    cfg = res["cfg"]
+    reqs, cap = CPU_SAMPLE[cfg.id]
+    if reqs is None:   # ragged: the first requests that verify a tree
+        reqs = [int(b) for b in np.nonzero(res["n"] > 0)[0][:2]]
+    h = host_sample(res, reqs)
+    value, desc = oracle_round(cfg, {k: (None if v is None else v.copy()) for k, v in h.items()},
+                               res["prefix"], res["n"], res["depth"], reqs, cap, cores)
+    out = {"value": round(value, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": desc}
+    if one_thread:
+        v1, _ = oracle_round(cfg, h, res["prefix"], res["n"], res["depth"], reqs, cap, 1)
+        out["value_1thread"] = round(v1, 2)
+    return out
+
+
+def attention_roofline(res, copy_gbs, gemm_tflops):
+    """Roofline of the attention launch: HBM for the grouped workloads, the
+    bf16 matrix peak for the latent ones; also against the measured peaks."""
+    cfg = res["cfg"]
+    t = res["attn_s"]
+    if cfg.mla:
+        a = res["attn_flops"] / t / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / MFMA_PEAK_TFLOPS, 4),
+                "measured_peak": round(gemm_tflops, 1),
+                "frac_of_measured": round(a / gemm_tflops, 4),
+                "algorithmic_flops": res["attn_flops"]}
+    a = res["attn_bytes"] / t / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "measured_peak": round(copy_gbs, 1),
+            "frac_of_measured": round(a / copy_gbs, 4), "algorithmic_bytes": res["attn_bytes"]}
+
+
+def workload_desc(cfg):
+    if cfg.mla:
+        heads = f"{cfg.Hq} heads x latent {cfg.d_qk}/{cfg.d_v}"
+    else:
+        heads = f"Hq {cfg.Hq} / Hkv {cfg.Hkv} x {cfg.d_qk}"
+    pre = (f"prefix {cfg.prefix_range[0]}-{cfg.prefix_range[1]}" if cfg.prefix_range
+           else f"prefix {cfg.prefix}")
+    bud = (f"adaptive budget (cap {cfg.n_budget})" if cfg.cost is not None
+           else f"fixed budget {cfg.n_budget}")
+    return (f"{cfg.name}: {cfg.B} requests, {heads}, {pre}, gamma {cfg.gamma}, V {cfg.V}, "
+            f"top-{cfg.top_k}, {bud}, {cfg.dtype}")
+
+
+def workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu):
+    cfg = res["cfg"]
+    e = {"workload": workload_desc(cfg), "steps": res["K"], "round_us": round(res["round_us"], 1),
+         "tokens_per_s": round(res["value"], 1),
+         "accepted_tokens_per_s": round(res["accepted_per_s"], 1),
+         "tree_tokens": res["tokens"], "input_copies": res["copies"],
+         "kernel_us": {k: round(v * 1e3, 1) for k, v in res["kernel_ms"].items()},
+         "attention": attention_roofline(res, copy_gbs, gemm_tflops)}
+    if with_cpu:
+        print(f"[bench] timing the CPU oracle on {cfg.name}", file=sys.stderr, flush=True)
+        e["cpu_baseline"] = cpu_baseline(res, cores)
+    return e
+
+
+def free(res):
+    for k in ("sets0", "marg0"):
+        res.pop(k, None)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=WORKLOAD, metavar="N",
+                    help="workload of the headline round (1..5 of workloads/gen.py)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-workload", action="store_true",
+                    help="time only the headline workload")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="run only the tree_verify_attn calls of the headline workload "
+                         "(for counter runs)")
+    ap.add_argument("--attention-workload", type=int, default=0, metavar="N",
+                    help="time only tree_verify_attn on workload N (implies --attention-only)")
+    ap.add_argument("--expand-workload", type=int, default=0, metavar="N",
+                    help="time only build_tree_expand on expansion workload N "
+                         "(101..104 of workloads/gen.py)")
+    ap.add_argument("--cpu-requests", type=int, default=4,
+                    help="requests of an expansion workload the CPU oracle runs")
+    ap.add_argument("--global-budget", action="store_true",
+                    help="time select_global_budget on the adaptive workload's trees")
+    ap.add_argument("--compressed-state", action="store_true",
+                    help="time compress_chains and refresh_compressed on the adaptive workload's trees")
+    ap.add_argument("--cost-profile", action="store_true",
+                    help="measure and fit the verification cost C_v(n; l) and test the "
+                         "adaptive budget's robustness to perturbed coefficients")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB three times between device buffers, so that "
+                         "byte counters can be scaled by a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        nb = args.copy_calibration << 20
+        bufs = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(6)]
+        for i in range(3):
+            bufs[2 * i + 1].copy_(bufs[2 * i])
+        torch.cuda.synchronize()
+        del bufs
+    if args.attention_only and not args.attention_workload:
+        args.attention_workload = args.workload
+    if args.attention_workload:
+        attention_only(args.attention_workload, args.steps, args.warmup, dev)
+        return
+    if args.cost_profile:
+        cost_profile(dev)
+        return
+    if args.global_budget:
+        global_budget_bench(dev, args.steps, args.warmup)
+        return
+    if args.compressed_state:
+        compressed_state_bench(dev, args.steps, args.warmup)
+        return
+    if args.expand_workload:
+        expand_only(args.expand_workload, args.steps, args.warmup, dev, args.cpu_requests)
+        return
+
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+    copy_gbs = copy_peak_gbs(dev)
+    gemm_tflops = gemm_peak_tflops(dev)
+    print(f"[bench] measured copy {copy_gbs:.0f} GB/s, bf16 GEMM {gemm_tflops:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    cores = cpu_cores()
+    with_cpu = not args.no_cpu_baseline
+
+    head = round_bench(args.workload, args.steps, args.warmup, dev)
+    cfg = head["cfg"]
+    roof = attention_roofline(head, copy_gbs, gemm_tflops)
+    roof["traffic"] = measured_traffic() if cfg.id == WORKLOAD else None
+    roof["kernel"] = "tree_verify_attn"
     line = {
         "metric": "verified tree tokens/s per GPU",
-        "value": round(value, 1),
+        "value": round(head["value"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(wall / K * 1e3, 4),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["wall"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": "gqa_bf16: 16 requests, Hq 32 / Hkv 8 x 128, prefix 4096, "
-                               "gamma 16, V 151936, top-32, fixed budget 32",
-                   "B": B, "gamma": cfg.gamma, "V": cfg.V, "top_k": cfg.top_k,
-                   "budget": cfg.n_budget, "prefix": cfg.prefix, "Hq": cfg.Hq,
-                   "Hkv": cfg.Hkv, "head_dim": cfg.d_qk},
-        "accepted_tokens_per_s": round(accepted * K / wall, 1),
-        "kernel_ms": {"build_tree": round(float(np.mean(t_build)), 4),
-                      "tree_verify_attn": round(float(np.mean(t_attn)), 4),
-                      "accept_walk": round(float(np.mean(t_walk)), 4),
-                      "commit_path": round(float(np.mean(t_commit)), 4)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "kernel": "tree_verify_attn",
-                     "algorithmic_bytes": attn_bytes},
+        "config": {"workload": workload_desc(cfg), "B": cfg.B, "gamma": cfg.gamma, "V": cfg.V,
+                   "top_k": cfg.top_k, "budget": cfg.n_budget, "prefix": cfg.prefix,
+                   "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": cfg.d_qk},
+        "accepted_tokens_per_s": round(head["accepted_per_s"], 1),
+        "kernel_ms": {k: round(v, 4) for k, v in head["kernel_ms"].items()},
+        "roofline": roof,
+        "measured_peaks": {"copy_gbs": round(copy_gbs, 1), "gemm_bf16_tflops": round(gemm_tflops, 1)},
     }
-
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = run_cpu_baseline(cfg, sets[0], marg0, prefix_np, n_np,
-                                                args.cpu_requests)
+    if with_cpu:
+        print(f"[bench] timing the CPU oracle on {cfg.name}", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(head, cores)
+    per = {}
+    if not args.no_per_workload:
+        per[cfg.name] = workload_entry(head, copy_gbs, gemm_tflops, cores, False)
+        if with_cpu:
+            per[cfg.name]["cpu_baseline"] = line["cpu_baseline"]
+    free(head)
+    if not args.no_per_workload:
+        for wid in (1, 2, 3, 4, 5):
+            if wid == cfg.id:
+                continue
+            K, W = PER_WORKLOAD_STEPS[wid]
+            res = round_bench(wid, K, W, dev)
+            per[res["cfg"].name] = workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu)
+            free(res)
+        line["per_workload"] = per
     print(json.dumps(line), flush=True)
-
-
-def run_cpu_baseline(cfg, st, marg_dev, prefix_np, n_gpu, n_req):
-    """One round of the oracle over the first n_req requests of the same
-    inputs (copied to the host before timing), single-threaded BLAS."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-
-    reqs = list(range(min(n_req, cfg.B)))
-    f32 = lambda t: (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
-    marg = marg_dev[reqs].cpu().numpy()
-    q, kc, vc = f32(st["q"][reqs]), f32(st["kc"][reqs]), f32(st["vc"][reqs])
-    kt, vt = f32(st["kt"][reqs]), f32(st["vt"][reqs])
-    tl = f32(st["tl"][reqs])
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        idx, p = oracle.topk_per_position(marg, cfg.top_k)
-        trees = [oracle.select_tree(idx[j], p[j], cfg.n_budget, cfg.N_max) for j in range(len(reqs))]
-        for j, t in enumerate(trees):
-            oracle.attend_request(q[j], kc[j], vc[j], kt[j], vt[j], int(prefix_np[j]), t.n,
-                                  t.parent, cfg.sm_scale)
-        alen = np.zeros(len(reqs), np.int32)
-        anodes = np.full((len(reqs), cfg.gamma), -1, np.int32)
-        for j, t in enumerate(trees):
-            m, nodes, _ = oracle.accept_walk(tl[j], t.n, t.parent, t.token, cfg.gamma)
-            alen[j], anodes[j] = m, nodes
-        pl = prefix_np[reqs].copy()
-        oracle.commit_path(kc, vc, pl, kt, vt, alen, anodes, cfg.gamma)
-        dt = time.perf_counter() - t0
-    tokens = sum(t.n for t in trees)
-    if [t.n for t in trees] != n_gpu[reqs].tolist():
-        raise RuntimeError("oracle and GPU trees differ in size")
-    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full round (top-k, tree, attention of all {tokens} nodes, walk, "
-                      f"commit) of {len(reqs)} of the {cfg.B} requests, {dt:.1f} s, "
-                      "numpy with BLAS limited to one thread"}
 
 
 if __name__ == "__main__":

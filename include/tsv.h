@@ -19,15 +19,15 @@
  * (unfold_chains, compress_chains and refresh_compressed keep a per-chain
  * compressed state beside the KV and commit the accepted chain's part),
  * and, once per deployment, tsv_fit_cost: measured latencies -> the cost
- * model build_tree's adaptive budget uses.
+ * model build_tree_fitted's adaptive budget uses.
  *
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer to a caller-owned, contiguous,
  *     row-major buffer, except `cost` (host).  The library never allocates,
  *     frees or synchronises, never reads device memory from the host and
  *     keeps no state between calls; calls are reentrant.
- *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
- *     stream) and returns before it runs.
+ *   - All work is enqueued on `s` (NULL = the default stream) and the call
+ *     returns before it runs.
  *   - Host-side argument checks fail with a negative status before anything is
  *     launched.  A failed launch returns TSV_EHIP.  Conditions only the device
  *     can see are reported per request through output arrays (commit_path's
@@ -38,12 +38,16 @@
  *   - Floating-point inputs must be finite (marginals also non-negative);
  *     results for NaN inputs are unspecified but memory-safe.
  *   - `ws` is device scratch of at least tsv_workspace_size(...) bytes, owned
- *     by the caller, 256-byte aligned.  For build_tree and accept_walk its
- *     contents on entry do not matter.  tree_verify_attn keeps arrival
- *     counters in it: that workspace must be all zero before its first use
- *     (e.g. one hipMemset at allocation), every call leaves the counters at
- *     zero again, and it must not be shared with the other entry points.
- *     Two calls that run concurrently need distinct workspaces.
+ *     by the caller, 256-byte aligned.  For the tree builders and
+ *     accept_walk its contents on entry do not matter.  tree_verify_attn
+ *     keeps arrival counters at the start of it (their number depends on B,
+ *     N_max, Hq and Hkv only): that workspace must be all zero before its
+ *     first call (e.g. one hipMemset at allocation) and again before the
+ *     first call after a call with another B, N_max, Hq or Hkv; every call
+ *     leaves the counters at zero, so calls at the same four sizes (any
+ *     dtype, head widths or L_cap) reuse it without clearing.  It must not
+ *     be shared with the other entry points.  Two calls that run
+ *     concurrently need distinct workspaces.
  *
  * Notation: B requests; gamma drafter positions (= maximum tree depth);
  * V vocabulary; k top-k branches per position; N_max node capacity
@@ -56,6 +60,8 @@
 #define TSV_H
 
 #include <stddef.h>
+
+#include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -71,16 +77,26 @@ enum {
   TSV_EHIP = -4          /* a kernel launch failed                           */
 };
 
-/* Round-cost coefficients ([caddtree] Methodology, item 1, with item 5's
- * convex, monotone verification cost):
- *   C(n; l) = c_d + C_v(n; l),  C_v(n; l) = a + b*n + c*n^2 + e*l*n + f*l.
- * The f*l term is the part of a request's verification that does not depend
- * on its tree size (reading its prefix once); f = 0 gives the plain family.
- * Requirements: a + c_d > 0 and b, c, e, f >= 0 (so C > 0, convex and
- * monotone in n). */
+/* Round-cost coefficients ([caddtree] Methodology, item 1: the round cost is
+ * the drafting cost plus a verification cost that grows with the tree size and
+ * the context length):
+ *   C(n; l) = c_d + C_v(n; l),  C_v(n; l) = a + b*n + c*n^2 + e*l*n.
+ * Requirements: a + c_d > 0 and b, c, e >= 0 (so C > 0, convex and monotone
+ * in n).  40 bytes, five doubles in this order. */
+typedef struct {
+  double a, b, c, e, c_d;
+} tsv_cost;
+
+/* The same family plus a term f*l that does not grow with the tree (reading
+ * the prefix once), as tsv_fit_cost returns it from measured latencies
+ * ([caddtree] Methodology, item 5: C_v is estimated once by convex regression
+ * over node counts and context lengths):
+ *   C_v(n; l) = a + b*n + c*n^2 + e*l*n + f*l,  f >= 0.
+ * The first five fields are tsv_cost's; f = 0 gives exactly tsv_cost's
+ * budgets. */
 typedef struct {
   double a, b, c, e, c_d, f;
-} tsv_cost;
+} tsv_cost_fitted;
 
 /*
  * build_tree -- per-position top-k, then the greedy best-first tree.
@@ -110,23 +126,63 @@ typedef struct {
  *   score       fp32  [B][N_max]  prefix probability
  *   anc_bits    uint32 [B][N_max][ceil(N_max/32)]  bit j of row i set iff node
  *               j is node i or one of its ancestors
- *   topk_idx    int32 [B][gamma][top_k] or NULL   the per-position top-k ids
- *   topk_p      fp32  [B][gamma][top_k] or NULL   and their probabilities
  *   Entries i >= n_nodes[b] are -1 (ints), 0.0f (score) and 0 (anc_bits).
+ * Workspace: tsv_workspace_size(0, B, gamma, V, top_k, N_max, ...) bytes,
+ * any contents (it holds the per-position top-k table between the two
+ * stages).
  * Order and ties
  *   top-k: probability descending, then token id ascending (-0 == +0).
  *   nodes: numbered in best-first order, i.e. ascending by the nested key
  *   (-score, depth, key(parent), rank), so parents precede children.
  *   Scores are fp32 products parent_score * q (root 1, round-to-nearest,
  *   never fused); Phi and C are fp64 in the order
- *   c_d + ((((a + b*n) + c*(n*n)) + (e*l)*n) + f*l); a node is added iff
+ *   c_d + (((a + b*n) + c*(n*n)) + (e*l)*n); a node is added iff
  *   (1 + Phi_{n+1}) / C(n+1) > (1 + Phi_n) / C(n).
  */
 int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
                int n_budget, const tsv_cost* cost, const int* prefix_len,
                int N_max, int* n_nodes, int* parent, int* token, int* depth,
-               float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
-               void* ws, size_t ws_bytes, void* stream);
+               float* score, unsigned* anc_bits, void* ws, size_t ws_bytes,
+               hipStream_t s);
+
+/*
+ * build_tree_topk -- build_tree that also returns the per-position top-k
+ * lists of its first stage, so that stage can be checked on its own.
+ *
+ * [caddtree] Methodology, item 2 and [review] "How it works", step 1: the
+ * top-k tokens of every drafter position are the branches a node at that
+ * depth may take.
+ *
+ * Arguments, results and errors are build_tree's, plus two outputs (device,
+ * both required):
+ *   topk_idx    int32 [B][gamma][top_k]  token ids, probability descending,
+ *               then token id ascending
+ *   topk_p      fp32  [B][gamma][top_k]  their probabilities (bit copies)
+ * Same workspace as build_tree; the tree outputs are bit-identical to
+ * build_tree's.
+ */
+int build_tree_topk(const float* marginals, int B, int gamma, int V, int top_k,
+                    int n_budget, const tsv_cost* cost, const int* prefix_len,
+                    int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                    float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
+                    void* ws, size_t ws_bytes, hipStream_t s);
+
+/*
+ * build_tree_fitted -- build_tree under a fitted cost model (the extra f*l
+ * term, tsv_cost_fitted).
+ *
+ * [caddtree] Methodology, item 5: the verification cost measured on the
+ * serving hardware and fitted by convex regression drives the same greedy
+ * stop.  Arguments, results, workspace and errors are build_tree's; `cost`
+ * (HOST, or NULL for the fixed budget) is a tsv_cost_fitted, and the stop
+ * rule evaluates C in the order c_d + ((((a + b*n) + c*(n*n)) + (e*l)*n) +
+ * f*l), so f = 0 reproduces build_tree bit for bit.
+ */
+int build_tree_fitted(const float* marginals, int B, int gamma, int V, int top_k,
+                      int n_budget, const tsv_cost_fitted* cost, const int* prefix_len,
+                      int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                      float* score, unsigned* anc_bits, void* ws, size_t ws_bytes,
+                      hipStream_t s);
 
 /*
  * build_tree_expand -- the same tree from per-node conditional expansion.
@@ -162,7 +218,7 @@ int build_tree_expand(const float* probs, int B, int steps, int V, int top_k,
                       int n_budget, const tsv_cost* cost, const int* prefix_len,
                       int N_max, int* n_nodes, int* parent, int* token, int* depth,
                       float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
-                      void* ws, size_t ws_bytes, void* stream);
+                      void* ws, size_t ws_bytes, hipStream_t s);
 
 /*
  * select_global_budget -- one verification budget for the whole batch.
@@ -195,7 +251,7 @@ int build_tree_expand(const float* probs, int B, int steps, int V, int top_k,
  */
 int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, float* score,
                          unsigned* anc_bits, int B, int N_max, const double* sps,
-                         long sps_len, void* stream);
+                         long sps_len, hipStream_t s);
 
 /*
  * unfold_chains -- a draft tree as its root-to-leaf chains.
@@ -217,7 +273,7 @@ int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, floa
  * chain_nodes int32 [B][N_max][gamma], node indices, -1 past each chain.
  */
 int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int gamma,
-                  int* n_chains, int* chain_len, int* chain_nodes, void* stream);
+                  int* n_chains, int* chain_len, int* chain_nodes, hipStream_t s);
 
 /*
  * compress_chains -- every chain's compressed state (verify preprocess).
@@ -253,7 +309,7 @@ int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int g
 int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
                     const float* tail, const int* prefix_len, const int* n_chains,
                     const int* chain_len, const int* chain_nodes, int B, int N_max,
-                    int gamma, float* entries, int* n_entries, void* stream);
+                    int gamma, float* entries, int* n_entries, hipStream_t s);
 
 /*
  * refresh_compressed -- commit the accepted chain's compressed state.
@@ -282,7 +338,7 @@ int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int
                        const int* prefix_len, const int* accept_len, const int* accept_nodes,
                        const int* n_chains, const int* chain_len, const int* chain_nodes,
                        const float* entries, int B, int N_max, int gamma, float* comp,
-                       int Lc_cap, float* tail, int* status, void* stream);
+                       int Lc_cap, float* tail, int* status, hipStream_t s);
 
 /*
  * tree_verify_attn -- branch-aware tree attention over a shared prefix.
@@ -311,7 +367,9 @@ int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int
  *   lse       fp32 [B][N_max][Hq] or NULL
  * Requirements: Hq % Hkv == 0; kv_row_stride >= Hkv*max(d_qk, d_v);
  * 1 <= d_qk, d_v <= 576; B <= 4096.  Accumulation is fp32.
- * Workspace: zero before the first call, see the conventions above.  The key
+ * Workspace: tsv_workspace_size(1, ...) bytes (enough for every path at
+ * these sizes), zero before the first call at these B, N_max, Hq, Hkv (see
+ * the conventions above).  The key
  * range of a (request, KV head, row block) may be split over several
  * workgroups whose partial results are combined in fp32 (for bf16 heads of
  * width 128 the partial rows are exchanged normalised and rounded to bf16),
@@ -324,7 +382,7 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const unsigned* anc_bits, int B, int N_max, int L_cap,
                      int Hq, int Hkv, int d_qk, int d_v, int dtype,
                      float sm_scale, void* out, float* lse, void* ws,
-                     size_t ws_bytes, void* stream);
+                     size_t ws_bytes, hipStream_t s);
 
 /*
  * accept_walk -- greedy acceptance of the longest matching path.
@@ -348,7 +406,7 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
 int accept_walk(const void* target_logits, int dtype, int B, int N_max, int V,
                 int gamma, const int* n_nodes, const int* parent,
                 const int* token, int* accept_len, int* accept_nodes,
-                int* out_tokens, void* ws, size_t ws_bytes, void* stream);
+                int* out_tokens, void* ws, size_t ws_bytes, hipStream_t s);
 
 /*
  * commit_path -- write the accepted chain into the persistent cache.
@@ -369,7 +427,7 @@ int commit_path(void* k_cache, void* v_cache, int* prefix_len,
                 const void* k_tree, const void* v_tree, long kv_row_stride,
                 const int* accept_len, const int* accept_nodes, int B,
                 int N_max, int L_cap, int Hkv, int d_k, int d_v, int gamma,
-                int dtype, int* status, void* stream);
+                int dtype, int* status, hipStream_t s);
 
 /*
  * tsv_fit_cost -- the convex, monotone verification cost from measured
@@ -388,7 +446,8 @@ int commit_path(void* k_cache, void* v_cache, int* prefix_len,
  * and measured verification latency of each point (finite, >= 0; t in any
  * time unit); 5 <= m <= 2^24; c_d the drafting cost in the same unit
  * (copied to out->c_d).
- * Output: *out (HOST) = {a, b, c, e, c_d, f}, ready for build_tree's `cost`.
+ * Output: *out (HOST) = {a, b, c, e, c_d, f}, ready for build_tree_fitted's
+ * `cost`.
  * When every point has one context length, e and f are not separable from
  * b and a; the optimum's value is still unique and the first optimal
  * support in the order (a, b, c, e, f) is returned.
@@ -397,7 +456,7 @@ int commit_path(void* k_cache, void* v_cache, int* prefix_len,
  * touches no device.
  */
 int tsv_fit_cost(const double* n, const double* l, const double* t, int m,
-                 double c_d, tsv_cost* out);
+                 double c_d, tsv_cost_fitted* out);
 
 /* Workspace bytes needed by entry point `which` (0 build_tree,
  * 1 tree_verify_attn, 2 accept_walk, 3 commit_path, 4 build_tree_expand,

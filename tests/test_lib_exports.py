@@ -21,7 +21,8 @@ def _declared():
 
 def test_all_declared_symbols_exported():
     names = _declared()
-    assert names == sorted(["build_tree", "build_tree_expand", "tree_verify_attn", "accept_walk",
+    assert names == sorted(["build_tree", "build_tree_topk", "build_tree_fitted",
+                            "build_tree_expand", "tree_verify_attn", "accept_walk",
                             "commit_path", "select_global_budget", "tsv_fit_cost",
                             "tsv_workspace_size", "tsv_status_string", "unfold_chains",
                             "compress_chains", "refresh_compressed"])
@@ -59,7 +60,7 @@ def test_host_validation_without_launch():
     nul = None
     # null pointers
     assert L.build_tree(nul, 1, 1, 1, 1, 1, None, nul, 1, nul, nul, nul, nul, nul, nul,
-                        nul, nul, nul, 0, nul) == -1
+                        nul, 0, nul) == -1
     assert L.tree_verify_attn(nul, nul, nul, nul, nul, 64, nul, nul, nul, 1, 1, 1, 1, 1, 64,
                               64, 0, 0.1, nul, nul, nul, 0, nul) == -1
     assert L.accept_walk(nul, 0, 1, 1, 1, 1, nul, nul, nul, nul, nul, nul, nul, 0, nul) == -1
@@ -68,10 +69,25 @@ def test_host_validation_without_launch():
     # non-null fake device addresses that are never dereferenced: argument
     # checks fail first, so nothing is launched
     p = ctypes.c_void_p(0x1000)
-    assert L.build_tree(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+    assert L.build_tree(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p, p,
                         1 << 20, nul) == -1                       # top_k > V
-    assert L.build_tree(p, 1, 2, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+    assert L.build_tree(p, 1, 2, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, p,
                         16, nul) == -3                            # workspace too small
+    cost = tsv.tsv_cost(1.0, 0.02, 1e-4, 1e-6, 0.5)
+    assert L.build_tree(p, 1, 2, 8, 2, 2, ctypes.byref(cost), nul, 4, p, p, p, p, p, p, p,
+                        1 << 20, nul) == -1                       # adaptive without prefix_len
+    bad = tsv.tsv_cost(1.0, -0.02, 1e-4, 1e-6, 0.5)
+    assert L.build_tree(p, 1, 2, 8, 2, 2, ctypes.byref(bad), p, 4, p, p, p, p, p, p, p,
+                        1 << 20, nul) == -1                       # negative coefficient
+    assert L.build_tree_topk(p, 1, 2, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, nul, nul, p,
+                             1 << 20, nul) == -1                  # top-k outputs are required
+    assert L.build_tree_topk(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p, p, p, p,
+                             1 << 20, nul) == -1                  # top_k > V
+    badf = tsv.tsv_cost_fitted(1.0, 0.02, 1e-4, 1e-6, 0.5, -1e-3)
+    assert L.build_tree_fitted(p, 1, 2, 8, 2, 2, ctypes.byref(badf), p, 4, p, p, p, p, p, p, p,
+                               1 << 20, nul) == -1                # negative f
+    assert L.build_tree_fitted(p, 1, 2, 8, 2, 2, None, nul, 4, p, p, p, p, p, p, p,
+                               16, nul) == -3                     # workspace too small
     assert L.tree_verify_attn(p, p, p, p, p, 64, p, p, p, 1, 4, 10, 4, 3, 64, 64, 1, 0.1,
                               p, nul, p, 1 << 30, nul) == -1      # Hq % Hkv
     assert L.tree_verify_attn(p, p, p, p, p, 10, p, p, p, 1, 4, 10, 4, 2, 64, 64, 1, 0.1,
@@ -113,6 +129,77 @@ def test_host_validation_without_launch():
                                 nul) == -1                                              # Lc_cap < 0
     assert L.refresh_compressed(p, 1, 64, 64, 4, p, p, p, p, p, p, p, 2, 8, 65, p, 8, p, p,
                                 nul) == -1                                              # gamma > 64
+
+
+# The four calls of a round and the cost struct, exactly as the boundary
+# fixes them (argument names, types and order), after comments are removed and
+# whitespace is collapsed.
+CONTRACT = [
+    "typedef struct { double a, b, c, e, c_d; } tsv_cost;",
+    "int build_tree(const float* marginals, int B, int gamma, int V, int top_k, int n_budget, "
+    "const tsv_cost* cost, const int* prefix_len, int N_max, int* n_nodes, int* parent, "
+    "int* token, int* depth, float* score, unsigned* anc_bits, void* ws, size_t ws_bytes, "
+    "hipStream_t s);",
+    "int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache, "
+    "const void* k_tree, const void* v_tree, long kv_row_stride, const int* prefix_len, "
+    "const int* n_nodes, const unsigned* anc_bits, int B, int N_max, int L_cap, int Hq, "
+    "int Hkv, int d_qk, int d_v, int dtype, float sm_scale, void* out, float* lse, void* ws, "
+    "size_t ws_bytes, hipStream_t s);",
+    "int accept_walk(const void* target_logits, int dtype, int B, int N_max, int V, int gamma, "
+    "const int* n_nodes, const int* parent, const int* token, int* accept_len, "
+    "int* accept_nodes, int* out_tokens, void* ws, size_t ws_bytes, hipStream_t s);",
+    "int commit_path(void* k_cache, void* v_cache, int* prefix_len, const void* k_tree, "
+    "const void* v_tree, long kv_row_stride, const int* accept_len, const int* accept_nodes, "
+    "int B, int N_max, int L_cap, int Hkv, int d_k, int d_v, int gamma, int dtype, "
+    "int* status, hipStream_t s);",
+    "size_t tsv_workspace_size(int which, int B, int gamma, int V, int top_k, int N_max, "
+    "int L_cap, int Hq, int Hkv, int d_qk, int d_v, int dtype);",
+    "const char* tsv_status_string(int code);",
+    "enum { TSV_F32 = 0, TSV_BF16 = 1 };",
+]
+
+
+def _flat_header():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"\s+", " ", text)
+    return re.sub(r"\s*([(),;{}])\s*", r"\1", text)
+
+
+def test_contract_prototypes_verbatim():
+    flat = _flat_header()
+    for decl in CONTRACT:
+        norm = re.sub(r"\s*([(),;{}])\s*", r"\1", re.sub(r"\s+", " ", decl))
+        assert norm in flat, decl
+    for code, name in ((0, "TSV_OK"), (-1, "TSV_EINVAL"), (-2, "TSV_EUNSUPPORTED"),
+                       (-3, "TSV_EWORKSPACE"), (-4, "TSV_EHIP")):
+        assert re.search(rf"{name}={code}\b", flat.replace(" ", "")), name
+
+
+def test_cost_struct_layout():
+    assert ctypes.sizeof(tsv.tsv_cost) == 40
+    assert [f for f, _ in tsv.tsv_cost._fields_] == ["a", "b", "c", "e", "c_d"]
+    assert ctypes.sizeof(tsv.tsv_cost_fitted) == 48
+    assert [f for f, _ in tsv.tsv_cost_fitted._fields_][:5] == ["a", "b", "c", "e", "c_d"]
+    # the C side agrees: a header-only check compiled with the host compiler
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = ('#include "tsv.h"\n#include <stddef.h>\n'
+           '_Static_assert(sizeof(tsv_cost) == 40, "tsv_cost");\n'
+           '_Static_assert(offsetof(tsv_cost, c_d) == 32, "c_d");\n'
+           '_Static_assert(sizeof(tsv_cost_fitted) == 48, "fitted");\n'
+           'int main(void) { return 0; }\n')
+    with tempfile.TemporaryDirectory() as d:
+        f = os.path.join(d, "c.c")
+        open(f, "w").write(src)
+        r = subprocess.run([cc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                            "-I", "/opt/rocm/include", "-fsyntax-only", f],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
 
 
 def test_binding_requires_device_tensors():

@@ -130,7 +130,36 @@ def test_sibling_isolation_and_determinism():
                 assert not torch.equal(o4[b, i], o1[b, i])
 
 
-SAMPLES = {2: 48, 3: 12, 4: 40, 5: 8}
+def _structured_samples(cid, trees, rng):
+    """Nodes checked at full size: for the latent workloads (one row block of
+    128 rows per node) every node of the first and last request plus one node
+    of every other request (3), or the first and last node of every request
+    (5, about a second of oracle time per node); for the grouped workloads
+    (a row block holds 32 nodes x 4 heads) one node of every request that
+    verifies a tree, its last node for the longest request, and a random
+    sample of the rest (2, 4)."""
+    B = len(trees)
+    picks = set()
+    if cid == 3:
+        for b in (0, B - 1):
+            picks.update((b, i) for i in range(trees[b].n))
+        for b in range(1, B - 1):
+            if trees[b].n:
+                picks.add((b, int(rng.integers(trees[b].n))))
+    elif cid == 5:
+        for b in range(B):
+            if trees[b].n:
+                picks.update({(b, 0), (b, trees[b].n - 1)})
+    else:
+        for b in range(B):
+            if trees[b].n:
+                picks.add((b, int(rng.integers(trees[b].n))))
+        bl = int(np.argmax([t.n for t in trees]))
+        picks.add((bl, trees[bl].n - 1))
+        pairs = [(b, i) for b in range(B) for i in range(trees[b].n)]
+        extra = rng.choice(len(pairs), size=min(32, len(pairs)), replace=False)
+        picks.update(pairs[j] for j in extra)
+    return sorted(picks)
 
 
 def test_workspace_reuse_and_counter_reset():
@@ -175,19 +204,13 @@ def test_workload(cid):
     _, _, trees = oracle_trees(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cfg.cost, pl_np)
     o, lse, _, _ = _run(ins["q"], ins["k_cache"], ins["v_cache"], ins["k_tree"], ins["v_tree"],
                         ins["prefix_len"], trees, cfg.Hkv, cfg.d_v, cfg.sm_scale)
-    samples = None
-    if cid in SAMPLES:
-        rng = np.random.default_rng(cid)
-        pairs = [(b, i) for b in range(cfg.B) for i in range(trees[b].n)]
-        pick = rng.choice(len(pairs), size=min(SAMPLES[cid], len(pairs)), replace=False)
-        samples = sorted(pairs[j] for j in pick)
-        # always include the last node of the longest request
-        bl = int(np.argmax([t.n for t in trees]))
-        samples.append((bl, trees[bl].n - 1))
+    samples = None if cid == 1 else _structured_samples(cid, trees, np.random.default_rng(cid))
     worst = check_attention(o, lse, ins["q"], ins["k_cache"], ins["v_cache"], ins["k_tree"],
                             ins["v_tree"], pl_np, trees, cfg.sm_scale, TOL[cfg.torch_dtype],
                             cfg.mla, cfg.d_v, samples)
-    print(f"workload {cid}: max |gpu - oracle| = {worst:.3e}", flush=True)
+    checked = sum(t.n for t in trees) if samples is None else len(samples)
+    print(f"MARGIN workload {cid} {cfg.name}: max |gpu - oracle| = {worst:.3e} over {checked} "
+          f"nodes (tolerance {TOL[cfg.torch_dtype]:g})", flush=True)
 
 
 def test_invalid_arguments():
@@ -235,3 +258,89 @@ def test_wide_heads_value_cache_of_its_own():
     assert rc == 0
     check_attention(out, lse, q, kc.unsqueeze(2), vc[..., :dv].unsqueeze(2), kt.unsqueeze(2),
                     vt[..., :dv].unsqueeze(2), prefix, trees, scale, TOL[torch.bfloat16], False, dv)
+
+
+def test_split_handoff_many_splits_sentinel():
+    """One unit whose 160000 keys are cut into 500 splits of 320 keys: the
+    last split to arrive combines every other split's published rows.  The
+    outputs are filled with NaN before each of four launches; every row of
+    every node must be written, bit-equal across launches, and within
+    tolerance of the oracle on a sample of nodes."""
+    rng = np.random.default_rng(17)
+    B, N_max, Hq, Hkv, d = 1, 32, 4, 1, 128
+    prefix = [160000]
+    L_cap = prefix[0] + 16
+    q, kc, vc, kt, vt, pl = _inputs(rng, B, N_max, L_cap, Hq, Hkv, d, d, torch.bfloat16, prefix)
+    trees = _random_trees(rng, B, N_max, [32])
+    n = torch.tensor([32], dtype=torch.int32, device=DEV)
+    anc = torch.from_numpy(np.stack([t.anc_bits for t in trees]).view(np.int32)).to(DEV)
+    # splits of the grouped kernel: one unit (capacity L_cap + N_max keys,
+    # about 512 workgroups aimed for, at least 256 keys and at most 4096 keys
+    # per split of the capacity), whose 160032 actual keys are cut into S
+    # chunks rounded up to 32 keys
+    cdiv = lambda x, y: -(-x // y)
+    keys_max = L_cap + N_max
+    cap_chunk = cdiv(max(256, cdiv(keys_max, 512)), 32) * 32
+    S = max(cdiv(keys_max, cap_chunk), cdiv(keys_max, 4096))
+    keys = prefix[0] + 32
+    chunk = max(cdiv(cdiv(keys, S), 32) * 32, 256)
+    splits = cdiv(keys, chunk)
+    assert splits > 300, splits
+    ws = tsv.workspace(tsv.workspace_size(1, B, 1, 1, 1, N_max, L_cap, Hq, Hkv, d, d,
+                                          tsv.TSV_BF16), DEV)
+    first = None
+    for launch in range(4):
+        out = torch.full((B, N_max, Hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((B, N_max, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        tsv.tree_verify_attn(q, kc, vc, kt, vt, pl, n, anc, Hkv, d, 0.0884, out=out, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any(), launch
+        assert not torch.isnan(lse).any(), launch
+        bits = (out.view(torch.int16).clone(), lse.view(torch.int32).clone())
+        if first is None:
+            first = bits
+        else:
+            assert torch.equal(bits[0], first[0]) and torch.equal(bits[1], first[1]), launch
+    check_attention(out, lse, q, kc, vc, kt, vt, prefix, trees, 0.0884, TOL[torch.bfloat16],
+                    False, d, [(0, i) for i in (0, 7, 19, 31)])
+
+
+def test_workspace_reuse_across_dtype_and_shapes():
+    """One workspace (zeroed once, sized for the largest call) serves fp32
+    and bf16 calls and other prefix capacities at the same B, N_max, Hq, Hkv
+    without clearing; after a call at another B it is zeroed again, as the
+    header requires.  Outputs are NaN-filled before every call, and every
+    row of every node must be written and match the oracle."""
+    rng = np.random.default_rng(23)
+    N_max, Hq, Hkv, d = 32, 16, 4, 128
+
+    def call(B, prefix, dtype, L_cap, ws):
+        q, kc, vc, kt, vt, pl = _inputs(rng, B, N_max, L_cap, Hq, Hkv, d, d, dtype, prefix)
+        trees = _random_trees(rng, B, N_max, [int(rng.integers(1, N_max + 1)) for _ in range(B)])
+        n = torch.tensor([t.n for t in trees], dtype=torch.int32, device=DEV)
+        anc = torch.from_numpy(np.stack([t.anc_bits for t in trees]).view(np.int32)).to(DEV)
+        out = torch.full((B, N_max, Hq, d), float("nan"), dtype=dtype, device=DEV)
+        lse = torch.full((B, N_max, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        tsv.tree_verify_attn(q, kc, vc, kt, vt, pl, n, anc, Hkv, d, 0.0884, out=out, lse=lse, ws=ws)
+        torch.cuda.synchronize()
+        for b, t in enumerate(trees):
+            assert not torch.isnan(out[b, :t.n]).any(), (B, dtype, b)
+            assert not torch.isnan(lse[b, :t.n]).any(), (B, dtype, b)
+        check_attention(out, lse, q, kc, vc, kt, vt, prefix, trees, 0.0884, TOL[dtype], False, d,
+                        [(b, t.n - 1) for b, t in enumerate(trees)])
+
+    need = max(tsv.workspace_size(1, B, 1, 1, 1, N_max, 9000, Hq, Hkv, d, d, dt)
+               for B in (2, 3) for dt in (tsv.TSV_F32, tsv.TSV_BF16))
+    ws = tsv.workspace(need, DEV)
+    # same B, N_max, Hq, Hkv: dtype, path and capacity change freely
+    call(2, [700, 5000], torch.float32, 5016, ws)
+    call(2, [4000, 9000 - 16], torch.bfloat16, 9000, ws)
+    call(2, [300, 2000], torch.float32, 2016, ws)
+    call(2, [2500, 60], torch.bfloat16, 2516, ws)
+    # another B: zero the workspace first
+    ws.zero_()
+    call(3, [5000, 128, 3000], torch.bfloat16, 5016, ws)
+    call(3, [900, 4000, 33], torch.float32, 4016, ws)
+    call(3, [6000, 10, 2222], torch.bfloat16, 6016, ws)
+    ws.zero_()
+    call(2, [1234, 4321], torch.bfloat16, 4337, ws)

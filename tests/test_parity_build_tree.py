@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def _run(marg_np, top_k, n_budget, N_max, cost=None, prefix=None):
     m = torch.from_numpy(np.ascontiguousarray(marg_np, dtype=np.float32)).to(DEV)
     pl = None if prefix is None else torch.from_numpy(np.asarray(prefix, np.int32)).to(DEV)
-    g = tsv.build_tree(m, top_k, n_budget, N_max, cost=cost, prefix_len=pl, with_topk=True)
+    g = tsv.build_tree_topk(m, top_k, n_budget, N_max, cost=cost, prefix_len=pl)
     torch.cuda.synchronize()
     idx, p, trees = oracle_trees(marg_np, top_k, n_budget, N_max, cost, prefix)
     assert_tree_equal(g, idx, p, trees)
@@ -114,3 +114,43 @@ def test_invalid_arguments_return_status():
     with pytest.raises(tsv.TsvError) as e:
         tsv.build_tree(m, 2, 2, 4, ws=ws)
     assert e.value.code == -3
+
+
+@pytest.mark.parametrize("adaptive", [False, True])
+def test_contract_call_matches_variants(adaptive):
+    """build_tree called with the boundary's exact argument list (18 arguments,
+    the 40-byte cost struct) gives the oracle's trees, bit-identical to
+    build_tree_topk and to build_tree_fitted with f = 0."""
+    import ctypes
+    rng = np.random.default_rng(31)
+    B, gamma, V, top_k, cap, N_max = 5, 9, 4000, 24, 48, 64
+    lg = rng.normal(0, 2, size=(B, gamma, V)) / rng.uniform(0.4, 1.5, size=(B, 1, 1))
+    marg = np.exp(lg - lg.max(-1, keepdims=True))
+    marg = (marg / marg.sum(-1, keepdims=True)).astype(np.float32)
+    prefix = rng.integers(1000, 30000, size=B).astype(np.int32)
+    cost = Cost(a=1.0, b=0.02, c=1e-4, e=1e-6, c_d=0.5) if adaptive else None
+    m = torch.from_numpy(marg).to(DEV)
+    pl = torch.from_numpy(prefix).to(DEV)
+    L = tsv.lib()
+    outs = tsv._lib._tree_outputs(B, N_max, m.device)
+    for t in outs.values():
+        t.fill_(0x5A)                          # every element must be overwritten
+    ws = tsv.workspace(tsv.workspace_size(tsv._lib.WS_BUILD, B, gamma, V, top_k, N_max), DEV)
+    c = tsv.tsv_cost(cost.a, cost.b, cost.c, cost.e, cost.c_d) if adaptive else None
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = L.build_tree(P(m), B, gamma, V, top_k, cap, ctypes.byref(c) if adaptive else None,
+                      P(pl) if adaptive else None, N_max, P(outs["n_nodes"]), P(outs["parent"]),
+                      P(outs["token"]), P(outs["depth"]), P(outs["score"]), P(outs["anc_bits"]),
+                      P(ws), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    g_topk = tsv.build_tree_topk(m, top_k, cap, N_max, cost=cost, prefix_len=pl if adaptive else None)
+    fitted = None if cost is None else dataclasses.replace(cost, f=0.0)
+    g_fit = tsv.build_tree_fitted(m, top_k, cap, N_max, cost=fitted,
+                                  prefix_len=pl if adaptive else None)
+    torch.cuda.synchronize()
+    idx, p, trees = oracle_trees(marg, top_k, cap, N_max, cost, prefix if adaptive else None)
+    assert_tree_equal(g_topk, idx, p, trees)
+    assert_tree_equal(outs, idx, p, trees, check_topk=False)
+    for k in outs:
+        assert torch.equal(outs[k], g_topk[k]), k
+        assert torch.equal(outs[k], g_fit[k]), k

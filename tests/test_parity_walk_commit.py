@@ -153,8 +153,8 @@ def test_chained_round(cid):
     marg = marginals(cfg, 0, DEV)
     ins = attention_inputs(cfg, 0, DEV)
     pl_np = ins["prefix_len"].cpu().numpy().copy()
-    g = tsv.build_tree(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=cfg.cost,
-                       prefix_len=ins["prefix_len"] if cfg.cost else None, with_topk=True)
+    g = tsv.build_tree_topk(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=cfg.cost,
+                            prefix_len=ins["prefix_len"] if cfg.cost else None)
     out, lse = tsv.tree_verify_attn(ins["q"], ins["k_cache"], ins["v_cache"], ins["k_tree"],
                                     ins["v_tree"], ins["prefix_len"], g["n_nodes"],
                                     g["anc_bits"], cfg.Hkv, cfg.d_v, cfg.sm_scale)
@@ -176,8 +176,12 @@ def test_chained_round(cid):
     alen = w["accept_len"].cpu().numpy()
     anodes = w["accept_nodes"].cpu().numpy()
     kt_np = np32(ins["k_tree"])
+    vt_np = None if cfg.mla else np32(ins["v_tree"])
     before = {b: np32(ins["k_cache"][b, max(0, pl_np[b] - 2): pl_np[b] + cfg.gamma + 2]).copy()
               for b in range(cfg.B)}
+    before_v = {} if cfg.mla else {
+        b: np32(ins["v_cache"][b, max(0, pl_np[b] - 2): pl_np[b] + cfg.gamma + 2]).copy()
+        for b in range(cfg.B)}
     vc = None if cfg.mla else ins["v_cache"]
     vt = None if cfg.mla else ins["v_tree"]
     status = tsv.commit_path(ins["k_cache"], vc, ins["prefix_len"], ins["k_tree"], vt,
@@ -192,6 +196,12 @@ def test_chained_round(cid):
         for j in range(alen[b]):
             want[pl_np[b] - lo + j] = kt_np[b, anodes[b, j]]
         assert np.array_equal(after, want), b
+        if not cfg.mla:
+            after_v = np32(ins["v_cache"][b, lo: pl_np[b] + cfg.gamma + 2])
+            want_v = before_v[b].copy()
+            for j in range(alen[b]):
+                want_v[pl_np[b] - lo + j] = vt_np[b, anodes[b, j]]
+            assert np.array_equal(after_v, want_v), b
     print(f"workload {cid}: accepted {int(alen.sum())} tokens + {cfg.B} bonus over "
           f"{int(st['n_nodes'].sum())} tree nodes", flush=True)
 

@@ -1,7 +1,8 @@
 """Tree-structured speculative verification on AMD Instinct MI355X (gfx950).
 
 One verification round = four calls into the HIP library libtsv.so
-(include/tsv.h): build_tree (or build_tree_expand), tree_verify_attn,
+(include/tsv.h): build_tree (or build_tree_topk / build_tree_fitted /
+build_tree_expand), tree_verify_attn,
 accept_walk, commit_path.
 This package is the thin Python binding over that C ABI.
 """
@@ -13,6 +14,8 @@ from ._lib import (  # noqa: F401
     accept_walk,
     build_tree,
     build_tree_expand,
+    build_tree_fitted,
+    build_tree_topk,
     expanded_rows,
     fit_cost,
     commit_path,
@@ -21,6 +24,8 @@ from ._lib import (  # noqa: F401
     refresh_compressed,
     select_global_budget,
     status_string,
+    tsv_cost,
+    tsv_cost_fitted,
     tree_verify_attn,
     unfold_chains,
     workspace,

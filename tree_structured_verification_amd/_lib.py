@@ -30,6 +30,13 @@ class TsvError(RuntimeError):
 
 
 class tsv_cost(ctypes.Structure):
+    """C_v(n; l) = a + b n + c n^2 + e l n, and c_d (40 bytes)."""
+    _fields_ = [("a", ctypes.c_double), ("b", ctypes.c_double), ("c", ctypes.c_double),
+                ("e", ctypes.c_double), ("c_d", ctypes.c_double)]
+
+
+class tsv_cost_fitted(ctypes.Structure):
+    """tsv_cost's fields plus the fitted f l term (48 bytes)."""
     _fields_ = [("a", ctypes.c_double), ("b", ctypes.c_double), ("c", ctypes.c_double),
                 ("e", ctypes.c_double), ("c_d", ctypes.c_double), ("f", ctypes.c_double)]
 
@@ -42,7 +49,11 @@ _F = ctypes.c_float
 
 _SIGS = {
     "build_tree": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
-                   _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+                   _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "build_tree_topk": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
+                        _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "build_tree_fitted": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost_fitted), _P, _I,
+                          _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "build_tree_expand": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "tree_verify_attn": [_P, _P, _P, _P, _P, _L, _P, _P, _P, _I, _I, _I, _I, _I,
@@ -52,7 +63,7 @@ _SIGS = {
                     _I, _P, _P],
     "tsv_fit_cost": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                      ctypes.POINTER(ctypes.c_double), _I, ctypes.c_double,
-                     ctypes.POINTER(tsv_cost)],
+                     ctypes.POINTER(tsv_cost_fitted)],
     "select_global_budget": [_P, _P, _P, _P, _P, _P, _I, _I, _P, _L, _P],
     "unfold_chains": [_P, _P, _I, _I, _I, _P, _P, _P, _P],
     "compress_chains": [_P, _I, _L, _L, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P],
@@ -131,44 +142,93 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def _cost_struct(cost):
+    """The plain 5-field cost of build_tree; a model with a non-zero f term
+    belongs to build_tree_fitted."""
     if cost is None:
         return None
+    if float(getattr(cost, "f", 0.0)) != 0.0:
+        raise ValueError("this cost model has an f*l term: use build_tree_fitted")
     return ctypes.byref(tsv_cost(float(cost.a), float(cost.b), float(cost.c),
-                                 float(cost.e), float(cost.c_d), float(getattr(cost, "f", 0.0))))
+                                 float(cost.e), float(cost.c_d)))
 
 
-def build_tree(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: int,
-               cost=None, prefix_len: Optional[torch.Tensor] = None,
-               with_topk: bool = False, out: Optional[dict] = None,
-               ws: Optional[torch.Tensor] = None) -> dict:
-    """marginals fp32 [B, gamma, V]; cost: object with a, b, c, e, c_d or None."""
+def _fitted_struct(cost):
+    if cost is None:
+        return None
+    return ctypes.byref(tsv_cost_fitted(float(cost.a), float(cost.b), float(cost.c),
+                                        float(cost.e), float(cost.c_d),
+                                        float(getattr(cost, "f", 0.0))))
+
+
+def _tree_outputs(B: int, N_max: int, dev) -> dict:
+    W = (N_max + 31) // 32
+    return dict(
+        n_nodes=torch.empty(B, dtype=torch.int32, device=dev),
+        parent=torch.empty(B, N_max, dtype=torch.int32, device=dev),
+        token=torch.empty(B, N_max, dtype=torch.int32, device=dev),
+        depth=torch.empty(B, N_max, dtype=torch.int32, device=dev),
+        score=torch.empty(B, N_max, dtype=torch.float32, device=dev),
+        anc_bits=torch.empty(B, N_max, W, dtype=torch.int32, device=dev),
+    )
+
+
+def _build_common(marginals, top_k, N_max, prefix_len, out, ws):
     _dev(marginals, "marginals", torch.float32)
     B, gamma, V = marginals.shape
     dev = marginals.device
-    W = (N_max + 31) // 32
     if out is None:
-        out = dict(
-            n_nodes=torch.empty(B, dtype=torch.int32, device=dev),
-            parent=torch.empty(B, N_max, dtype=torch.int32, device=dev),
-            token=torch.empty(B, N_max, dtype=torch.int32, device=dev),
-            depth=torch.empty(B, N_max, dtype=torch.int32, device=dev),
-            score=torch.empty(B, N_max, dtype=torch.float32, device=dev),
-            anc_bits=torch.empty(B, N_max, W, dtype=torch.int32, device=dev),
-        )
-        if with_topk:
-            out["topk_idx"] = torch.empty(B, gamma, top_k, dtype=torch.int32, device=dev)
-            out["topk_p"] = torch.empty(B, gamma, top_k, dtype=torch.float32, device=dev)
+        out = _tree_outputs(B, N_max, dev)
     if prefix_len is not None:
         _dev(prefix_len, "prefix_len", torch.int32)
     if ws is None:
         ws = workspace(workspace_size(WS_BUILD, B, gamma, V, top_k, N_max), dev)
+    return B, gamma, V, dev, out, ws
+
+
+def _tree_ptrs(out):
+    return (_ptr(out["n_nodes"]), _ptr(out["parent"]), _ptr(out["token"]), _ptr(out["depth"]),
+            _ptr(out["score"]), _ptr(out["anc_bits"]))
+
+
+def build_tree(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: int,
+               cost=None, prefix_len: Optional[torch.Tensor] = None,
+               out: Optional[dict] = None, ws: Optional[torch.Tensor] = None) -> dict:
+    """marginals fp32 [B, gamma, V]; cost: object with a, b, c, e, c_d (and
+    f == 0 if present) or None for the fixed budget."""
+    B, gamma, V, dev, out, ws = _build_common(marginals, top_k, N_max, prefix_len, out, ws)
     code = lib().build_tree(
         _ptr(marginals), B, gamma, V, top_k, n_budget, _cost_struct(cost),
-        _ptr(prefix_len), N_max, _ptr(out["n_nodes"]), _ptr(out["parent"]),
-        _ptr(out["token"]), _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc_bits"]),
-        _ptr(out.get("topk_idx")), _ptr(out.get("topk_p")), _ptr(ws), ws.numel(),
-        _stream(dev))
+        _ptr(prefix_len), N_max, *_tree_ptrs(out), _ptr(ws), ws.numel(), _stream(dev))
     _check("build_tree", code)
+    return out
+
+
+def build_tree_topk(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: int,
+                    cost=None, prefix_len: Optional[torch.Tensor] = None,
+                    out: Optional[dict] = None, ws: Optional[torch.Tensor] = None) -> dict:
+    """build_tree plus the per-position top-k lists (out["topk_idx"] int32,
+    out["topk_p"] fp32, both [B, gamma, top_k])."""
+    B, gamma, V, dev, out, ws = _build_common(marginals, top_k, N_max, prefix_len, out, ws)
+    if "topk_idx" not in out:
+        out["topk_idx"] = torch.empty(B, gamma, top_k, dtype=torch.int32, device=dev)
+        out["topk_p"] = torch.empty(B, gamma, top_k, dtype=torch.float32, device=dev)
+    code = lib().build_tree_topk(
+        _ptr(marginals), B, gamma, V, top_k, n_budget, _cost_struct(cost),
+        _ptr(prefix_len), N_max, *_tree_ptrs(out), _ptr(out["topk_idx"]), _ptr(out["topk_p"]),
+        _ptr(ws), ws.numel(), _stream(dev))
+    _check("build_tree_topk", code)
+    return out
+
+
+def build_tree_fitted(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: int,
+                      cost=None, prefix_len: Optional[torch.Tensor] = None,
+                      out: Optional[dict] = None, ws: Optional[torch.Tensor] = None) -> dict:
+    """build_tree under the fitted cost family (a, b, c, e, c_d, f)."""
+    B, gamma, V, dev, out, ws = _build_common(marginals, top_k, N_max, prefix_len, out, ws)
+    code = lib().build_tree_fitted(
+        _ptr(marginals), B, gamma, V, top_k, n_budget, _fitted_struct(cost),
+        _ptr(prefix_len), N_max, *_tree_ptrs(out), _ptr(ws), ws.numel(), _stream(dev))
+    _check("build_tree_fitted", code)
     return out
 
 
@@ -189,16 +249,8 @@ def build_tree_expand(probs: torch.Tensor, steps: int, top_k: int, n_budget: int
         raise ValueError(f"probs has {P} rows per request, {steps} steps of top-{top_k} "
                          f"need {expanded_rows(steps, top_k)}")
     dev = probs.device
-    W = (N_max + 31) // 32
     if out is None:
-        out = dict(
-            n_nodes=torch.empty(B, dtype=torch.int32, device=dev),
-            parent=torch.empty(B, N_max, dtype=torch.int32, device=dev),
-            token=torch.empty(B, N_max, dtype=torch.int32, device=dev),
-            depth=torch.empty(B, N_max, dtype=torch.int32, device=dev),
-            score=torch.empty(B, N_max, dtype=torch.float32, device=dev),
-            anc_bits=torch.empty(B, N_max, W, dtype=torch.int32, device=dev),
-        )
+        out = _tree_outputs(B, N_max, dev)
         if with_topk:
             out["topk_idx"] = torch.empty(B, P, top_k, dtype=torch.int32, device=dev)
             out["topk_p"] = torch.empty(B, P, top_k, dtype=torch.float32, device=dev)
@@ -208,18 +260,17 @@ def build_tree_expand(probs: torch.Tensor, steps: int, top_k: int, n_budget: int
         ws = workspace(workspace_size(WS_EXPAND, B, steps, V, top_k, N_max), dev)
     code = lib().build_tree_expand(
         _ptr(probs), B, steps, V, top_k, n_budget, _cost_struct(cost),
-        _ptr(prefix_len), N_max, _ptr(out["n_nodes"]), _ptr(out["parent"]),
-        _ptr(out["token"]), _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["anc_bits"]),
+        _ptr(prefix_len), N_max, *_tree_ptrs(out),
         _ptr(out.get("topk_idx")), _ptr(out.get("topk_p")), _ptr(ws), ws.numel(),
         _stream(dev))
     _check("build_tree_expand", code)
     return out
 
 
-def fit_cost(n, l, t, c_d: float = 0.0) -> tsv_cost:
+def fit_cost(n, l, t, c_d: float = 0.0) -> tsv_cost_fitted:
     """Non-negative least-squares fit of C_v(n; l) = a + b n + c n^2 + e l n + f l to
-    measured latencies t at (n, l) (host sequences); returns the tsv_cost
-    struct (with c_d) for build_tree's adaptive budget."""
+    measured latencies t at (n, l) (host sequences); returns the
+    tsv_cost_fitted struct (with c_d) for build_tree_fitted's adaptive budget."""
     import numpy as np
     n = np.ascontiguousarray(n, dtype=np.float64)
     l = np.ascontiguousarray(l, dtype=np.float64)
@@ -227,7 +278,7 @@ def fit_cost(n, l, t, c_d: float = 0.0) -> tsv_cost:
     if not (n.shape == l.shape == t.shape) or n.ndim != 1:
         raise ValueError("n, l and t must be 1-D sequences of one length")
     dp = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
-    out = tsv_cost()
+    out = tsv_cost_fitted()
     code = lib().tsv_fit_cost(dp(n), dp(l), dp(t), int(n.size), float(c_d), ctypes.byref(out))
     _check("tsv_fit_cost", code)
     return out

@@ -81,24 +81,28 @@ bool expand_sizes_ok(int B, int steps, int V, int top_k, int N_max) {
   return true;
 }
 
-bool cost_ok(const tsv_cost* cost) {
+bool cost_ok(const tsv_cost_fitted* cost) {
   return isfinite(cost->a) && isfinite(cost->c_d) && cost->a + cost->c_d > 0.0 &&
          finite_nonneg(cost->b) && finite_nonneg(cost->c) && finite_nonneg(cost->e) &&
          finite_nonneg(cost->f);
 }
 
+// The plain family as the fitted one with f = 0: the stop rule appends + f*l
+// last, and v + 0.0 == v for the positive v it is added to, so the budgets
+// are bit-identical.
+tsv_cost_fitted widen(const tsv_cost& c) { return tsv_cost_fitted{c.a, c.b, c.c, c.e, c.c_d, 0.0}; }
+
 // top-k of every list, then the best-first tree; shared by both builders
 int launch_build(const float* probs, int B, int rows_per_b, int steps, int V, int top_k,
-                 int n_budget, const tsv_cost* cost, const int* prefix_len, int N_max,
+                 int n_budget, const tsv_cost_fitted* cost, const int* prefix_len, int N_max,
                  int* n_nodes, int* parent, int* token, int* depth, float* score,
                  unsigned* anc_bits, int* topk_idx, float* topk_p, void* ws,
-                 size_t ws_bytes, void* stream, bool per_node) {
+                 size_t ws_bytes, hipStream_t s, bool per_node) {
   const BuildLayout L = build_layout(B, rows_per_b, V, top_k);
   if (!ws || ws_bytes < L.bytes || !aligned_to(ws, kAlign)) return TSV_EWORKSPACE;
   char* w = static_cast<char*>(ws);
   int* tk_idx = topk_idx ? topk_idx : reinterpret_cast<int*>(w + L.off_idx);
   float* tk_p = topk_p ? topk_p : reinterpret_cast<float*>(w + L.off_p);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_topk(probs, L.plan, reinterpret_cast<uint64_t*>(w + L.off_seg),
                              tk_idx, tk_p, s);
   if (e != hipSuccess) return TSV_EHIP;
@@ -113,7 +117,7 @@ int launch_build(const float* probs, int B, int rows_per_b, int steps, int V, in
   a.adaptive = cost ? 1 : 0;
   a.rows = rows_per_b;
   a.per_node = per_node ? 1 : 0;
-  a.cost = cost ? *cost : tsv_cost{0, 0, 0, 0, 0, 0};
+  a.cost = cost ? *cost : tsv_cost_fitted{0, 0, 0, 0, 0, 0};
   a.prefix_len = prefix_len;
   a.n_nodes = n_nodes;
   a.parent = parent;
@@ -148,6 +152,20 @@ size_t walk_bytes(int B, int N_max, int V, int dtype) {
   return align_up(static_cast<size_t>(rows) * p.nseg * sizeof(uint64_t));
 }
 
+// Argument checks shared by build_tree and its variants; TSV_OK when the
+// call may go ahead.
+int check_build(const float* marginals, int B, int gamma, int V, int top_k, int n_budget,
+                const tsv_cost_fitted* cost, const int* prefix_len, int N_max,
+                const int* n_nodes, const int* parent, const int* token, const int* depth,
+                const float* score, const unsigned* anc_bits) {
+  if (!marginals || !n_nodes || !parent || !token || !depth || !score || !anc_bits)
+    return TSV_EINVAL;
+  if (B < 1 || gamma < 1 || V < 1 || top_k < 1 || N_max < 1) return TSV_EINVAL;
+  if (top_k > V || n_budget < 0 || n_budget > N_max) return TSV_EINVAL;
+  if (!build_sizes_ok(B, gamma, V, top_k, N_max)) return TSV_EUNSUPPORTED;
+  if (cost && (!prefix_len || !cost_ok(cost))) return TSV_EINVAL;
+  return TSV_OK;
+}
 
 }  // namespace
 
@@ -192,40 +210,72 @@ size_t tsv_workspace_size(int which, int B, int gamma, int V, int top_k,
 int build_tree(const float* marginals, int B, int gamma, int V, int top_k,
                int n_budget, const tsv_cost* cost, const int* prefix_len,
                int N_max, int* n_nodes, int* parent, int* token, int* depth,
-               float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
-               void* ws, size_t ws_bytes, void* stream) {
-  if (!marginals || !n_nodes || !parent || !token || !depth || !score || !anc_bits)
-    return TSV_EINVAL;
-  if ((topk_idx == nullptr) != (topk_p == nullptr)) return TSV_EINVAL;
-  if (B < 1 || gamma < 1 || V < 1 || top_k < 1 || N_max < 1) return TSV_EINVAL;
-  if (top_k > V || n_budget < 0 || n_budget > N_max) return TSV_EINVAL;
-  if (!build_sizes_ok(B, gamma, V, top_k, N_max)) return TSV_EUNSUPPORTED;
-  if (cost && (!prefix_len || !cost_ok(cost))) return TSV_EINVAL;
-  return launch_build(marginals, B, gamma, gamma, V, top_k, n_budget, cost, prefix_len, N_max,
+               float* score, unsigned* anc_bits, void* ws, size_t ws_bytes,
+               hipStream_t s) {
+  tsv_cost_fitted fc;
+  if (cost) fc = widen(*cost);
+  const tsv_cost_fitted* c = cost ? &fc : nullptr;
+  const int st = check_build(marginals, B, gamma, V, top_k, n_budget, c, prefix_len, N_max,
+                             n_nodes, parent, token, depth, score, anc_bits);
+  if (st != TSV_OK) return st;
+  return launch_build(marginals, B, gamma, gamma, V, top_k, n_budget, c, prefix_len, N_max,
+                      n_nodes, parent, token, depth, score, anc_bits, nullptr, nullptr, ws,
+                      ws_bytes, s, false);
+}
+
+int build_tree_topk(const float* marginals, int B, int gamma, int V, int top_k,
+                    int n_budget, const tsv_cost* cost, const int* prefix_len,
+                    int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                    float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
+                    void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!topk_idx || !topk_p) return TSV_EINVAL;
+  tsv_cost_fitted fc;
+  if (cost) fc = widen(*cost);
+  const tsv_cost_fitted* c = cost ? &fc : nullptr;
+  const int st = check_build(marginals, B, gamma, V, top_k, n_budget, c, prefix_len, N_max,
+                             n_nodes, parent, token, depth, score, anc_bits);
+  if (st != TSV_OK) return st;
+  return launch_build(marginals, B, gamma, gamma, V, top_k, n_budget, c, prefix_len, N_max,
                       n_nodes, parent, token, depth, score, anc_bits, topk_idx, topk_p, ws,
-                      ws_bytes, stream, false);
+                      ws_bytes, s, false);
+}
+
+int build_tree_fitted(const float* marginals, int B, int gamma, int V, int top_k,
+                      int n_budget, const tsv_cost_fitted* cost, const int* prefix_len,
+                      int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                      float* score, unsigned* anc_bits, void* ws, size_t ws_bytes,
+                      hipStream_t s) {
+  const int st = check_build(marginals, B, gamma, V, top_k, n_budget, cost, prefix_len, N_max,
+                             n_nodes, parent, token, depth, score, anc_bits);
+  if (st != TSV_OK) return st;
+  return launch_build(marginals, B, gamma, gamma, V, top_k, n_budget, cost, prefix_len, N_max,
+                      n_nodes, parent, token, depth, score, anc_bits, nullptr, nullptr, ws,
+                      ws_bytes, s, false);
 }
 
 int build_tree_expand(const float* probs, int B, int steps, int V, int top_k,
                       int n_budget, const tsv_cost* cost, const int* prefix_len,
                       int N_max, int* n_nodes, int* parent, int* token, int* depth,
                       float* score, unsigned* anc_bits, int* topk_idx, float* topk_p,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      void* ws, size_t ws_bytes, hipStream_t s) {
   if (!probs || !n_nodes || !parent || !token || !depth || !score || !anc_bits)
     return TSV_EINVAL;
   if ((topk_idx == nullptr) != (topk_p == nullptr)) return TSV_EINVAL;
   if (B < 1 || steps < 1 || V < 1 || top_k < 1 || N_max < 1) return TSV_EINVAL;
   if (top_k > V || n_budget < 0 || n_budget > N_max) return TSV_EINVAL;
   if (!expand_sizes_ok(B, steps, V, top_k, N_max)) return TSV_EUNSUPPORTED;
-  if (cost && (!prefix_len || !cost_ok(cost))) return TSV_EINVAL;
-  return launch_build(probs, B, expanded_rows(steps, top_k), steps, V, top_k, n_budget, cost,
+  tsv_cost_fitted fc;
+  if (cost) fc = widen(*cost);
+  const tsv_cost_fitted* c = cost ? &fc : nullptr;
+  if (c && (!prefix_len || !cost_ok(c))) return TSV_EINVAL;
+  return launch_build(probs, B, expanded_rows(steps, top_k), steps, V, top_k, n_budget, c,
                       prefix_len, N_max, n_nodes, parent, token, depth, score, anc_bits,
-                      topk_idx, topk_p, ws, ws_bytes, stream, true);
+                      topk_idx, topk_p, ws, ws_bytes, s, true);
 }
 
 int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, float* score,
                          unsigned* anc_bits, int B, int N_max, const double* sps, long sps_len,
-                         void* stream) {
+                         hipStream_t s) {
   if (!n_nodes || !parent || !token || !depth || !score || !anc_bits || !sps) return TSV_EINVAL;
   if (B < 1 || N_max < 1 || N_max > kMaxNodes || sps_len < 1) return TSV_EINVAL;
   if (B > kMaxGlobalRequests || static_cast<long long>(B) * N_max > kMaxGlobalCandidates)
@@ -241,11 +291,11 @@ int select_global_budget(int* n_nodes, int* parent, int* token, int* depth, floa
   a.N_max = N_max;
   a.sps = sps;
   a.sps_len = sps_len;
-  return launch_status(launch_global_budget(a, static_cast<hipStream_t>(stream)));
+  return launch_status(launch_global_budget(a, s));
 }
 
 int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int gamma,
-                  int* n_chains, int* chain_len, int* chain_nodes, void* stream) {
+                  int* n_chains, int* chain_len, int* chain_nodes, hipStream_t s) {
   if (!n_nodes || !parent || !n_chains || !chain_len || !chain_nodes) return TSV_EINVAL;
   if (B < 1 || N_max < 1 || N_max > kMaxNodes || gamma < 1 || gamma > kMaxGamma) return TSV_EINVAL;
   ChainArgs a;
@@ -257,13 +307,13 @@ int unfold_chains(const int* n_nodes, const int* parent, int B, int N_max, int g
   a.n_chains = n_chains;
   a.chain_len = chain_len;
   a.chain_nodes = chain_nodes;
-  return launch_status(launch_unfold_chains(a, static_cast<hipStream_t>(stream)));
+  return launch_status(launch_unfold_chains(a, s));
 }
 
 int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
                     const float* tail, const int* prefix_len, const int* n_chains,
                     const int* chain_len, const int* chain_nodes, int B, int N_max,
-                    int gamma, float* entries, int* n_entries, void* stream) {
+                    int gamma, float* entries, int* n_entries, hipStream_t s) {
   if (!rows || !tail || !prefix_len || !n_chains || !chain_len || !chain_nodes || !entries ||
       !n_entries)
     return TSV_EINVAL;
@@ -289,14 +339,14 @@ int compress_chains(const void* rows, int dtype, long row_stride, long E, int c,
   const int es = esize(dtype);
   const bool vec = E % 4 == 0 && (row_stride * es) % (4 * es) == 0 && aligned_to(rows, 4 * es) &&
                    aligned_to(tail, 16) && aligned_to(entries, 16);
-  return launch_status(launch_compress_chains(a, dtype, vec, static_cast<hipStream_t>(stream)));
+  return launch_status(launch_compress_chains(a, dtype, vec, s));
 }
 
 int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int c,
                        const int* prefix_len, const int* accept_len, const int* accept_nodes,
                        const int* n_chains, const int* chain_len, const int* chain_nodes,
                        const float* entries, int B, int N_max, int gamma, float* comp,
-                       int Lc_cap, float* tail, int* status, void* stream) {
+                       int Lc_cap, float* tail, int* status, hipStream_t s) {
   if (!rows || !prefix_len || !accept_len || !accept_nodes || !n_chains || !chain_len ||
       !chain_nodes || !entries || !comp || !tail || !status)
     return TSV_EINVAL;
@@ -322,7 +372,7 @@ int refresh_compressed(const void* rows, int dtype, long row_stride, long E, int
   a.Lc_cap = Lc_cap;
   a.tail = tail;
   a.status = status;
-  return launch_status(launch_refresh_compressed(a, dtype, static_cast<hipStream_t>(stream)));
+  return launch_status(launch_refresh_compressed(a, dtype, s));
 }
 
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -331,7 +381,7 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const unsigned* anc_bits, int B, int N_max, int L_cap,
                      int Hq, int Hkv, int d_qk, int d_v, int dtype,
                      float sm_scale, void* out, float* lse, void* ws,
-                     size_t ws_bytes, void* stream) {
+                     size_t ws_bytes, hipStream_t s) {
   if (!q || !k_cache || !v_cache || !k_tree || !v_tree || !prefix_len || !n_nodes ||
       !anc_bits || !out)
     return TSV_EINVAL;
@@ -388,13 +438,13 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
   a.S = P.S;
   a.units = P.units;
   a.rbs = P.rbs;
-  return launch_status(launch_attention(a, P.path, dtype, static_cast<hipStream_t>(stream)));
+  return launch_status(launch_attention(a, P.path, dtype, s));
 }
 
 int accept_walk(const void* target_logits, int dtype, int B, int N_max, int V,
                 int gamma, const int* n_nodes, const int* parent,
                 const int* token, int* accept_len, int* accept_nodes,
-                int* out_tokens, void* ws, size_t ws_bytes, void* stream) {
+                int* out_tokens, void* ws, size_t ws_bytes, hipStream_t s) {
   if (!target_logits || !n_nodes || !parent || !token || !accept_len || !accept_nodes ||
       !out_tokens)
     return TSV_EINVAL;
@@ -409,14 +459,14 @@ int accept_walk(const void* target_logits, int dtype, int B, int N_max, int V,
   return launch_status(launch_accept_walk(target_logits, dtype, B, N_max, V, gamma, n_nodes,
                                           parent, token, accept_len, accept_nodes, out_tokens,
                                           static_cast<uint64_t*>(ws), p,
-                                          static_cast<hipStream_t>(stream)));
+                                          s));
 }
 
 int commit_path(void* k_cache, void* v_cache, int* prefix_len,
                 const void* k_tree, const void* v_tree, long kv_row_stride,
                 const int* accept_len, const int* accept_nodes, int B,
                 int N_max, int L_cap, int Hkv, int d_k, int d_v, int gamma,
-                int dtype, int* status, void* stream) {
+                int dtype, int* status, hipStream_t s) {
   if (!k_cache || !prefix_len || !k_tree || !accept_len || !accept_nodes || !status)
     return TSV_EINVAL;
   if ((v_cache == nullptr) != (v_tree == nullptr)) return TSV_EINVAL;
@@ -432,7 +482,7 @@ int commit_path(void* k_cache, void* v_cache, int* prefix_len,
                                      static_cast<size_t>(kv_row_stride) * es, accept_len,
                                      accept_nodes, B, N_max, L_cap, static_cast<size_t>(vk) * es,
                                      static_cast<size_t>(vv) * es, gamma, status,
-                                     static_cast<hipStream_t>(stream)));
+                                     s));
 }
 
 }  // extern "C"

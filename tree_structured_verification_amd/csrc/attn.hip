@@ -1683,7 +1683,15 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
   AttnPlan p;
   const bool bf = sh.dtype == TSV_BF16;
   p.chunk = p.S = p.units = p.rbs = 0;
+  // Every path starts its workspace with the grouped path's arrival counters
+  // (one int per request x KV head x block of 128 rows), which only that path
+  // touches and always leaves at zero.  The region depends on B, N_max, Hq
+  // and Hkv only, so one zeroed workspace serves calls of any dtype, path or
+  // prefix capacity at those sizes.
+  const int G0 = sh.Hq / sh.Hkv;
+  const long long cnt_units = static_cast<long long>(sh.B) * sh.Hkv * ((static_cast<long long>(sh.N_max) * G0 + 127) / 128);
   p.off_cnt = 0;
+  const size_t cnt_bytes = align_up(static_cast<size_t>((cnt_units + 7) / 8 * 8) * sizeof(int));
   if (bf && aligned && sh.d_qk == 128 && sh.d_v == 128) {
     // One kernel: the key range of every unit (request, KV head, block of
     // 128 rows) is cut into splits of `chunk` keys, sized from the capacity
@@ -1711,9 +1719,7 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
     if (p.S < s_len) p.S = static_cast<int>(s_len);
     p.chunk = p.min_chunk;  // the device cuts each unit's actual keys into S chunks of at least this
     p.items_max = units_pad * p.S;
-    size_t off = 0;
-    p.off_cnt = off;
-    off = align_up(off + static_cast<size_t>(units_pad) * sizeof(int));
+    size_t off = cnt_bytes;
     p.off_info = p.off_desc = off;
     p.off_ml = off;
     off = align_up(off + static_cast<size_t>(p.items_max) * p.RB * 2 * sizeof(float));
@@ -1740,7 +1746,7 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
   const long units = static_cast<long>(sh.B) * sh.Hkv * ((static_cast<long>(sh.N_max) * G + p.RB - 1) / p.RB);
   const long items = p.target_items + units;
   p.items_max = static_cast<int>(items);
-  size_t off = 0;
+  size_t off = cnt_bytes;
   p.off_info = off;
   off = align_up(off + (4 * static_cast<size_t>(sh.B) + 2) * sizeof(int));
   p.off_desc = off;

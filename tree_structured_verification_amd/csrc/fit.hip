@@ -74,7 +74,7 @@ bool subset_lsq(const double* n, const double* l, const double* t, const double*
 }  // namespace
 
 extern "C" int tsv_fit_cost(const double* n, const double* l, const double* t, int m, double c_d,
-                            tsv_cost* out) {
+                            tsv_cost_fitted* out) {
   if (!n || !l || !t || !out || m < kCols || m > (1 << 24)) return TSV_EINVAL;
   if (!isfinite(c_d)) return TSV_EINVAL;
   for (int i = 0; i < m; ++i)

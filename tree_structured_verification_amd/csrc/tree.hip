@@ -45,7 +45,7 @@ __device__ __forceinline__ float key_score(uint64_t key) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-__device__ __forceinline__ double round_cost(const tsv_cost& c, int n, double l) {
+__device__ __forceinline__ double round_cost(const tsv_cost_fitted& c, int n, double l) {
   double m = static_cast<double>(n);
   double v = __dadd_rn(c.a, __dmul_rn(c.b, m));
   v = __dadd_rn(v, __dmul_rn(c.c, __dmul_rn(m, m)));

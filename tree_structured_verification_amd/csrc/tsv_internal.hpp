@@ -33,7 +33,7 @@ struct TreeArgs {
   // rows of top-k lists per request: gamma (one per position), or the
   // expanded nodes in level order when per_node is set
   int rows, per_node;
-  tsv_cost cost;
+  tsv_cost_fitted cost;
   const int* prefix_len;
   int* n_nodes;
   int* parent;
