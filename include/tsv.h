@@ -168,6 +168,27 @@ int build_tree_topk(const float* marginals, int B, int gamma, int V, int top_k,
                     void* ws, size_t ws_bytes, hipStream_t s);
 
 /*
+ * build_tree_noalloc -- build_tree without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, results and errors are build_tree's without `ws` / `ws_bytes`:
+ * the per-position top-k table between the two stages lives in a scratch
+ * array of 4 MiB that the library holds on every GPU it runs on until the
+ * process ends (its address is looked up once per device, on the first call
+ * there).  Nothing is allocated or freed.  Limit: 8 * B * gamma * top_k <=
+ * 4 MiB (e.g. 64 requests x 16 positions x top-128); larger calls return
+ * TSV_EUNSUPPORTED before any launch.  The table's contents on entry do not
+ * matter, so nothing is cleared.  Every call on one GPU uses the same array:
+ * calls whose kernels may overlap on one GPU (different streams, or other
+ * threads) race and must be serialised by the caller.
+ */
+int build_tree_noalloc(const float* marginals, int B, int gamma, int V, int top_k,
+                       int n_budget, const tsv_cost* cost, const int* prefix_len,
+                       int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                       float* score, unsigned* anc_bits, hipStream_t s);
+
+/*
  * build_tree_fitted -- build_tree under a fitted cost model (the extra f*l
  * term, tsv_cost_fitted).
  *

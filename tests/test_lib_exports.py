@@ -21,7 +21,7 @@ def _declared():
 
 def test_all_declared_symbols_exported():
     names = _declared()
-    assert names == sorted(["build_tree", "build_tree_topk", "build_tree_fitted",
+    assert names == sorted(["build_tree", "build_tree_topk", "build_tree_fitted", "build_tree_noalloc",
                             "build_tree_expand", "tree_verify_attn", "accept_walk",
                             "commit_path", "select_global_budget", "tsv_fit_cost",
                             "tsv_workspace_size", "tsv_status_string", "unfold_chains",
@@ -83,6 +83,10 @@ def test_host_validation_without_launch():
                              1 << 20, nul) == -1                  # top-k outputs are required
     assert L.build_tree_topk(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p, p, p, p,
                              1 << 20, nul) == -1                  # top_k > V
+    assert L.build_tree_noalloc(p, 1, 2, 8, 9, 2, None, nul, 4, p, p, p, p, p, p,
+                                nul) == -1                        # top_k > V
+    assert L.build_tree_noalloc(p, 200, 32, 256, 128, 2, None, nul, 4, p, p, p, p, p, p,
+                                nul) == -2                        # top-k table above 4 MiB
     badf = tsv.tsv_cost_fitted(1.0, 0.02, 1e-4, 1e-6, 0.5, -1e-3)
     assert L.build_tree_fitted(p, 1, 2, 8, 2, 2, ctypes.byref(badf), p, 4, p, p, p, p, p, p, p,
                                1 << 20, nul) == -1                # negative f

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     build_tree,
     build_tree_expand,
     build_tree_fitted,
+    build_tree_noalloc,
     build_tree_topk,
     expanded_rows,
     fit_cost,

@@ -52,6 +52,8 @@ _SIGS = {
                    _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "build_tree_topk": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P],
+    "build_tree_noalloc": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
+                           _P, _P, _P, _P, _P, _P, _P],
     "build_tree_fitted": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost_fitted), _P, _I,
                           _P, _P, _P, _P, _P, _P, _P, _S, _P],
     "build_tree_expand": [_P, _I, _I, _I, _I, _I, ctypes.POINTER(tsv_cost), _P, _I,
@@ -217,6 +219,26 @@ def build_tree_topk(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: i
         _ptr(prefix_len), N_max, *_tree_ptrs(out), _ptr(out["topk_idx"]), _ptr(out["topk_p"]),
         _ptr(ws), ws.numel(), _stream(dev))
     _check("build_tree_topk", code)
+    return out
+
+
+def build_tree_noalloc(marginals: torch.Tensor, top_k: int, n_budget: int, N_max: int,
+                       cost=None, prefix_len: Optional[torch.Tensor] = None,
+                       out: Optional[dict] = None) -> dict:
+    """build_tree with the library's own per-device scratch instead of a
+    workspace (no device allocation by the library; outputs are still the
+    caller's)."""
+    _dev(marginals, "marginals", torch.float32)
+    B, gamma, V = marginals.shape
+    dev = marginals.device
+    if out is None:
+        out = _tree_outputs(B, N_max, dev)
+    if prefix_len is not None:
+        _dev(prefix_len, "prefix_len", torch.int32)
+    code = lib().build_tree_noalloc(
+        _ptr(marginals), B, gamma, V, top_k, n_budget, _cost_struct(cost),
+        _ptr(prefix_len), N_max, *_tree_ptrs(out), _stream(dev))
+    _check("build_tree_noalloc", code)
     return out
 
 

@@ -4,9 +4,20 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tsv_internal.hpp"
 
 using namespace tsv;
+
+// Scratch of build_tree_noalloc: the top-k table between its two kernels
+// (8 bytes per list entry, B * gamma * top_k entries).  Every GPU the library
+// runs on holds its own copy until the process ends; host code never uses
+// this name as an address (it is a host-side stand-in), only the device
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -167,6 +178,35 @@ int check_build(const float* marginals, int B, int gamma, int V, int top_k, int 
   return TSV_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the scratch array on the device of stream s (the current
+// device for the null stream), looked up once per device with that device
+// current.
+int scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return TSV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return TSV_EUNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return TSV_EHIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return TSV_EHIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && hipSetDevice(cur) != hipSuccess) return TSV_EHIP;
+      if (e != hipSuccess || !p) return TSV_EHIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return TSV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,6 +278,25 @@ int build_tree_topk(const float* marginals, int B, int gamma, int V, int top_k,
   return launch_build(marginals, B, gamma, gamma, V, top_k, n_budget, c, prefix_len, N_max,
                       n_nodes, parent, token, depth, score, anc_bits, topk_idx, topk_p, ws,
                       ws_bytes, s, false);
+}
+
+int build_tree_noalloc(const float* marginals, int B, int gamma, int V, int top_k,
+                       int n_budget, const tsv_cost* cost, const int* prefix_len,
+                       int N_max, int* n_nodes, int* parent, int* token, int* depth,
+                       float* score, unsigned* anc_bits, hipStream_t s) {
+  tsv_cost_fitted fc;
+  if (cost) fc = widen(*cost);
+  const tsv_cost_fitted* c = cost ? &fc : nullptr;
+  const int st = check_build(marginals, B, gamma, V, top_k, n_budget, c, prefix_len, N_max,
+                             n_nodes, parent, token, depth, score, anc_bits);
+  if (st != TSV_OK) return st;
+  if (build_layout(B, gamma, V, top_k).bytes > kNoAllocScratchBytes) return TSV_EUNSUPPORTED;
+  void* ws = nullptr;
+  const int sa = scratch_address(s, &ws);
+  if (sa != TSV_OK) return sa;
+  return launch_build(marginals, B, gamma, gamma, V, top_k, n_budget, c, prefix_len, N_max,
+                      n_nodes, parent, token, depth, score, anc_bits, nullptr, nullptr, ws,
+                      kNoAllocScratchBytes, s, false);
 }
 
 int build_tree_fitted(const float* marginals, int B, int gamma, int V, int top_k,
