@@ -204,192 +204,237 @@ struct WaveSelect {
 };
 
 constexpr int kMaxSegments = 16;
+constexpr int kComputeUnits = 256;   // of the MI355X
+constexpr int kBlock = 2048;   // elements a wavefront reads per block (32 per lane)
+// the final merge holds every wave's list
+constexpr int kMaxCand = kMaxSegments * 128;
 
-// One workgroup per row, wavefront w scanning segment w.
+// Element j (0..31) of this lane in a block starting at `base`: four
+// adjacent elements per 16-byte load when the row allows vector access, one
+// element per lane and load otherwise.
+template <bool VEC>
+__device__ __forceinline__ int blk_elem(int base, int j, int lane) {
+  return VEC ? base + (j >> 2) * 256 + lane * 4 + (j & 3) : base + j * 64 + lane;
+}
+
+// A block is read through a buffer resource over [base, end) of the row
+// (stride 0, dword 3 = 0x00020000, the raw 32-bit format of the CDNA buffer
+// descriptor): loads past its end return zeros without touching memory and
+// are never used, so no address is clamped and every load is issued without
+// a condition (a block's wait then covers only its own loads).
+template <bool VEC>
+__device__ __forceinline__ void load_blk(float (&v)[32], const float* p, int base, int end, int lane) {
+  const int avail = base < end ? end - base : 0;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p) + (base < end ? base : 0), 0, avail * 4, 0x00020000);
+  if (VEC) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (u * 256 + lane * 4) * 4, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[4 * u + c] = __uint_as_float(x[c]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (j * 64 + lane) * 4, 0, 0));
+  }
+}
+
+// One workgroup per row.  The row is cut into blocks of kBlock elements;
+// wave w of the W waves reads blocks w, w + W, w + 2W, ... (interleaved, so
+// the waves of a row stream neighbouring blocks and finish together) and
+// keeps its own list.
 template <int SLOTS, bool VEC>
 __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
     const float* __restrict__ x, int rows, int V, int k, int nseg, int seg_len,
     int* __restrict__ out_idx, float* __restrict__ out_p) {
   __shared__ uint64_t queue[kMaxSegments][64];
-  __shared__ uint64_t keys[kMaxSegments * 128];   // list hand-over, up to 128 keys per wave
+  __shared__ uint64_t cand[kMaxCand];
   __shared__ uint32_t published[kMaxSegments];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform values live in scalar registers (uniform branches)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x;
-  if (threadIdx.x < kMaxSegments) published[threadIdx.x] = 0;
-  __syncthreads();
-  // wave-uniform, so that a block's buffer resource lives in scalar registers
-  const int beg = __builtin_amdgcn_readfirstlane(wave * seg_len);
-  const int end = __builtin_amdgcn_readfirstlane(min(V, beg + seg_len));
+  const int W = nseg;                         // waves of the workgroup
+  const int nb = (V + kBlock - 1) / kBlock;   // blocks of the row, >= W
+  const int end = V;
   const float* p = x + static_cast<size_t>(row) * V;
 
-  WaveSelect<SLOTS> sel;
-  sel.init(k, queue[wave], published, wave, nseg, lane);
+  // The first block is requested before anything else happens; the second
+  // once the first has arrived, so that it is in flight while the first one
+  // seeds the list (requested together, both land in one burst and nothing
+  // is in flight during the seed).
+  float b0[32], b1[32];
+  int i0 = wave, i1 = wave + W;
+  load_blk<VEC>(b0, p, i0 * kBlock, end, lane);
+  if (threadIdx.x < kMaxSegments) published[threadIdx.x] = 0;
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only: the first block is here
+  asm volatile("" ::: "memory");
+  load_blk<VEC>(b1, p, i1 * kBlock, end, lane);
 
-  // Warm-up on the first 1024 elements: seed the list with every lane's best
-  // (and, for lists of 128, second best) element in one sort, then offer
-  // only the rest.  Without the seed the threshold admits everything until k
-  // keys are seen, and each 64 admissions cost a full sort and merge.
+  WaveSelect<SLOTS> sel;
+  sel.init(k, queue[wave], published, wave, W, lane);
+  // Offers the elements of a block at or above thr, except element `skip1`
+  // and `skip2` of this lane (the ones the first block seeded the list with).
+  // A lane's passing elements of a 16-byte group become keys (0 for the
+  // others), sorted descending by a five-step network, and are offered only
+  // while some lane still has one, so a group usually costs one offer.  The
+  // list's final contents do not depend on the order of the offers.
+  auto offer_block = [&](const float (&v)[32], int base, float thr, int skip1, int skip2) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // the group's maximum decides first whether any key needs building
+      const float gm = vmax3(vmax3(v[4 * u], v[4 * u + 1], v[4 * u + 2]), v[4 * u + 3], v[4 * u + 3]);
+      if (__ballot(gm >= thr && blk_elem<VEC>(base, 4 * u, lane) < end) == 0) continue;
+      uint64_t kk[4];
+      bool any = false;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * u + c;
+        const int e = blk_elem<VEC>(base, j, lane);
+        const bool ok = e < end && v[j] >= thr && j != skip1 && j != skip2;
+        kk[c] = ok ? sel_key(v[j], static_cast<uint32_t>(e)) : 0;
+        any |= ok;
+      }
+      if (__ballot(any) == 0) continue;
+      auto order = [](uint64_t& a, uint64_t& b) {
+        const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+        a = hi;
+        b = lo;
+      };
+      order(kk[0], kk[1]);
+      order(kk[2], kk[3]);
+      order(kk[0], kk[2]);
+      order(kk[1], kk[3]);
+      order(kk[1], kk[2]);
+      sel.offer(kk[0]);
+      if (__ballot(kk[1] != 0) != 0) {
+        sel.offer(kk[1]);
+        if (__ballot(kk[2] != 0) != 0) {
+          sel.offer(kk[2]);
+          if (__ballot(kk[3] != 0) != 0) sel.offer(kk[3]);
+        }
+      }
+    }
+  };
+  auto process = [&](const float (&v)[32], int base) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+      const int e = blk_elem<VEC>(base, j, lane);
+      float g;
+      if (VEC) {
+        // a 16-byte group lies wholly inside or wholly outside the row
+        g = vmax3(vmax3(v[j], v[j + 1], v[j + 2]), v[j + 3], v[j + 3]);
+        g = e < end ? g : -INFINITY;
+      } else {
+        g = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) g = blk_elem<VEC>(base, j + c, lane) < end ? fmaxf(g, v[j + c]) : g;
+      }
+      m = fmaxf(m, g);
+    }
+    const float thr = sel.threshold();
+    if (__ballot(m >= thr) == 0) return;
+    offer_block(v, base, thr, -1, -1);
+  };
+
+  // A wave's first block seeds the list with every lane's best (and, for lists of 128,
+  // second best) element in one sort; only the rest is offered.  Without the
+  // seed the threshold admits everything until k keys are seen, and each 64
+  // admissions cost a full sort and merge.
   {
-    float v[16];
-    int e0[16];
+    // a lane's best element is its largest value, the first one on ties
+    // (element indices grow with j, and the lower index is the better key)
+    float m1 = -INFINITY, m2 = -INFINITY;
+    int j1 = -1, j2 = -1;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      // element order per lane is increasing in index, as in the main loop
-      const int e = VEC ? beg + (u >> 2) * 256 + lane * 4 + (u & 3) : beg + u * 64 + lane;
-      e0[u] = e;
-      v[u] = e < end ? p[e] : -INFINITY;
+    for (int j = 0; j < 32; ++j) {
+      const bool ok = blk_elem<VEC>(i0 * kBlock, j, lane) < end && b0[j] > m1;
+      m1 = ok ? b0[j] : m1;
+      j1 = ok ? j : j1;
     }
-    uint64_t k1 = 0, k2 = 0;
-    int u1 = -1, u2 = -1;
+    if (SLOTS > 1) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint64_t kk = e0[u] < end ? sel_key(v[u], e0[u]) : 0;
-      if (kk > k1) { k2 = k1; u2 = u1; k1 = kk; u1 = u; }
-      else if (kk > k2) { k2 = kk; u2 = u; }
+      for (int j = 0; j < 32; ++j) {
+        const bool ok = blk_elem<VEC>(i0 * kBlock, j, lane) < end && j != j1 && b0[j] > m2;
+        m2 = ok ? b0[j] : m2;
+        j2 = ok ? j : j2;
+      }
     }
+    const uint64_t k1 = j1 >= 0 ? sel_key(m1, static_cast<uint32_t>(blk_elem<VEC>(i0 * kBlock, j1, lane))) : 0;
+    const uint64_t k2 = j2 >= 0 ? sel_key(m2, static_cast<uint32_t>(blk_elem<VEC>(i0 * kBlock, j2, lane))) : 0;
     sel.list.v[0] = sort64_desc(k1, lane);
     if (SLOTS > 1) sel.list.merge(sort64_desc(k2, lane));
     sel.set_tau();
-    const float thr = sel.threshold();
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const bool seeded = (u == u1) || (SLOTS > 1 && u == u2);
-      const bool ok = e0[u] < end && !seeded && v[u] >= thr;
-      if (__ballot(ok) == 0) continue;
-      sel.offer(ok ? sel_key(v[u], e0[u]) : 0);
-    }
+    offer_block(b0, i0 * kBlock, sel.threshold(), j1, j2);
+  }
+  // two blocks in turn: one in flight while the other is scanned
+  int inext = i1 + W;
+  auto take = [&]() {
+    const int i = inext;
+    inext += W;
+    return i;
+  };
+  while (i1 < nb) {
+    const int i2 = take();
+    load_blk<VEC>(b0, p, i2 * kBlock, end, lane);
+    process(b1, i1 * kBlock);
+    if (i2 >= nb) break;
+    i1 = take();
+    load_blk<VEC>(b1, p, i1 * kBlock, end, lane);
+    process(b0, i2 * kBlock);
   }
 
-  if (VEC) {
-    // blocks of 8 float4 per lane (2048 elements); a group past the end
-    // re-reads the slice's last group and is ignored, so loads are
-    // unconditional; two blocks alternate so that one is in flight while the
-    // other is scanned
-    // A block is read through a buffer resource over [base, end) of the row
-    // (stride 0, dword 3 = 0x00020000, the raw 32-bit format of the CDNA
-    // buffer descriptor): loads past its end return zeros without touching
-    // memory and are never processed, so no address is clamped and the lane
-    // offsets stay constant registers.
-    auto load_block = [&](float4 (&raw)[8], int base) {
-      const int avail = base < end ? end - base : 0;
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(p) + (base < end ? base : 0), 0, avail * 4, 0x00020000);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (u * 256 + lane * 4) * 4, 0, 0);
-        raw[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                             __uint_as_float(v[3]));
-      }
-    };
-    auto process = [&](const float4 (&v)[8], int base) {
-      float m4[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = base + u * 256 + lane * 4;
-        const float m = vmax3(vmax3(v[u].x, v[u].y, v[u].z), v[u].w, v[u].w);
-        m4[u] = e < end ? m : -INFINITY;
-      }
-      const float m = vmax3(vmax3(m4[0], m4[1], m4[2]), vmax3(m4[3], m4[4], m4[5]), vmax3(m4[6], m4[7], m4[7]));
-      const float thr = sel.threshold();
-      if (__ballot(m >= thr) == 0) return;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = base + u * 256 + lane * 4;
-        const bool ok = e < end;
-        if (__ballot(ok && m4[u] >= thr) == 0) continue;
-        // The lane's elements at or above the filter become keys (0 for the
-        // others), sorted descending by a five-step network; they are offered
-        // only while some lane still has one, so a group usually costs one
-        // or two offers instead of four.  The list's final contents do not
-        // depend on the order of the offers.  (Indices stay static: a loop
-        // over a lane's pending elements moved the block to scratch memory.)
-        uint64_t k0 = ok && v[u].x >= thr ? sel_key(v[u].x, e) : 0;
-        uint64_t k1 = ok && v[u].y >= thr ? sel_key(v[u].y, e + 1) : 0;
-        uint64_t k2 = ok && v[u].z >= thr ? sel_key(v[u].z, e + 2) : 0;
-        uint64_t k3 = ok && v[u].w >= thr ? sel_key(v[u].w, e + 3) : 0;
-        auto order = [](uint64_t& a, uint64_t& b) {
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          a = hi;
-          b = lo;
-        };
-        order(k0, k1);
-        order(k2, k3);
-        order(k0, k2);
-        order(k1, k3);
-        order(k1, k2);
-        sel.offer(k0);
-        if (__ballot(k1 != 0) != 0) {
-          sel.offer(k1);
-          if (__ballot(k2 != 0) != 0) {
-            sel.offer(k2);
-            if (__ballot(k3 != 0) != 0) sel.offer(k3);
-          }
-        }
-      }
-    };
-    // The next block's loads are issued without a condition (past the end
-    // they return zeros, never processed): behind a branch, the wait
-    // before the current block's last use would also cover them, and the
-    // two blocks would no longer overlap.
-    float4 b0[8], b1[8];
-    const int first = beg + 1024;
-    load_block(b0, first);
-    for (int base = first; base < end; base += 4096) {
-      load_block(b1, base + 2048);
-      process(b0, base);
-      if (base + 2048 >= end) break;
-      load_block(b0, base + 4096);
-      process(b1, base + 2048);
-    }
-  } else {
-    for (int base = beg + 1024; base < end; base += 1024) {
-      float v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        int e = base + u * 64 + lane;
-        v[u] = e < end ? p[e] : -INFINITY;
-      }
-      float m = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) m = fmaxf(m, v[u]);
-      if (__ballot(m >= sel.threshold()) == 0) continue;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        int e = base + u * 64 + lane;
-        sel.offer(e < end ? sel_key(v[u], e) : 0);
-      }
-    }
-  }
+  // Final merge.  A wave's own k best keys are the first k of its list once
+  // its queue is merged in (an element passed the filter when it was seen,
+  // the filter being a lower bound of the row's k-th value, and a list drops
+  // a key only for 64 * SLOTS >= k better keys of the same wave), so the
+  // row's top k is among the waves' first k keys.  Those go to LDS in
+  // order.  The rank of a key in the row is, summed over the lists, the
+  // number of keys larger than it (binary searches: the lists are
+  // descending and keys are unique); only keys at or above the row floor
+  // (every wave has published its final value) can rank below k, and the key
+  // of rank r < k is written to place r.
   sel.finish();
-
-  // Tree merge of the wave lists (each holds its segment's best keys, and
-  // the row's top k is among them): in round r, wave w with w % 2r == r
-  // hands its list through LDS to wave w - r, which merges it into its own.
-  // A wave's LDS slot is read only in the round it sends, and it sends only
-  // after its last merge, so one barrier per round orders everything.
-  for (int r = 1; r < nseg; r <<= 1) {
-    if ((wave & (2 * r - 1)) == r) {
-#pragma unroll
-      for (int s2 = 0; s2 < SLOTS; ++s2) keys[wave * 128 + s2 * 64 + lane] = sel.list.v[s2];
-    }
-    __syncthreads();
-    if ((wave & (2 * r - 1)) == 0 && wave + r < nseg) {
-#pragma unroll
-      for (int s2 = 0; s2 < SLOTS; ++s2) sel.list.merge(keys[(wave + r) * 128 + s2 * 64 + lane]);
-    }
+  const int KL = 64 * SLOTS;
+  for (int s2 = 0; s2 < SLOTS; ++s2) cand[wave * KL + s2 * 64 + lane] = sel.list.v[s2];
+  __syncthreads();
+  uint32_t ofloor = 0;
+  {
+    uint32_t o = lane < W ? published[lane] : 0u;
+    o = sort16_desc_u32(o, lane);
+    ofloor = __builtin_amdgcn_readlane(o, sel.r - 1);   // 0: no floor
   }
-  if (wave != 0) return;
+  const int kl = min(k, KL);
+  for (int i = threadIdx.x; i < W * kl; i += blockDim.x) {
+    const int w = i / kl, pos = i - w * kl;
+    const uint64_t key = cand[w * KL + pos];
+    if (key == 0 || static_cast<uint32_t>(key >> 32) < ofloor) continue;
+    // one binary search per list, advanced a step at a time over all lists
+    // so that their LDS reads are independent
+    int at[kMaxSegments];
 #pragma unroll
-  for (int s2 = 0; s2 < SLOTS; ++s2) {
-    const int pos = s2 * 64 + lane;
-    if (pos >= k) continue;
-    const uint64_t key = sel.list.v[s2];
-    // every row holds V >= k elements, so the first k places are filled;
-    // the guard keeps an impossible empty place inside the row
-    const uint32_t idx = key ? sel_key_index(key) : 0u;
-    out_idx[static_cast<size_t>(row) * k + pos] = static_cast<int>(idx);
-    // re-read the element so the stored probability keeps its exact bits
-    out_p[static_cast<size_t>(row) * k + pos] = p[idx];
+    for (int w2 = 0; w2 < kMaxSegments; ++w2) at[w2] = 0;
+#pragma unroll
+    for (int st = 128; st >= 1; st >>= 1) {
+      if (st > KL || st > kl) continue;
+#pragma unroll
+      for (int w2 = 0; w2 < kMaxSegments; ++w2) {
+        const int q = at[w2] + st;
+        if (w2 < W && q <= kl && cand[w2 * KL + q - 1] > key) at[w2] = q;
+      }
+    }
+    int rank = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kMaxSegments; ++w2) rank += at[w2];
+    if (rank < k) {
+      const uint32_t idx = sel_key_index(key);
+      out_idx[static_cast<size_t>(row) * k + rank] = static_cast<int>(idx);
+      // re-read the element so the stored probability keeps its exact bits
+      out_p[static_cast<size_t>(row) * k + rank] = p[idx];
+    }
   }
 }
 
@@ -402,14 +447,13 @@ TopkPlan topk_plan(int rows, int V, int k) {
   p.k = k;
   p.slots = k <= 64 ? 1 : 2;
   p.vec = (V % 4) == 0;
-  // segments of at least ~8k elements, at most kMaxSegments per row
-  int nseg = (V + 8191) / 8192;
-  if (nseg > kMaxSegments) nseg = kMaxSegments;
-  if (nseg < 1) nseg = 1;
-  int len = (V + nseg - 1) / nseg;
-  len = (len + 1023) / 2048 * 2048 + 1024;  // one warm-up block of 1024, then steps of 2048
-  p.seg_len = len;
-  p.nseg = (V + len - 1) / len;
+  // One wave per block of the row, at most kMaxSegments; with more rows than
+  // compute units, half as many, so that two rows share a compute unit and
+  // one streams while the other merges.
+  const int nb = (V + kBlock - 1) / kBlock;
+  const int most = rows > kComputeUnits ? kMaxSegments / 2 : kMaxSegments;
+  p.nseg = nb < most ? nb : most;
+  p.seg_len = kBlock;
   return p;
 }
 
