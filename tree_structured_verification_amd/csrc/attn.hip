@@ -326,7 +326,11 @@ __device__ __forceinline__ void wait_later(int later) {
 __device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& unit) {
   const int id = static_cast<int>(blockIdx.x);
   const int slot = id >> 3;
-  unit = (slot / a.S) * 8 + (id & 7);
+  // consecutive groups of 8 units rotate over the XCDs, so that every XCD
+  // streams every KV head (the units of a group are the KV heads of one
+  // request and row block)
+  const int grp = slot / a.S;
+  unit = grp * 8 + (((id & 7) + grp) & 7);
   const int split = slot % a.S;
   if (unit >= a.units) return false;
   // units are numbered row block first: the first row block of every
@@ -898,12 +902,24 @@ constexpr int kLatQK = 576, kLatV = 512;
 constexpr int kLatTile = 32 * kLatQK * 2;        // bytes of one K tile
 constexpr int kLatSlots = 3;
 constexpr int kLatP = kLatSlots * kLatTile;      // weights, two buffers of 8 KiB
-constexpr int kLatAlpha = kLatP + 2 * 8192;      // rescale factors [2][4 copies][16][8]
-constexpr int kLatFlag = kLatAlpha + 2 * 2048;   // rescale flags [2][4 waves][64 lanes]
+// rescale factors [2][4 copies][16 rows][9 floats] (8 used; the ninth pads
+// the rows so that the 32 lanes of a write or read hit distinct banks)
+constexpr int kLatAlphaCopy = 16 * 9;            // floats per copy
+constexpr int kLatAlphaBuf = 2304;               // bytes per buffer (4 copies, 256-aligned)
+constexpr int kLatAlpha = kLatP + 2 * 8192;
+constexpr int kLatFlag = kLatAlpha + 2 * kLatAlphaBuf;   // rescale flags [2][4 waves][64 lanes]
 constexpr int kLatStat = kLatFlag + 2 * 1024;    // final (max, sum) per row
 constexpr int kLatLds = kLatStat + 128 * 8;
 
-__device__ __forceinline__ int lat_s(int k) { return ((k & 3) << 1) | ((k & 4) << 1) | ((k >> 3) & 1); }
+// Granule swizzle of key k (a bijection of k % 16): granule C of key k sits
+// at C ^ s(k) in its row.  Measured with the LDS bank-conflict counter on the
+// long latent workload: the identity leaves 0.48 conflict cycles per LDS
+// instruction, where a swizzle chosen for 16 lanes per cycle over 64 banks
+// (conflict-free on paper for both the score operand reads and the
+// transposed value reads) gave 2.1; the hardware serves these reads in a
+// pattern neither model captures, and the kernel's time does not depend on
+// the difference.
+__device__ __forceinline__ int lat_s(int k) { return k & 15; }
 __device__ __forceinline__ int lat_t(int k) { return (k >> 1) & 7; }
 
 // s_waitcnt vmcnt(0) lgkmcnt(0): this wave's DMA blocks and LDS writes done
@@ -1171,7 +1187,7 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
       const bool any = __ballot(moved) != 0;
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg)
-        *reinterpret_cast<float*>(smem + kLatAlpha + nbuf * 2048 + lq * 512 + (lr * 8 + 2 * wave + rg) * 4) = alpha[rg];
+        *reinterpret_cast<float*>(smem + kLatAlpha + nbuf * kLatAlphaBuf + (lq * kLatAlphaCopy + lr * 9 + 2 * wave + rg) * 4) = alpha[rg];
       *reinterpret_cast<int*>(smem + kLatFlag + nbuf * 1024 + wave * 256 + lane * 4) = any ? 1 : 0;
     };
     bf16x8 pt[8], vf[2];
@@ -1205,7 +1221,7 @@ __global__ __launch_bounds__(256, 1) void attn_latent_kernel(AttnArgs a) {
     const int fm = __builtin_amdgcn_readfirstlane((fl[0] ? 1 : 0) | (fl[64] ? 2 : 0) | (fl[128] ? 4 : 0) | (fl[192] ? 8 : 0));
     if (fm == 0) return;
     asm volatile("" ::: "memory");  // a real branch: rare after the first tile
-    const float* al = reinterpret_cast<const float*>(smem + kLatAlpha + buf * 2048 + lq * 512 + lr * 32);
+    const float* al = reinterpret_cast<const float*>(smem + kLatAlpha + buf * kLatAlphaBuf + (lq * kLatAlphaCopy + lr * 9) * 4);
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
       const float f = ((fm >> (rb >> 1)) & 1) ? al[rb] : 1.f;
