@@ -252,6 +252,7 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
   __shared__ uint64_t queue[kMaxSegments][64];
   __shared__ uint64_t cand[kMaxCand];
   __shared__ uint32_t published[kMaxSegments];
+  __shared__ int cand_n;
   // wave-uniform values live in scalar registers (uniform branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x;
@@ -268,6 +269,7 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
   int i0 = wave, i1 = wave + W;
   load_blk<VEC>(b0, p, i0 * kBlock, end, lane);
   if (threadIdx.x < kMaxSegments) published[threadIdx.x] = 0;
+  if (threadIdx.x == 0) cand_n = 0;
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only: the first block is here
   asm volatile("" ::: "memory");
@@ -391,49 +393,58 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
   // its queue is merged in (an element passed the filter when it was seen,
   // the filter being a lower bound of the row's k-th value, and a list drops
   // a key only for 64 * SLOTS >= k better keys of the same wave), so the
-  // row's top k is among the waves' first k keys.  Those go to LDS in
-  // order.  The rank of a key in the row is, summed over the lists, the
-  // number of keys larger than it (binary searches: the lists are
-  // descending and keys are unique); only keys at or above the row floor
-  // (every wave has published its final value) can rank below k, and the key
-  // of rank r < k is written to place r.
+  // row's top k is among the waves' first k keys.  Once every wave has
+  // published its final value, the keys at or above the row floor (only
+  // those can rank below k) are gathered in LDS; the rank of a key is the
+  // number of gathered keys larger than it (keys are unique), and the key of
+  // rank r < k is written to place r.
   sel.finish();
-  const int KL = 64 * SLOTS;
-  for (int s2 = 0; s2 < SLOTS; ++s2) cand[wave * KL + s2 * 64 + lane] = sel.list.v[s2];
   __syncthreads();
-  uint32_t ofloor = 0;
+  const int KL = 64 * SLOTS;
+  const int kl = min(k, KL);
   {
     uint32_t o = lane < W ? published[lane] : 0u;
     o = sort16_desc_u32(o, lane);
-    ofloor = __builtin_amdgcn_readlane(o, sel.r - 1);   // 0: no floor
-  }
-  const int kl = min(k, KL);
-  for (int i = threadIdx.x; i < W * kl; i += blockDim.x) {
-    const int w = i / kl, pos = i - w * kl;
-    const uint64_t key = cand[w * KL + pos];
-    if (key == 0 || static_cast<uint32_t>(key >> 32) < ofloor) continue;
-    // one binary search per list, advanced a step at a time over all lists
-    // so that their LDS reads are independent
-    int at[kMaxSegments];
+    const uint32_t ofloor = __builtin_amdgcn_readlane(o, sel.r - 1);   // 0: no floor
+    int n = 0;
+    uint64_t mk[SLOTS];
 #pragma unroll
-    for (int w2 = 0; w2 < kMaxSegments; ++w2) at[w2] = 0;
-#pragma unroll
-    for (int st = 128; st >= 1; st >>= 1) {
-      if (st > KL || st > kl) continue;
-#pragma unroll
-      for (int w2 = 0; w2 < kMaxSegments; ++w2) {
-        const int q = at[w2] + st;
-        if (w2 < W && q <= kl && cand[w2 * KL + q - 1] > key) at[w2] = q;
-      }
+    for (int s2 = 0; s2 < SLOTS; ++s2) {
+      const uint64_t key = sel.list.v[s2];
+      const bool keep = s2 * 64 + lane < kl && key != 0 && static_cast<uint32_t>(key >> 32) >= ofloor;
+      mk[s2] = __ballot(keep);
+      n += __popcll(mk[s2]);
     }
-    int rank = 0;
+    int base = 0;
+    if (lane == 0) base = __hip_atomic_fetch_add(&cand_n, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
-    for (int w2 = 0; w2 < kMaxSegments; ++w2) rank += at[w2];
+    for (int s2 = 0; s2 < SLOTS; ++s2) {
+      if ((mk[s2] >> lane) & 1) {
+        const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mk[s2] >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk[s2]), 0));
+        cand[base + below] = sel.list.v[s2];
+      }
+      base += __popcll(mk[s2]);
+    }
+  }
+  __syncthreads();
+  const int C = cand_n;
+  for (int i = threadIdx.x; i < C; i += blockDim.x) {
+    const uint64_t key = cand[i];
+    int rank = 0, j = 0;
+    for (; j + 4 <= C; j += 4)
+      rank += (cand[j] > key ? 1 : 0) + (cand[j + 1] > key ? 1 : 0) + (cand[j + 2] > key ? 1 : 0) +
+              (cand[j + 3] > key ? 1 : 0);
+    for (; j < C; ++j) rank += cand[j] > key ? 1 : 0;
     if (rank < k) {
       const uint32_t idx = sel_key_index(key);
       out_idx[static_cast<size_t>(row) * k + rank] = static_cast<int>(idx);
-      // re-read the element so the stored probability keeps its exact bits
-      out_p[static_cast<size_t>(row) * k + rank] = p[idx];
+      // the key holds the value's exact bits except the sign of a zero,
+      // so only a zero is read again
+      float v = ord_value(static_cast<uint32_t>(key >> 32));
+      if (v == 0.0f) v = p[idx];
+      out_p[static_cast<size_t>(row) * k + rank] = v;
     }
   }
 }
