@@ -78,7 +78,7 @@ if ROOT not in sys.path:
 
 import tree_structured_verification_amd as tsv  # noqa: E402
 from tree_structured_verification_amd import _lib  # noqa: E402
-from workloads import Cost, attention_inputs, config, marginals, prefix_lengths, target_logits  # noqa: E402
+from workloads import Cost, attention_inputs, config, marginals, pitched, prefix_lengths, target_logits  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak
@@ -123,19 +123,41 @@ def attention_bytes(cfg, prefix, n):
     return prefix_bytes + nodes * per_node
 
 
+KV_LAYOUT = "padded"   # set from --kv-layout
+
+
+def kv_pitch(cfg):
+    """Elements between cache (and scratch) rows: the library's recommended
+    pitch (an odd number of 128-byte lines) or the dense row width."""
+    width = cfg.d_qk if cfg.mla else cfg.Hkv * max(cfg.d_qk, cfg.d_v)
+    if KV_LAYOUT == "dense":
+        return width
+    return tsv.kv_row_pitch(width, 2 if cfg.dtype == "bf16" else 4)
+
+
+def clone_rows(t):
+    """A copy of a cache or scratch tensor with the same row pitch (clone()
+    would pack the rows)."""
+    if t.is_contiguous():
+        return t.clone()
+    out = pitched(t.shape[0], t.shape[1], tuple(t.shape[2:]), t.dtype, t.device, t.stride(1))
+    out.copy_(t)
+    return out
+
+
 def attention_only(wid, K, W, dev):
     """K timed tree_verify_attn calls (after W) on workload wid, inputs in
     three rotating copies; prints one JSON line."""
     cfg = config(wid)
     print(f"[bench] attention only, workload {cfg.name}", file=sys.stderr, flush=True)
-    ins = attention_inputs(cfg, 0, dev)
+    ins = attention_inputs(cfg, 0, dev, row_pitch=kv_pitch(cfg))
     marg = marginals(cfg, 0, dev)
     pl = ins["prefix_len"]
     tree = tsv.build_tree(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=cfg.cost,
                           prefix_len=pl if cfg.cost is not None else None)
     del marg
     keys = ("q", "k_cache", "v_cache", "k_tree", "v_tree")
-    sets = [ins] + [{k: ins[k].clone() for k in keys} for _ in range(ROTATE - 1)]
+    sets = [ins] + [{k: clone_rows(ins[k]) for k in keys} for _ in range(ROTATE - 1)]
     if cfg.mla:   # one latent cache serves as key and value
         for st in sets:
             st["v_cache"], st["v_tree"] = st["k_cache"], st["k_tree"]
@@ -163,7 +185,8 @@ def attention_only(wid, K, W, dev):
     pairs = sum(int(n[b]) * int(prefix[b]) + int(depth[b, :n[b]].sum()) for b in range(B))
     flops = 2.0 * pairs * cfg.Hq * (cfg.d_qk + cfg.d_v)
     nbytes = attention_bytes(cfg, prefix, n)
-    print(json.dumps({"attention_workload": cfg.name, "calls": K, "us_per_call": round(t * 1e6, 1),
+    print(json.dumps({"attention_workload": cfg.name, "kv_row_bytes": ins["k_cache"].stride(1) * ins["k_cache"].element_size(),
+                      "calls": K, "us_per_call": round(t * 1e6, 1),
                       "tflops": round(flops / t / 1e12, 1),
                       "mfma_frac_bf16": round(flops / t / 2.5e15, 4),
                       "gbs": round(nbytes / t / 1e9, 1),
@@ -491,7 +514,7 @@ def round_bench(wid, K, W, dev):
     adaptive = cfg.cost is not None
     print(f"[bench] generating workload {cfg.name}", file=sys.stderr, flush=True)
     marg0 = marginals(cfg, 0, dev)
-    ins0 = attention_inputs(cfg, 0, dev)
+    ins0 = attention_inputs(cfg, 0, dev, row_pitch=kv_pitch(cfg))
     prefix0 = ins0["prefix_len"].clone()
     # the workload's tree (deterministic) lays out the target rows
     tree0 = tsv.build_tree(marg0, cfg.top_k, cfg.n_budget, cfg.N_max, cost=cfg.cost,
@@ -503,17 +526,18 @@ def round_bench(wid, K, W, dev):
     big = [marg0, ins0["q"], ins0["k_cache"], ins0["k_tree"], tl0]
     if not cfg.mla:
         big += [ins0["v_cache"], ins0["v_tree"]]
-    per_copy = sum(t.numel() * t.element_size() for t in big)
+    per_copy = sum(t.numel() * t.element_size() for t in big)   # bytes in use
     # rotating copies keep the 256 MB last-level cache from serving a step
     # from the previous one; one copy of several GB already does that
     copies = ROTATE if per_copy < (4 << 30) else 1
     sets = []
     for r in range(copies):
         c = (lambda t: t) if r == 0 else (lambda t: t.clone())
-        st = dict(marg=c(marg0), q=c(ins0["q"]), kc=c(ins0["k_cache"]), kt=c(ins0["k_tree"]),
+        cr = (lambda t: t) if r == 0 else clone_rows
+        st = dict(marg=c(marg0), q=c(ins0["q"]), kc=cr(ins0["k_cache"]), kt=cr(ins0["k_tree"]),
                   tl=c(tl0))
-        st["vc"] = st["kc"] if cfg.mla else c(ins0["v_cache"])
-        st["vt"] = st["kt"] if cfg.mla else c(ins0["v_tree"])
+        st["vc"] = st["kc"] if cfg.mla else cr(ins0["v_cache"])
+        st["vt"] = st["kt"] if cfg.mla else cr(ins0["v_tree"])
         sets.append(st)
     prefixes = [prefix0.clone() for _ in range(K + W)]
 
@@ -539,7 +563,10 @@ def round_bench(wid, K, W, dev):
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-    stride = cfg.kv_stride
+    stride = ins0["k_cache"].stride(1)
+    for st in sets:
+        if {st[k].stride(1) for k in ("kc", "vc", "kt", "vt")} != {stride}:
+            raise RuntimeError("rotating copies lost the row pitch")
 
     # pre-marshalled argument tuples: the timed loop only calls the library
     def step_args(s):
@@ -633,6 +660,7 @@ def round_bench(wid, K, W, dev):
                           "accept_walk": float(np.mean(t_walk)),
                           "commit_path": float(np.mean(t_commit))},
                attn_s=attn_s, attn_bytes=attention_bytes(cfg, prefix_np, n_np),
+               kv_row_bytes=stride * ins0["k_cache"].element_size(),
                attn_flops=attention_flops(cfg, n_np, depth_np, prefix_np),
                n=n_np, prefix=prefix_np, depth=depth_np)
     res["sets0"] = sets[0]
@@ -787,6 +815,7 @@ def workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu):
          "tokens_per_s": round(res["value"], 1),
          "accepted_tokens_per_s": round(res["accepted_per_s"], 1),
          "tree_tokens": res["tokens"], "input_copies": res["copies"],
+         "kv_row_bytes": res["kv_row_bytes"],
          "kernel_us": {k: round(v * 1e3, 1) for k, v in res["kernel_ms"].items()},
          "attention": attention_roofline(res, copy_gbs, gemm_tflops)}
     if with_cpu:
@@ -812,6 +841,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-workload", action="store_true",
                     help="time only the headline workload")
+    ap.add_argument("--kv-layout", choices=("padded", "dense"), default="padded",
+                    help="cache and scratch rows at the library's recommended pitch (an odd "
+                         "number of 128-byte lines) or packed")
     ap.add_argument("--attention-only", action="store_true",
                     help="run only the tree_verify_attn calls of the headline workload "
                          "(for counter runs)")
@@ -838,6 +870,8 @@ def main():
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
+    global KV_LAYOUT
+    KV_LAYOUT = args.kv_layout
     dev = torch.device("cuda:0")
     if args.copy_calibration > 0:
         nb = args.copy_calibration << 20
@@ -892,7 +926,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_desc(cfg), "B": cfg.B, "gamma": cfg.gamma, "V": cfg.V,
                    "top_k": cfg.top_k, "budget": cfg.n_budget, "prefix": cfg.prefix,
-                   "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": cfg.d_qk},
+                   "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": cfg.d_qk,
+                   "kv_row_bytes": head["kv_row_bytes"]},
         "accepted_tokens_per_s": round(head["accepted_per_s"], 1),
         "kernel_ms": {k: round(v, 4) for k, v in head["kernel_ms"].items()},
         "roofline": roof,

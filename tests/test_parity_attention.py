@@ -344,3 +344,69 @@ def test_workspace_reuse_across_dtype_and_shapes():
     call(3, [6000, 10, 2222], torch.bfloat16, 6016, ws)
     ws.zero_()
     call(2, [1234, 4321], torch.bfloat16, 4337, ws)
+
+
+def _pitched_copy(t, pitch):
+    out = tsv.kv_rows(t.shape[0], t.shape[1], tuple(t.shape[2:]), t.dtype, DEV, pitch)
+    out.copy_(t)
+    return out
+
+
+PITCH_CASES = ["fp32_mha", "bf16_gqa_g4", "bf16_latent_mfma", "bf16_valu_d64", "bf16_many_splits"]
+
+
+@pytest.mark.parametrize("name", PITCH_CASES)
+def test_pitched_rows(name):
+    """Cache and scratch rows further apart than their width (the recommended
+    pitch, and an arbitrary 16-byte multiple): the same bits as packed rows,
+    and the oracle's values."""
+    case = next(c for c in CASES if c[0] == name)
+    _, B, N_max, Hq, Hkv, d_qk, d_v, dtype, prefix, n_list, mla = case
+    print(f"attention case {name}, pitched rows", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + 1)
+    L_cap = max(prefix) + 16
+    q, kc, vc, kt, vt, pl = _inputs(rng, B, N_max, L_cap, Hq, Hkv, d_qk, d_v, dtype, prefix, mla)
+    trees = _random_trees(rng, B, N_max, n_list)
+    scale = 1.0 / math.sqrt(d_qk)
+    o0, l0, _, _ = _run(q, kc, vc, kt, vt, pl, trees, Hkv, d_v, scale)
+    width = d_qk if mla else Hkv * max(d_qk, d_v)
+    es = kc.element_size()
+    for pitch in (tsv.kv_row_pitch(width, es), width + 48 // es):
+        kc2, kt2 = _pitched_copy(kc, pitch), _pitched_copy(kt, pitch)
+        vc2, vt2 = (kc2, kt2) if mla else (_pitched_copy(vc, pitch), _pitched_copy(vt, pitch))
+        o, lse, _, _ = _run(q, kc2, vc2, kt2, vt2, pl, trees, Hkv, d_v, scale)
+        for b, t in enumerate(trees):
+            assert torch.equal(o[b, :t.n].view(torch.int16) if dtype == torch.bfloat16 else o[b, :t.n],
+                               o0[b, :t.n].view(torch.int16) if dtype == torch.bfloat16 else o0[b, :t.n])
+            assert torch.equal(lse[b, :t.n], l0[b, :t.n])
+        check_attention(o, lse, q, kc2, vc2, kt2, vt2, prefix, trees, scale, TOL[dtype], mla, d_v)
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_workload_recommended_pitch(cid):
+    """Full-size grouped workloads with rows at the recommended pitch: the
+    same bits as packed rows (whose values test_workload checks against the
+    oracle), and a seeded sample of nodes against the oracle."""
+    cfg = config(cid)
+    pitch = tsv.kv_row_pitch(cfg.Hkv * cfg.d_qk, 2)
+    print(f"attention workload {cid} {cfg.name}, row pitch {pitch}", flush=True)
+    dense = attention_inputs(cfg, 0, DEV)
+    ins = attention_inputs(cfg, 0, DEV, row_pitch=pitch)
+    assert ins["k_cache"].stride(1) == pitch
+    pl_np = ins["prefix_len"].cpu().numpy()
+    marg = marginals(cfg, 0, DEV).cpu().numpy()
+    _, _, trees = oracle_trees(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cfg.cost, pl_np)
+    runs = []
+    for st in (dense, ins):
+        runs.append(_run(st["q"], st["k_cache"], st["v_cache"], st["k_tree"], st["v_tree"],
+                         st["prefix_len"], trees, cfg.Hkv, cfg.d_v, cfg.sm_scale))
+    for b, t in enumerate(trees):
+        assert torch.equal(runs[0][0][b, :t.n].view(torch.int16), runs[1][0][b, :t.n].view(torch.int16))
+        assert torch.equal(runs[0][1][b, :t.n], runs[1][1][b, :t.n])
+    del dense
+    samples = _structured_samples(cid, trees, np.random.default_rng(cid + 100))[:64]
+    worst = check_attention(runs[1][0], runs[1][1], ins["q"], ins["k_cache"], ins["v_cache"],
+                            ins["k_tree"], ins["v_tree"], pl_np, trees, cfg.sm_scale,
+                            TOL[cfg.torch_dtype], cfg.mla, cfg.d_v, samples)
+    print(f"MARGIN workload {cid} {cfg.name} (row pitch {pitch}): max |gpu - oracle| = {worst:.3e} "
+          f"over {len(samples)} nodes", flush=True)

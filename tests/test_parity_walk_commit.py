@@ -121,13 +121,37 @@ def _commit_case(rng, B, L_cap, N_max, Hkv, d, gamma, mla, dtype):
     return kc, vc, kt, vt, pl, alen, nodes
 
 
+def _pitched(t, pitch, fill):
+    """A copy of t with rows `pitch` elements apart; the elements between rows
+    hold `fill`.  Returns the copy and a view of its whole storage."""
+    B, R = t.shape[:2]
+    out = tsv.kv_rows(B, R, tuple(t.shape[2:]), t.dtype, DEV, pitch)
+    full = out.as_strided((B, R, pitch), (R * pitch, pitch, 1))
+    full.fill_(fill)
+    out.copy_(t)
+    return out, full
+
+
+@pytest.mark.parametrize("pitched", [False, True])
 @pytest.mark.parametrize("mla", [False, True])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_commit_vs_oracle(mla, dtype):
+def test_commit_vs_oracle(mla, dtype, pitched):
     rng = np.random.default_rng(int(mla) * 2 + int(dtype == torch.float32))
     B, L_cap, N_max, Hkv, gamma = 6, 300, 20, 4, 5
     d = 576 if mla else 64
     kc, vc, kt, vt, pl, alen, nodes = _commit_case(rng, B, L_cap, N_max, Hkv, d, gamma, mla, dtype)
+    fulls = []
+    if pitched:
+        # rows further apart than their width: only the rows' own elements move
+        width = d if mla else Hkv * d
+        pitch = tsv.kv_row_pitch(width, kc.element_size())
+        if pitch == width:
+            pitch = width + 32 // kc.element_size()
+        kc, f = _pitched(kc, pitch, 7.0); fulls.append((f, width))
+        kt, f = _pitched(kt, pitch, 7.0); fulls.append((f, width))
+        if not mla:
+            vc, f = _pitched(vc, pitch, 7.0); fulls.append((f, width))
+            vt, f = _pitched(vt, pitch, 7.0); fulls.append((f, width))
     ref_k = np32(kc).copy()
     ref_v = None if mla else np32(vc).copy()
     ref_pl = pl.copy()
@@ -142,16 +166,21 @@ def test_commit_vs_oracle(mla, dtype):
     assert np.array_equal(np32(kc), ref_k)
     if not mla:
         assert np.array_equal(np32(vc), ref_v)
+    for f, width in fulls:
+        assert bool((f[:, :, width:] == 7.0).all()), "an element between rows was written"
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_chained_round(cid):
+@pytest.mark.parametrize("cid,pitched", [(1, False), (2, False), (3, False), (4, False), (5, False),
+                                         (2, True)])
+def test_chained_round(cid, pitched):
     """build_tree -> tree_verify_attn -> accept_walk -> commit_path on the GPU,
-    every output against the oracle (attention on a sample of nodes)."""
+    every output against the oracle (attention on a sample of nodes); once
+    with cache and scratch rows at the recommended pitch."""
     cfg = config(cid)
-    print(f"chained round workload {cid} {cfg.name}", flush=True)
+    pitch = tsv.kv_row_pitch(cfg.Hkv * cfg.d_qk, 2) if pitched else None
+    print(f"chained round workload {cid} {cfg.name}, row pitch {pitch}", flush=True)
     marg = marginals(cfg, 0, DEV)
-    ins = attention_inputs(cfg, 0, DEV)
+    ins = attention_inputs(cfg, 0, DEV, row_pitch=pitch)
     pl_np = ins["prefix_len"].cpu().numpy().copy()
     g = tsv.build_tree_topk(marg, cfg.top_k, cfg.n_budget, cfg.N_max, cost=cfg.cost,
                             prefix_len=ins["prefix_len"] if cfg.cost else None)

@@ -19,10 +19,13 @@ from ._lib import (  # noqa: F401
     build_tree_topk,
     expanded_rows,
     fit_cost,
+    kv_row_pitch,
+    kv_rows,
     commit_path,
     compress_chains,
     lib,
     refresh_compressed,
+    row_layout,
     select_global_budget,
     status_string,
     tsv_cost,

@@ -123,6 +123,66 @@ def _dev(t: torch.Tensor, what: str, dtype=None):
     return t
 
 
+def _rows(t: torch.Tensor, what: str, dtype=None) -> int:
+    """A device cache or scratch tensor laid out as row_layout() describes;
+    returns its pitch."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    return row_layout(t, what)
+
+
+def row_layout(t: torch.Tensor, what: str = "tensor") -> int:
+    """Checks that a cache or scratch tensor [B, R, ...] has its per-row
+    block (the trailing dims) dense, rows `pitch` elements apart and batches
+    R rows apart (the layout the C ABI's row stride describes); returns the
+    pitch."""
+    if t.dim() < 3:
+        raise ValueError(f"{what} must be [B, rows, ...]")
+    width = 1
+    for d in range(t.dim() - 1, 1, -1):
+        if t.shape[d] > 1 and t.stride(d) != width:
+            raise ValueError(f"{what}: the row block must be dense")
+        width *= t.shape[d]
+    pitch = t.stride(1)
+    if pitch < width or (t.shape[0] > 1 and t.stride(0) != t.shape[1] * pitch):
+        raise ValueError(f"{what}: rows must be {width} or more elements apart and the "
+                         "batches one row count apart")
+    return pitch
+
+
+def kv_row_pitch(width: int, element_size: int) -> int:
+    """Elements between token rows for a cache whose rows hold `width`
+    elements of `element_size` bytes: the row rounded up to whole 128-byte
+    lines, plus one line when that gives an even number of lines.  With an
+    even number of lines every row puts a given KV head at the same low
+    address bits, and on MI355X the heads at some of those offsets stream
+    measurably more slowly (the grouped workload's attention takes about
+    10 % longer); an odd number of lines rotates every head over them."""
+    lines = -(-int(width) * int(element_size) // 128)
+    if lines % 2 == 0:
+        lines += 1
+    return lines * 128 // int(element_size)
+
+
+def kv_rows(B: int, R: int, row_shape, dtype: torch.dtype, device, pitch: Optional[int] = None,
+            zero: bool = True) -> torch.Tensor:
+    """A [B, R, *row_shape] view whose rows are `pitch` elements apart
+    (kv_row_pitch by default), for caches and scratch rows."""
+    row_shape = tuple(int(x) for x in row_shape)
+    width = 1
+    for x in row_shape:
+        width *= x
+    es = torch.empty((), dtype=dtype).element_size()
+    pitch = kv_row_pitch(width, es) if pitch is None else int(pitch)
+    if pitch < width:
+        raise ValueError("pitch smaller than the row")
+    alloc = torch.zeros if zero else torch.empty
+    base = alloc((B, R, pitch), dtype=dtype, device=device)
+    return base[:, :, :width].view((B, R) + row_shape)
+
+
 def dtype_code(dt: torch.dtype) -> int:
     if dt == torch.float32:
         return TSV_F32
@@ -414,17 +474,17 @@ def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     """q [B, N_max, Hq, d_qk]; caches [B, L_cap, ...]; scratch [B, N_max, ...].
     A latent cache passes the same tensor as k_cache and v_cache.
     Returns (out [B, N_max, Hq, d_v], lse fp32 [B, N_max, Hq] or None)."""
-    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
-                  (k_tree, "k_tree"), (v_tree, "v_tree")):
-        _dev(t, nm, q.dtype)
+    _dev(q, "q")
+    pitches = {_rows(t, nm, q.dtype) for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache"),
+                                                   (k_tree, "k_tree"), (v_tree, "v_tree"))}
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(n_nodes, "n_nodes", torch.int32)
     _dev(anc_bits, "anc_bits")
     B, N_max, Hq, d_qk = q.shape
     L_cap = k_cache.shape[1]
-    stride = k_cache.stride(1)
-    if v_cache.stride(1) != stride or k_tree.stride(1) != stride or v_tree.stride(1) != stride:
-        raise ValueError("caches and scratch must share one row stride")
+    if len(pitches) != 1:
+        raise ValueError("caches and scratch must share one row pitch")
+    stride = pitches.pop()
     dev = q.device
     if out is None:
         out = torch.empty(B, N_max, Hq, d_v, dtype=q.dtype, device=dev)
@@ -474,14 +534,15 @@ def commit_path(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
                 status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Latent caches pass v_cache = v_tree = None.  Updates k_cache, v_cache
     and prefix_len in place; returns status int32 [B]."""
-    _dev(k_cache, "k_cache")
-    _dev(k_tree, "k_tree", k_cache.dtype)
+    pitches = {_rows(k_cache, "k_cache"), _rows(k_tree, "k_tree", k_cache.dtype)}
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(accept_len, "accept_len", torch.int32)
     _dev(accept_nodes, "accept_nodes", torch.int32)
     if v_cache is not None:
-        _dev(v_cache, "v_cache", k_cache.dtype)
-        _dev(v_tree, "v_tree", k_cache.dtype)
+        pitches |= {_rows(v_cache, "v_cache", k_cache.dtype), _rows(v_tree, "v_tree", k_cache.dtype)}
+    if len(pitches) != 1:
+        raise ValueError("caches and scratch must share one row pitch")
+    pitch = pitches.pop()
     B, L_cap = k_cache.shape[:2]
     N_max = k_tree.shape[1]
     gamma = accept_nodes.shape[1]
@@ -490,7 +551,7 @@ def commit_path(k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
         status = torch.empty(B, dtype=torch.int32, device=dev)
     code = lib().commit_path(
         _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree),
-        k_cache.stride(1), _ptr(accept_len), _ptr(accept_nodes), B, N_max, L_cap, Hkv,
+        pitch, _ptr(accept_len), _ptr(accept_nodes), B, N_max, L_cap, Hkv,
         d_k, d_v, gamma, dtype_code(k_cache.dtype), _ptr(status), _stream(dev))
     _check("commit_path", code)
     return status

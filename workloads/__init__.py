@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     Cost,
     ExpandConfig,
     attention_inputs,
+    pitched,
     config,
     drafter_logits,
     expand_config,

@@ -244,23 +244,36 @@ def node_distributions(cfg: ExpandConfig, seed: int = 0, device="cpu") -> torch.
     return out
 
 
-def attention_inputs(cfg: Config, seed: int = 0, device="cpu") -> dict:
+def pitched(B: int, R: int, row_shape, dtype, device, pitch: Optional[int] = None) -> torch.Tensor:
+    """Zeros of shape [B, R, *row_shape] whose rows lie `pitch` elements apart
+    (dense when pitch is None); the elements between rows are never used."""
+    width = int(np.prod(row_shape))
+    if pitch is None or pitch == width:
+        return torch.zeros((B, R) + tuple(row_shape), dtype=dtype, device=device)
+    if pitch < width:
+        raise ValueError("row pitch smaller than the row")
+    base = torch.zeros((B, R, pitch), dtype=dtype, device=device)
+    return base[:, :, :width].view((B, R) + tuple(row_shape))
+
+
+def attention_inputs(cfg: Config, seed: int = 0, device="cpu", row_pitch: Optional[int] = None) -> dict:
     """Queries, persistent caches, scratch (tree) KV and prefix lengths.
 
     GQA layout: q [B, N_max, Hq, d_qk]; k_cache/v_cache [B, L_cap, Hkv, d];
     k_tree/v_tree [B, N_max, Hkv, d].  Latent layout: k_cache [B, L_cap, d_qk]
     with v_cache the same tensor (values are its first d_v columns); likewise
-    k_tree/v_tree.
+    k_tree/v_tree.  Cache and scratch rows lie `row_pitch` elements apart
+    (dense by default); the values do not depend on it.
     """
     dt = cfg.torch_dtype
     pl = prefix_lengths(cfg, seed)
     B, L, N = cfg.B, cfg.L_cap, cfg.N_max
     row = (cfg.d_qk,) if cfg.mla else (cfg.Hkv, cfg.d_qk)
     q = torch.empty((B, N, cfg.Hq, cfg.d_qk), dtype=dt, device=device)
-    kc = torch.zeros((B, L) + row, dtype=dt, device=device)
-    kt = torch.empty((B, N) + row, dtype=dt, device=device)
-    vc = kc if cfg.mla else torch.zeros((B, L, cfg.Hkv, cfg.d_v), dtype=dt, device=device)
-    vt = kt if cfg.mla else torch.empty((B, N, cfg.Hkv, cfg.d_v), dtype=dt, device=device)
+    kc = pitched(B, L, row, dt, device, row_pitch)
+    kt = pitched(B, N, row, dt, device, row_pitch)
+    vc = kc if cfg.mla else pitched(B, L, (cfg.Hkv, cfg.d_v), dt, device, row_pitch)
+    vt = kt if cfg.mla else pitched(B, N, (cfg.Hkv, cfg.d_v), dt, device, row_pitch)
     for b in range(B):
         lb = int(pl[b])
         q[b] = _randn(q.shape[1:], seed, cfg, _T_Q, b, device).to(dt)
