@@ -74,6 +74,11 @@ CASES = [
     ("bf16_n128_prefix0", 1, 128, 4, 1, 128, 128, torch.bfloat16, [0], [128], False),
     # ~313 splits of 16 keys: several groups of 64 in the combine, two column passes of d_v 72
     ("fp32_dv72_many_splits", 1, 8, 2, 2, 72, 72, torch.float32, [5000], [8], False),
+    # 128 units x 4 splits = 512 workgroups, two per compute unit: long units take the
+    # first-dispatched / second-dispatched key shares, short ones equal chunks
+    ("bf16_gqa_paired_splits", 16, 32, 32, 8, 128, 128, torch.bfloat16,
+     [2100, 2000, 1500, 1200, 900, 500, 64, 1, 2100, 1800, 1000, 0, 2050, 1300, 700, 2100],
+     [32, 32, 17, 5, 32, 1, 0, 32, 32, 20, 32, 8, 32, 32, 3, 32], False),
 ]
 
 
@@ -352,7 +357,8 @@ def _pitched_copy(t, pitch):
     return out
 
 
-PITCH_CASES = ["fp32_mha", "bf16_gqa_g4", "bf16_latent_mfma", "bf16_valu_d64", "bf16_many_splits"]
+PITCH_CASES = ["fp32_mha", "bf16_gqa_g4", "bf16_latent_mfma", "bf16_valu_d64", "bf16_many_splits",
+               "bf16_gqa_paired_splits"]
 
 
 @pytest.mark.parametrize("name", PITCH_CASES)

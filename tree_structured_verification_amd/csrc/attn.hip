@@ -323,15 +323,39 @@ __device__ __forceinline__ void wait_later(int later) {
 // of one unit, so a unit's splits run side by side and share that XCD's L2,
 // where the last one to finish reads the others' partials.  A unit is (row
 // block, request, KV head), in that order of significance.
+//
+// A launch of exactly two workgroups per compute unit (512) is resident at
+// once, and workgroup id i shares its compute unit with id i + 256.  The
+// first-dispatched of the two is served first and, on equal work, ends its
+// loop about 17 % earlier (measured on the grouped workload: 41 against 49
+// us).  Such a launch gives each unit's first S/2 splits to first-dispatched
+// slots and 57 % of its keys, the other S/2 splits to the second slots and
+// the rest, so that both workgroups of a compute unit end together.  Split
+// boundaries depend only on the unit's key count, never on timing.
+constexpr int kResidentGrid = 512;
+constexpr int kFirstShareNum = 57, kFirstShareDen = 100;
+
 __device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& unit) {
   const int id = static_cast<int>(blockIdx.x);
   const int slot = id >> 3;
+  const int per_xcd = static_cast<int>(gridDim.x) >> 3;
+  const bool paired = static_cast<int>(gridDim.x) == kResidentGrid && (a.S & 1) == 0;
+  const int hs = a.S >> 1;
+  int grp, split;
+  if (paired) {
+    const int half = per_xcd >> 1;
+    const bool first = slot < half;
+    const int s_in = first ? slot : slot - half;
+    grp = s_in / hs;
+    split = s_in % hs + (first ? 0 : hs);
+  } else {
+    grp = slot / a.S;
+    split = slot % a.S;
+  }
   // consecutive groups of 8 units rotate over the XCDs, so that every XCD
   // streams every KV head (the units of a group are the KV heads of one
   // request and row block)
-  const int grp = slot / a.S;
   unit = grp * 8 + (((id & 7) + grp) & 7);
-  const int split = slot % a.S;
   if (unit >= a.units) return false;
   // units are numbered row block first: the first row block of every
   // (request, KV head) comes before any second one, so the work of short
@@ -346,6 +370,23 @@ __device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& u
   c.rows_b = c.n_b * a.G;
   if (c.rowb * 128 >= c.rows_b) return false;
   c.keys_b = c.l_b + c.n_b;
+  if (paired) {
+    // first-dispatched splits: keys [0, ka) in hs chunks of ca; the others:
+    // [ka, keys_b) in hs chunks of cb (multiples of 32 keys); used when
+    // every split keeps at least a.chunk keys
+    const int ka = static_cast<int>(static_cast<long long>(c.keys_b) * kFirstShareNum / kFirstShareDen) / 32 * 32;
+    const int ca = ((ka + hs - 1) / hs + 31) / 32 * 32;
+    const int cb = ((c.keys_b - ka + hs - 1) / hs + 31) / 32 * 32;
+    const bool fits = ka >= hs * a.chunk && c.keys_b - ka >= hs * a.chunk && (hs - 1) * ca < ka &&
+                      (hs - 1) * cb < c.keys_b - ka;
+    if (fits) {
+      c.splits = a.S;
+      c.split = split;
+      c.k_beg = split < hs ? split * ca : ka + (split - hs) * cb;
+      c.k_end = split < hs ? min(ka, c.k_beg + ca) : min(c.keys_b, c.k_beg + cb);
+      return true;
+    }
+  }
   // the unit's keys in S nearly equal chunks (a multiple of 32 keys, at least
   // a.chunk keys), so that the splits stay busy however short the prefix
   int chunk = (c.keys_b + a.S - 1) / a.S;
