@@ -88,10 +88,10 @@ ATTN_SOURCE = os.path.join(ROOT, "tree_structured_verification_amd", "csrc", "at
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tree_verify_attn_gqa_bf16_traffic.md")
 
 
-def measured_traffic():
+def measured_traffic(kv_row_bytes):
     """HBM bytes per attention launch from the committed counter summary, or
     None when it is missing or was taken on another version of the kernel
-    source (the summary records the source's SHA-256)."""
+    source or another cache row pitch (the summary records both)."""
     import hashlib
     try:
         text = open(TRAFFIC_PROFILE).read()
@@ -103,7 +103,7 @@ def measured_traffic():
             k, v = ln.strip()[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
     digest = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    if fields.get("attn_source_sha256") != digest:
+    if fields.get("attn_source_sha256") != digest or fields.get("kv_row_bytes") != str(kv_row_bytes):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -477,6 +477,26 @@ def copy_peak_gbs(dev, mib=1024, reps=8):
     return 2.0 * nb / best / 1e9
 
 
+def read_peak_gbs(dev, mib=1024, reps=8):
+    """Measured read-only bandwidth: torch's int64 sum over `mib` MiB (far
+    larger than the 256 MB last-level cache; its float reductions are slower
+    than the memory), the best of `reps` calls."""
+    nb = mib << 20
+    x = torch.ones(nb // 8, dtype=torch.int64, device=dev)
+    x.sum()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    stream = torch.cuda.current_stream(dev)
+    for a, b in ev:
+        a.record(stream)
+        x.sum()
+        b.record(stream)
+    torch.cuda.synchronize()
+    best = min(a.elapsed_time(b) for a, b in ev) / 1e3
+    del x
+    return nb / best / 1e9
+
+
 def gemm_peak_tflops(dev, n=8192, reps=5):
     """Measured dense bf16 matrix throughput of the vendor GEMM (torch.matmul,
     n x n x n), the best of `reps` calls."""
@@ -778,9 +798,10 @@ def cpu_baseline(res, cores, one_thread=True):
     return out
 
 
-def attention_roofline(res, copy_gbs, gemm_tflops):
+def attention_roofline(res, copy_gbs, gemm_tflops, read_gbs=None):
     """Roofline of the attention launch: HBM for the grouped workloads, the
-    bf16 matrix peak for the latent ones; also against the measured peaks."""
+    bf16 matrix peak for the latent ones; also against the measured peaks
+    (device copy and, for HBM, a read-only stream)."""
     cfg = res["cfg"]
     t = res["attn_s"]
     if cfg.mla:
@@ -791,9 +812,13 @@ def attention_roofline(res, copy_gbs, gemm_tflops):
                 "frac_of_measured": round(a / gemm_tflops, 4),
                 "algorithmic_flops": res["attn_flops"]}
     a = res["attn_bytes"] / t / 1e9
-    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(a / HBM_PEAK_GBS, 4), "measured_peak": round(copy_gbs, 1),
-            "frac_of_measured": round(a / copy_gbs, 4), "algorithmic_bytes": res["attn_bytes"]}
+    r = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(a / HBM_PEAK_GBS, 4), "measured_peak": round(copy_gbs, 1),
+         "frac_of_measured": round(a / copy_gbs, 4), "algorithmic_bytes": res["attn_bytes"]}
+    if read_gbs:
+        r["measured_read_peak"] = round(read_gbs, 1)
+        r["frac_of_read_peak"] = round(a / read_gbs, 4)
+    return r
 
 
 def workload_desc(cfg):
@@ -809,7 +834,7 @@ def workload_desc(cfg):
             f"top-{cfg.top_k}, {bud}, {cfg.dtype}")
 
 
-def workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu):
+def workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu, read_gbs=None):
     cfg = res["cfg"]
     e = {"workload": workload_desc(cfg), "steps": res["K"], "round_us": round(res["round_us"], 1),
          "tokens_per_s": round(res["value"], 1),
@@ -817,7 +842,7 @@ def workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu):
          "tree_tokens": res["tokens"], "input_copies": res["copies"],
          "kv_row_bytes": res["kv_row_bytes"],
          "kernel_us": {k: round(v * 1e3, 1) for k, v in res["kernel_ms"].items()},
-         "attention": attention_roofline(res, copy_gbs, gemm_tflops)}
+         "attention": attention_roofline(res, copy_gbs, gemm_tflops, read_gbs)}
     if with_cpu:
         print(f"[bench] timing the CPU oracle on {cfg.name}", file=sys.stderr, flush=True)
         e["cpu_baseline"] = cpu_baseline(res, cores)
@@ -900,16 +925,17 @@ def main():
 
     print(f"[bench] device {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
     copy_gbs = copy_peak_gbs(dev)
+    read_gbs = read_peak_gbs(dev)
     gemm_tflops = gemm_peak_tflops(dev)
-    print(f"[bench] measured copy {copy_gbs:.0f} GB/s, bf16 GEMM {gemm_tflops:.0f} TFLOP/s",
-          file=sys.stderr, flush=True)
+    print(f"[bench] measured copy {copy_gbs:.0f} GB/s, read {read_gbs:.0f} GB/s, "
+          f"bf16 GEMM {gemm_tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
     cores = cpu_cores()
     with_cpu = not args.no_cpu_baseline
 
     head = round_bench(args.workload, args.steps, args.warmup, dev)
     cfg = head["cfg"]
-    roof = attention_roofline(head, copy_gbs, gemm_tflops)
-    roof["traffic"] = measured_traffic() if cfg.id == WORKLOAD else None
+    roof = attention_roofline(head, copy_gbs, gemm_tflops, read_gbs)
+    roof["traffic"] = measured_traffic(head["kv_row_bytes"]) if cfg.id == WORKLOAD else None
     roof["kernel"] = "tree_verify_attn"
     line = {
         "metric": "verified tree tokens/s per GPU",
@@ -931,14 +957,15 @@ def main():
         "accepted_tokens_per_s": round(head["accepted_per_s"], 1),
         "kernel_ms": {k: round(v, 4) for k, v in head["kernel_ms"].items()},
         "roofline": roof,
-        "measured_peaks": {"copy_gbs": round(copy_gbs, 1), "gemm_bf16_tflops": round(gemm_tflops, 1)},
+        "measured_peaks": {"copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
+                           "gemm_bf16_tflops": round(gemm_tflops, 1)},
     }
     if with_cpu:
         print(f"[bench] timing the CPU oracle on {cfg.name}", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(head, cores)
     per = {}
     if not args.no_per_workload:
-        per[cfg.name] = workload_entry(head, copy_gbs, gemm_tflops, cores, False)
+        per[cfg.name] = workload_entry(head, copy_gbs, gemm_tflops, cores, False, read_gbs)
         if with_cpu:
             per[cfg.name]["cpu_baseline"] = line["cpu_baseline"]
     free(head)
@@ -948,7 +975,7 @@ def main():
                 continue
             K, W = PER_WORKLOAD_STEPS[wid]
             res = round_bench(wid, K, W, dev)
-            per[res["cfg"].name] = workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu)
+            per[res["cfg"].name] = workload_entry(res, copy_gbs, gemm_tflops, cores, with_cpu, read_gbs)
             free(res)
         line["per_workload"] = per
     print(json.dumps(line), flush=True)
