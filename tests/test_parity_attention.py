@@ -79,6 +79,11 @@ CASES = [
     ("bf16_gqa_paired_splits", 16, 32, 32, 8, 128, 128, torch.bfloat16,
      [2100, 2000, 1500, 1200, 900, 500, 64, 1, 2100, 1800, 1000, 0, 2050, 1300, 700, 2100],
      [32, 32, 17, 5, 32, 1, 0, 32, 32, 20, 32, 8, 32, 32, 3, 32], False),
+    # 384 units x 3 splits = 1152 work items (more than resident): no split shorter than
+    # 4096 keys, so ragged units take one, two or three splits
+    ("bf16_gqa_split_floor", 48, 16, 32, 8, 128, 128, torch.bfloat16,
+     [int(x) for x in np.random.default_rng(7).integers(100, 9001, 48)],
+     [int(x) for x in np.random.default_rng(8).integers(0, 17, 48)], False),
 ]
 
 

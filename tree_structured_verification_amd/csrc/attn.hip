@@ -334,6 +334,7 @@ __device__ __forceinline__ void wait_later(int later) {
 // boundaries depend only on the unit's key count, never on timing.
 constexpr int kResidentGrid = 512;
 constexpr int kFirstShareNum = 57, kFirstShareDen = 100;
+constexpr int kPairedMinChunk = 256;
 
 __device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& unit) {
   const int id = static_cast<int>(blockIdx.x);
@@ -373,12 +374,12 @@ __device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& u
   if (paired) {
     // first-dispatched splits: keys [0, ka) in hs chunks of ca; the others:
     // [ka, keys_b) in hs chunks of cb (multiples of 32 keys); used when
-    // every split keeps at least a.chunk keys
+    // every split keeps at least kPairedMinChunk keys
     const int ka = static_cast<int>(static_cast<long long>(c.keys_b) * kFirstShareNum / kFirstShareDen) / 32 * 32;
     const int ca = ((ka + hs - 1) / hs + 31) / 32 * 32;
     const int cb = ((c.keys_b - ka + hs - 1) / hs + 31) / 32 * 32;
-    const bool fits = ka >= hs * a.chunk && c.keys_b - ka >= hs * a.chunk && (hs - 1) * ca < ka &&
-                      (hs - 1) * cb < c.keys_b - ka;
+    const bool fits = ka >= hs * kPairedMinChunk && c.keys_b - ka >= hs * kPairedMinChunk &&
+                      (hs - 1) * ca < ka && (hs - 1) * cb < c.keys_b - ka;
     if (fits) {
       c.splits = a.S;
       c.split = split;
@@ -387,8 +388,10 @@ __device__ __forceinline__ bool fused_item(const AttnArgs& a, ItemCtx& c, int& u
       return true;
     }
   }
-  // the unit's keys in S nearly equal chunks (a multiple of 32 keys, at least
-  // a.chunk keys), so that the splits stay busy however short the prefix
+  // the unit's keys in S nearly equal chunks (a multiple of 32 keys), but
+  // none shorter than a.chunk, the chunk of the longest possible unit: a
+  // short unit takes fewer splits rather than shorter ones, each of which
+  // would cost a published partial and its read-back
   int chunk = (c.keys_b + a.S - 1) / a.S;
   chunk = (chunk + 31) / 32 * 32;
   chunk = chunk > a.chunk ? chunk : a.chunk;
@@ -1774,7 +1777,17 @@ AttnPlan attn_plan(const AttnShape& sh, bool aligned, bool shared_value) {
     // long prefixes cut: at least one split per kSplitKeys keys.
     const long long s_len = (keys_max + kSplitKeys - 1) / kSplitKeys;
     if (p.S < s_len) p.S = static_cast<int>(s_len);
-    p.chunk = p.min_chunk;  // the device cuts each unit's actual keys into S chunks of at least this
+    // the device cuts each unit's actual keys into S chunks, none shorter
+    // than the longest possible unit's (at least min_chunk); with many more
+    // work items than resident workgroups (the dispatcher then balances the
+    // compute units), none shorter than kSplitKeys either, so that a short
+    // unit takes fewer splits and fewer partials to publish and read back
+    // (measured on the ragged 64-request workload: floors of 3.5k-3.8k keys
+    // 407-410 us, 4k-4.5k keys 392-395 us, 5k keys and more 405-430 us)
+    p.chunk = static_cast<int>((keys_max + p.S - 1) / p.S + p.KT - 1) / p.KT * p.KT;
+    if (p.chunk < p.min_chunk) p.chunk = p.min_chunk;
+    if (static_cast<long long>(units_pad) * p.S > 2LL * kResidentGrid && p.chunk < kSplitKeys)
+      p.chunk = static_cast<int>(kSplitKeys);
     p.items_max = units_pad * p.S;
     size_t off = cnt_bytes;
     p.off_info = p.off_desc = off;
