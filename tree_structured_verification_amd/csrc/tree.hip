@@ -79,7 +79,7 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
 constexpr int kShl1 = 0x130;  // lane l takes lane l + 1 (lane 63 takes the fill)
 constexpr int kShr1 = 0x138;  // lane l takes lane l - 1 (lane 0 takes the fill)
 
-template <int SL, bool PER_NODE>
+template <int SL, bool PER_NODE, bool ADAPTIVE>
 __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   __shared__ float s_p[kMaxTopkTable];
   __shared__ int s_i[kMaxTopkTable];
@@ -163,9 +163,9 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     insert(frontier_key(r0, 1, -1, 0), 0);
   }
 
-  const double l = a.adaptive ? static_cast<double>(a.prefix_len[b]) : 0.0;
+  const double l = ADAPTIVE ? static_cast<double>(a.prefix_len[b]) : 0.0;
   double phi = 0.0;
-  double theta = a.adaptive ? __ddiv_rn(1.0, round_cost(a.cost, 0, l)) : 0.0;
+  double theta = ADAPTIVE ? __ddiv_rn(1.0, round_cost(a.cost, 0, l)) : 0.0;
 
   int m = 0;
   while (m < a.cap) {
@@ -184,12 +184,13 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     const float q_sib = rank + 1 < a.k ? s_p[row * a.k + rank + 1] : 0.f;
     float q_kid = 0.f;
     if (dep < a.gamma) q_kid = PER_NODE ? s_p[kid_row * a.k] : readlane_f32(q_first, dep);
-    if (a.adaptive) {
-      const double phi2 = __dadd_rn(phi, static_cast<double>(sc));
-      const double th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, m + 1, l));
-      if (!(th2 > theta)) break;  // marginal gain not positive
-      phi = phi2;
-      theta = th2;
+    // The stop rule is evaluated here but decided after this pop's inserts
+    // (a stop discards them and the record below), so that its fp64
+    // arithmetic overlaps the inserts instead of preceding them.
+    double phi2 = 0.0, th2 = 0.0;
+    if constexpr (ADAPTIVE) {
+      phi2 = __dadd_rn(phi, static_cast<double>(sc));
+      th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, m + 1, l));
     }
     if (lane == 0) {
       n_par[m] = par;
@@ -206,6 +207,11 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     if (dep < a.gamma) {
       const float v = __fmul_rn(sc, q_kid);
       insert(frontier_key(v, dep + 1, m, 0), kid_row);
+    }
+    if constexpr (ADAPTIVE) {
+      if (!(th2 > theta)) break;  // marginal gain not positive
+      phi = phi2;
+      theta = th2;
     }
     ++m;
   }
@@ -246,18 +252,26 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 }  // namespace
 
 hipError_t launch_best_first(const TreeArgs& a, hipStream_t s) {
-  // sorted frontier of 64 or 128 places (at least cap)
+  // sorted frontier of 64 or 128 places (at least cap); the stop rule only
+  // in the adaptive instances
+  const dim3 g(a.B), blk(64);
+#define TSV_BF(SL, PN)                                                   \
+  if (a.adaptive) best_first_kernel<SL, PN, true><<<g, blk, 0, s>>>(a);  \
+  else best_first_kernel<SL, PN, false><<<g, blk, 0, s>>>(a);
   if (a.per_node) {
-    if (a.cap <= 64)
-      best_first_kernel<1, true><<<dim3(a.B), dim3(64), 0, s>>>(a);
-    else
-      best_first_kernel<2, true><<<dim3(a.B), dim3(64), 0, s>>>(a);
+    if (a.cap <= 64) {
+      TSV_BF(1, true)
+    } else {
+      TSV_BF(2, true)
+    }
   } else {
-    if (a.cap <= 64)
-      best_first_kernel<1, false><<<dim3(a.B), dim3(64), 0, s>>>(a);
-    else
-      best_first_kernel<2, false><<<dim3(a.B), dim3(64), 0, s>>>(a);
+    if (a.cap <= 64) {
+      TSV_BF(1, false)
+    } else {
+      TSV_BF(2, false)
+    }
   }
+#undef TSV_BF
   return hipGetLastError();
 }
 
