@@ -167,6 +167,17 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   double phi = 0.0;
   double theta = ADAPTIVE ? __ddiv_rn(1.0, round_cost(a.cost, 0, l)) : 0.0;
 
+  // Popped nodes' records stay in registers during the pops (node m at lane
+  // m % 64 of slot m / 64; a parent's score is one readlane away) and go to
+  // LDS once afterwards, so no pop waits on an LDS store or load of them.
+  float r_sc[SL];
+  int r_par[SL], r_dep[SL], r_rank[SL], r_row[SL];
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    r_sc[s] = 0.f;
+    r_par[s] = r_dep[s] = r_rank[s] = r_row[s] = 0;
+  }
+
   int m = 0;
   while (m < a.cap) {
     const uint64_t hk = readlane_u64(fk[0], 0);
@@ -176,14 +187,19 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     const int par = 255 - static_cast<int>((wl >> 7) & 255) - 1;
     const int dep = 63 - static_cast<int>((wl >> 15) & 63) + 1;
     const float sc = key_score(hk);
-    const float ps = par >= 0 ? n_sc[par] : 1.0f;   // the parent was popped earlier
     // list of the popped node's token (shared with its siblings) and the
     // list its children come from
     const int row = PER_NODE ? __builtin_amdgcn_readlane(frw[0], 0) : dep - 1;
     const int kid_row = PER_NODE ? a.k * row + 1 + rank : dep;
+    // the sibling's table read is issued first and lands while the child
+    // (built from registers alone, per position) is inserted
     const float q_sib = rank + 1 < a.k ? s_p[row * a.k + rank + 1] : 0.f;
     float q_kid = 0.f;
     if (dep < a.gamma) q_kid = PER_NODE ? s_p[kid_row * a.k] : readlane_f32(q_first, dep);
+    // the parent was popped earlier: its score from the registers
+    const float ps0 = readlane_f32(r_sc[0], par & 63);
+    const float ps1 = readlane_f32(r_sc[SL - 1], par & 63);
+    const float ps = par < 0 ? 1.0f : (par < 64 ? ps0 : ps1);
     // The stop rule is evaluated here but decided after this pop's inserts
     // (a stop discards them and the record below), so that its fp64
     // arithmetic overlaps the inserts instead of preceding them.
@@ -192,21 +208,25 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       phi2 = __dadd_rn(phi, static_cast<double>(sc));
       th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, m + 1, l));
     }
-    if (lane == 0) {
-      n_par[m] = par;
-      n_dep[m] = dep;
-      n_rank[m] = rank;
-      if constexpr (PER_NODE) n_row[m] = row;
-      n_sc[m] = sc;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      if (s == (m >> 6)) {
+        const bool me = lane == (m & 63);
+        r_sc[s] = me ? sc : r_sc[s];
+        r_par[s] = me ? par : r_par[s];
+        r_dep[s] = me ? dep : r_dep[s];
+        r_rank[s] = me ? rank : r_rank[s];
+        if constexpr (PER_NODE) r_row[s] = me ? row : r_row[s];
+      }
     }
     drop_front();
-    if (rank + 1 < a.k) {
-      const float v = __fmul_rn(ps, q_sib);
-      insert(frontier_key(v, dep, par, rank + 1), row);
-    }
     if (dep < a.gamma) {
       const float v = __fmul_rn(sc, q_kid);
       insert(frontier_key(v, dep + 1, m, 0), kid_row);
+    }
+    if (rank + 1 < a.k) {
+      const float v = __fmul_rn(ps, q_sib);
+      insert(frontier_key(v, dep, par, rank + 1), row);
     }
     if constexpr (ADAPTIVE) {
       if (!(th2 > theta)) break;  // marginal gain not positive
@@ -216,6 +236,17 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     ++m;
   }
   const int n = m;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const int i = s * 64 + lane;
+    if (i < n) {
+      n_par[i] = r_par[s];
+      n_dep[i] = r_dep[s];
+      n_rank[i] = r_rank[s];
+      if constexpr (PER_NODE) n_row[i] = r_row[s];
+      n_sc[i] = r_sc[s];
+    }
+  }
   __syncthreads();
 
   const int W = (a.N_max + 31) >> 5;
