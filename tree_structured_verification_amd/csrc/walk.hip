@@ -134,15 +134,40 @@ __global__ __launch_bounds__(64) void walk_kernel(
   const int b = blockIdx.x, lane = threadIdx.x;
   const int n = clampi(n_nodes[b], 0, N_max);
   const int rows_per_b = N_max + 1;
+  // every load of this lane in flight together: the tree (at most 128
+  // nodes, two per lane) and eight segment keys of each row at a time
+  int par2[2], tok2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    par2[h] = i < n ? parent[static_cast<size_t>(b) * N_max + i] : 0;
+    tok2[h] = i < n ? token[static_cast<size_t>(b) * N_max + i] : 0;
+  }
+  // the first eight segment keys of the lane's first row go with them
+  // (usually all of them: the walk then waits once)
+  uint64_t v0[8];
+  const uint64_t* src0 = seg_best + (static_cast<size_t>(b) * rows_per_b + lane) * nseg;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v0[u] = lane <= n && u < nseg ? src0[u] : 0;
   for (int r = lane; r <= n; r += 64) {
     const uint64_t* src = seg_best + (static_cast<size_t>(b) * rows_per_b + r) * nseg;
     uint64_t best = 0;
-    for (int s = 0; s < nseg; ++s) best = umax64(best, src[s]);
+    for (int s0 = 0; s0 < nseg; s0 += 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = r == lane && s0 == 0 ? v0[u] : (s0 + u < nseg ? src[s0 + u] : 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) best = umax64(best, v[u]);
+    }
     s_arg[r] = best ? static_cast<int>(sel_key_index(best)) : -1;
   }
-  for (int i = lane; i < n; i += 64) {
-    s_par[i] = parent[static_cast<size_t>(b) * N_max + i];
-    s_tok[i] = token[static_cast<size_t>(b) * N_max + i];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    if (i < n) {
+      s_par[i] = par2[h];
+      s_tok[i] = tok2[h];
+    }
   }
   __syncthreads();
 
