@@ -491,6 +491,19 @@ size_t tsv_workspace_size(int which, int B, int gamma, int V, int top_k,
 /* Static description of a status code. */
 const char* tsv_status_string(int code);
 
+/* Diagnostic switch for the tree selection of build_tree, build_tree_topk,
+ * build_tree_fitted and build_tree_noalloc (per-position lists; the
+ * cost-aware page, "Methodology", item 2).  Two exact methods compute the
+ * same best-first tree: serial pops (one per node) and a level-by-level
+ * merge; by default (method 0) both run side by side in each request's
+ * workgroup and the first to finish writes the tree.  Method 1 runs the
+ * serial pops only, method 2 the level merge only; every method returns
+ * the same bits.  Process-wide (every device), read when a call is
+ * launched; not synchronised with calls in flight on other host threads.
+ * Returns the previous method, or TSV_EINVAL (setting unchanged) for a
+ * method outside 0..2. */
+int tsv_set_tree_method(int method);
+
 #ifdef __cplusplus
 }
 #endif

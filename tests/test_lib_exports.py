@@ -25,7 +25,7 @@ def test_all_declared_symbols_exported():
                             "build_tree_expand", "tree_verify_attn", "accept_walk",
                             "commit_path", "select_global_budget", "tsv_fit_cost",
                             "tsv_workspace_size", "tsv_status_string", "unfold_chains",
-                            "compress_chains", "refresh_compressed"])
+                            "compress_chains", "refresh_compressed", "tsv_set_tree_method"])
     lib = ctypes.CDLL(tsv._lib.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -13,6 +13,15 @@ from workloads import Cost, config, marginals, prefix_lengths
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True, params=[0, 1, 2], ids=["both", "serial", "level"])
+def tree_method(request):
+    """Every case under each tree selection: both methods side by side (the
+    default), the serial pops alone and the level merge alone."""
+    prev = tsv.set_tree_method(request.param)
+    yield request.param
+    tsv.set_tree_method(prev)
+
+
 def _run(marg_np, top_k, n_budget, N_max, cost=None, prefix=None):
     m = torch.from_numpy(np.ascontiguousarray(marg_np, dtype=np.float32)).to(DEV)
     pl = None if prefix is None else torch.from_numpy(np.asarray(prefix, np.int32)).to(DEV)
@@ -79,6 +88,40 @@ def test_adaptive_budget(seed):
                  dataclasses.replace(base, a=0.75, b=0.5, c=0.0, e=0.0, c_d=0.25)):
         for cap in (0, 7, 100):
             _run(marg, 32, cap, 100, cost, prefix)
+
+
+def _softmax_rows(rng, shape, sigma):
+    lg = rng.normal(0, sigma, size=shape)
+    m = np.exp(lg - lg.max(-1, keepdims=True))
+    return (m / m.sum(-1, keepdims=True)).astype(np.float32)
+
+
+@pytest.mark.parametrize("sigma", [5.0, 12.0])
+def test_peaked_drafter(sigma):
+    """Confident drafter distributions (top-1 probability 0.4-0.8): deep trees
+    whose levels re-merge many nodes, fixed and adaptive budgets, both
+    frontier capacities."""
+    rng = np.random.default_rng(int(sigma))
+    marg = _softmax_rows(rng, (4, 16, 5000), sigma)
+    for top_k, cap in ((32, 32), (128, 128), (4, 128), (8, 64)):
+        _run(marg, top_k, cap, 128)
+    prefix = rng.integers(0, 50000, size=4).astype(np.int32)
+    cost = Cost(a=1.0, b=0.002, c=1e-5, e=1e-7, c_d=0.5)
+    for top_k, cap in ((32, 32), (128, 128), (4, 100)):
+        _run(marg, top_k, cap, 128, cost, prefix)
+
+
+def test_adaptive_scores_below_exact_range():
+    """Near-uniform marginals over a large vocabulary: depth-2 scores fall
+    below 2^-23, so the throughput sums past them are taken one at a time;
+    a nearly flat cost keeps the stop rule from ending early."""
+    rng = np.random.default_rng(17)
+    marg = _softmax_rows(rng, (3, 8, 60000), 0.05)
+    prefix = np.array([10, 2000, 40000], np.int32)
+    for cost in (Cost(a=1.0, b=1e-12, c=0.0, e=0.0, c_d=0.5),
+                 Cost(a=1.0, b=1e-9, c=0.0, e=0.0, c_d=0.5)):
+        for top_k, cap in ((4, 128), (16, 40), (128, 128)):
+            _run(marg, top_k, cap, 128, cost, prefix)
 
 
 def test_exact_zero_gain_stops():

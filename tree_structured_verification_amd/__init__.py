@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     refresh_compressed,
     row_layout,
     select_global_budget,
+    set_tree_method,
     status_string,
     tsv_cost,
     tsv_cost_fitted,

@@ -73,6 +73,7 @@ _SIGS = {
                            _I, _P, _P, _P],
     "tsv_workspace_size": [_I] * 12,
     "tsv_status_string": [_I],
+    "tsv_set_tree_method": [_I],
 }
 
 _lib = None
@@ -98,6 +99,16 @@ def lib() -> ctypes.CDLL:
 
 def status_string(code: int) -> str:
     return lib().tsv_status_string(int(code)).decode()
+
+
+def set_tree_method(method: int) -> int:
+    """Tree selection of the build_tree family: 0 both methods side by side
+    (default), 1 serial pops only, 2 level merge only.  Returns the previous
+    setting."""
+    r = lib().tsv_set_tree_method(int(method))
+    if r < 0:
+        raise TsvError("tsv_set_tree_method", r)
+    return r
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -103,6 +103,9 @@ bool cost_ok(const tsv_cost_fitted* cost) {
 // are bit-identical.
 tsv_cost_fitted widen(const tsv_cost& c) { return tsv_cost_fitted{c.a, c.b, c.c, c.e, c.c_d, 0.0}; }
 
+// method of the per-position tree selection (tsv_set_tree_method)
+std::atomic<int> g_tree_method{0};
+
 // top-k of every list, then the best-first tree; shared by both builders
 int launch_build(const float* probs, int B, int rows_per_b, int steps, int V, int top_k,
                  int n_budget, const tsv_cost_fitted* cost, const int* prefix_len, int N_max,
@@ -128,6 +131,7 @@ int launch_build(const float* probs, int B, int rows_per_b, int steps, int V, in
   a.adaptive = cost ? 1 : 0;
   a.rows = rows_per_b;
   a.per_node = per_node ? 1 : 0;
+  a.method = g_tree_method.load(std::memory_order_relaxed);
   a.cost = cost ? *cost : tsv_cost_fitted{0, 0, 0, 0, 0, 0};
   a.prefix_len = prefix_len;
   a.n_nodes = n_nodes;
@@ -210,6 +214,11 @@ int scratch_address(hipStream_t s, void** out) {
 }  // namespace
 
 extern "C" {
+
+int tsv_set_tree_method(int method) {
+  if (method < 0 || method > 2) return TSV_EINVAL;
+  return g_tree_method.exchange(method, std::memory_order_relaxed);
+}
 
 const char* tsv_status_string(int code) {
   switch (code) {

@@ -13,16 +13,19 @@
 // of the node whose token came from list i has list k*i + 1 + r (the root's
 // list is 0).  Each frontier entry then carries the list its token came from.
 //
-// One wavefront per request.  The frontier holds, for every popped node, its
+// Serial pops (one wavefront): the frontier holds, for every popped node, its
 // best unpopped child and its next unpopped sibling -- enough because a
 // node's children are ranked by probability, so a child never beats its
 // better-ranked sibling or its parent.  Each frontier entry is one 64-bit key
 // that orders exactly like the selection order
 //   (score desc, depth asc, parent's position asc, rank asc),
 // and the frontier is kept sorted by it across the lanes, so a pop reads
-// lane 0.  Scores are fp32
-// products (never fused); the stop rule is evaluated in fp64 with explicit
-// round-to-nearest operations in a fixed order.
+// lane 0.  With per-position lists a second wavefront of the same workgroup
+// builds the same tree level by level (far fewer dependent steps when few
+// nodes below depth 1 are selected) and the first of the two to finish
+// writes it.  Scores are fp32 products (never fused); the stop rule is
+// evaluated in fp64 with explicit round-to-nearest operations in a fixed
+// order.
 
 #include "tsv_device.hpp"
 #include "tsv_internal.hpp"
@@ -79,43 +82,72 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
 constexpr int kShl1 = 0x130;  // lane l takes lane l + 1 (lane 63 takes the fill)
 constexpr int kShr1 = 0x138;  // lane l takes lane l - 1 (lane 0 takes the fill)
 
-template <int SL, bool PER_NODE, bool ADAPTIVE>
-__global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
-  __shared__ float s_p[kMaxTopkTable];
-  __shared__ int s_i[kMaxTopkTable];
-  __shared__ int n_par[128], n_dep[128], n_rank[128], n_row[128];
-  __shared__ float n_sc[128];
-
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+// ---- the table of top-k lists, staged in LDS ------------------------------
+// Loads are issued in batches of 8 per thread, all in flight together.
+__device__ __forceinline__ void load_table(const TreeArgs& a, int b, int tid, int nth, float* s_p, int* s_i) {
   const int gk = a.rows * a.k;
   const size_t tbase = static_cast<size_t>(b) * gk;
-  // the table in batches of 8 loads per lane, all in flight together
-  for (int e0 = 0; e0 < gk; e0 += 8 * 64) {
+  for (int e0 = 0; e0 < gk; e0 += 8 * nth) {
     float p[8];
     int ix[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * 64 + lane;
+      const int e = e0 + u * nth + tid;
       p[u] = e < gk ? a.tk_p[tbase + e] : 0.f;
       ix[u] = e < gk ? a.tk_idx[tbase + e] : 0;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * 64 + lane;
+      const int e = e0 + u * nth + tid;
       if (e < gk) {
         s_p[e] = p[u];
         s_i[e] = ix[u];
       }
     }
   }
-  // the best child of a node at depth d has probability p[d][0]: lane d keeps it
-  const float q_first = (!PER_NODE && lane < a.gamma) ? a.tk_p[tbase + static_cast<size_t>(lane) * a.k] : 0.f;
-  __syncthreads();
+}
 
+// Two wavefronts of a workgroup may compute the same tree by different
+// methods; the first to finish claims the result (an LDS word, 0 = open),
+// the other sees the claim and stops.
+__device__ __forceinline__ int claimed(int* w) {
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+__device__ __forceinline__ bool claim(int* w, int id) {
+  int won = 0;
+  if (__lane_id() == 0) {
+    int expected = 0;
+    won = __hip_atomic_compare_exchange_strong(w, &expected, id, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP)
+              ? 1
+              : 0;
+  }
+  return __builtin_amdgcn_readfirstlane(won) != 0;
+}
+
+// Records of the selected nodes, in selection order (LDS).
+struct NodeRecords {
+  int* par;
+  int* dep;
+  int* rank;
+  int* row;
+  float* sc;
+};
+
+// ---- serial best-first pops ---------------------------------------------
+// The frontier holds, for every popped node, its best unpopped child and its
+// next unpopped sibling (children are ranked by probability, so a child
+// never beats its better-ranked sibling or its parent), sorted across the
+// lanes by a 64-bit key that orders exactly like the selection order.  One
+// pop per node.  Returns the node count, or -1 when another wavefront has
+// claimed the result first (RACE).
+template <int SL, bool PER_NODE, bool ADAPTIVE, bool RACE>
+__device__ __forceinline__ int serial_select(const TreeArgs& a, int b, int lane, const float* s_p, float q_first,
+                                             int* winner, float (&r_sc)[SL], int (&r_par)[SL], int (&r_dep)[SL],
+                                             int (&r_rank)[SL], int (&r_row)[SL]) {
   // entry = order key (0 = empty; it holds the node's exact score) and (per
   // node) the list its token comes from; the parent's score is read from
-  // the popped nodes' record when the entry is popped
+  // the popped nodes' records when the entry is popped
   uint64_t fk[SL];
   int frw[SL];
 #pragma unroll
@@ -168,10 +200,7 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
   double theta = ADAPTIVE ? __ddiv_rn(1.0, round_cost(a.cost, 0, l)) : 0.0;
 
   // Popped nodes' records stay in registers during the pops (node m at lane
-  // m % 64 of slot m / 64; a parent's score is one readlane away) and go to
-  // LDS once afterwards, so no pop waits on an LDS store or load of them.
-  float r_sc[SL];
-  int r_par[SL], r_dep[SL], r_rank[SL], r_row[SL];
+  // m % 64 of slot m / 64; a parent's score is one readlane away).
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
     r_sc[s] = 0.f;
@@ -180,6 +209,8 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
 
   int m = 0;
   while (m < a.cap) {
+    // the other wavefront's claim, read now and tested after this pop
+    const int other = RACE ? claimed(winner) : 0;
     const uint64_t hk = readlane_u64(fk[0], 0);
     if (hk == 0) break;  // every candidate taken
     const uint32_t wl = static_cast<uint32_t>(hk);
@@ -234,30 +265,303 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
       theta = th2;
     }
     ++m;
+    if (RACE && other != 0) return -1;
   }
-  const int n = m;
+  return m;
+}
+
+template <int SL, bool PER_NODE>
+__device__ __forceinline__ void store_serial_records(int n, int lane, const float (&r_sc)[SL], const int (&r_par)[SL],
+                                                     const int (&r_dep)[SL], const int (&r_rank)[SL],
+                                                     const int (&r_row)[SL], const NodeRecords& o) {
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
     const int i = s * 64 + lane;
     if (i < n) {
-      n_par[i] = r_par[s];
-      n_dep[i] = r_dep[s];
-      n_rank[i] = r_rank[s];
-      if constexpr (PER_NODE) n_row[i] = r_row[s];
-      n_sc[i] = r_sc[s];
+      o.par[i] = r_par[s];
+      o.dep[i] = r_dep[s];
+      o.rank[i] = r_rank[s];
+      if constexpr (PER_NODE) o.row[i] = r_row[s];
+      o.sc[i] = r_sc[s];
     }
   }
-  __syncthreads();
+}
 
+// ---- level-by-level selection (per-position lists) ------------------------
+// The first c nodes of the selection order among depths <= d are contained in
+// the first c among depths <= d-1 plus the children of its depth-(d-1)
+// members (any prefix of the order is ancestor-closed), and depth 1 is the
+// first list itself.  So the kept list K (at most cap nodes, in selection
+// order) is built level by level: the members' children are merged in
+// selection order (a sorted frontier of one entry per member: a member's
+// children are ranked by probability) until the next child would fall at or
+// beyond place cap; a child ranks after every kept node of equal or higher
+// score, since it is deeper than all of them.  Cheap when few nodes below
+// depth 1 make the cut (flat drafter distributions); a peaked distribution
+// re-merges many nodes at every level, which is why the serial pops run
+// beside it.
+__device__ __forceinline__ int meta_pack(int par, int dep, int rank) { return (par + 1) | (dep << 8) | (rank << 16); }
+__device__ __forceinline__ int meta_par(int v) { return (v & 255) - 1; }
+__device__ __forceinline__ int meta_dep(int v) { return (v >> 8) & 127; }
+__device__ __forceinline__ int meta_rank(int v) { return v >> 16; }
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, ROW_MASK, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, ROW_MASK, 0xF, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+// Inclusive sum over the lanes (row shifts 1, 2, 4, 8, then the row totals
+// broadcast into the following rows).  Used only where every partial sum is
+// exact, so its association order does not matter.
+__device__ __forceinline__ double wave_incl_sum_f64(double v) {
+  v = __dadd_rn(v, dpp_f64<0x111, 0xF>(v));
+  v = __dadd_rn(v, dpp_f64<0x112, 0xF>(v));
+  v = __dadd_rn(v, dpp_f64<0x114, 0xF>(v));
+  v = __dadd_rn(v, dpp_f64<0x118, 0xF>(v));
+  v = __dadd_rn(v, dpp_f64<0x142, 0xA>(v));
+  v = __dadd_rn(v, dpp_f64<0x143, 0xC>(v));
+  return v;
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  return __longlong_as_double(static_cast<long long>(readlane_u64(static_cast<uint64_t>(__double_as_longlong(v)), l)));
+}
+__device__ __forceinline__ double wave_shr1_f64(double v, double fill) {
+  return __longlong_as_double(static_cast<long long>(
+      wave_shift_u64<kShr1>(static_cast<uint64_t>(__double_as_longlong(v)), static_cast<uint64_t>(__double_as_longlong(fill)))));
+}
+
+struct LevelScratch {
+  float* sc;     // merged list, scores
+  int* meta;     // merged list, packed parent / depth / rank
+  int* src;      // members' places in K
+  float* msc;    // members' scores
+};
+
+template <int SL, bool ADAPTIVE>
+__device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, const float* s_p, const LevelScratch& w,
+                                            int* winner, float (&K_sc)[SL], int (&K_meta)[SL]) {
+  const int k = a.k, cap = a.cap;
+  const int kr = cap < k ? cap : k;
+  int c = kr;
+  // depth 1: the first list, in rank order (score 1 * q = q)
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const int P = s * 64 + lane;
+    K_sc[s] = P < c ? s_p[P] : 0.f;
+    K_meta[s] = P < c ? meta_pack(-1, 1, P) : 0;
+  }
+
+  for (int d = 2; d <= a.gamma; ++d) {
+    const int other = claimed(winner);
+    // members: the kept nodes of depth d-1, in selection order
+    int m = 0, tix[SL];
+    bool mem[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      mem[s] = P < c && meta_dep(K_meta[s]) == d - 1;
+      const uint64_t bm = __ballot(mem[s]);
+      tix[s] = m + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0u)));
+      m += __popcll(bm);
+    }
+    if (m == 0) break;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      if (mem[s]) {
+        w.src[tix[s]] = s * 64 + lane;
+        w.msc[tix[s]] = K_sc[s];
+      }
+    }
+    // list of position d: lane r of slot s holds q[d][64 s + r]
+    float qd[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      qd[s] = P < k ? s_p[(d - 1) * k + P] : 0.f;
+    }
+    wave_lds_sync();
+    const float q0 = readlane_f32(qd[0], 0);
+    // one frontier entry per member: its best unmerged child (the members'
+    // first children are already in selection order)
+    uint64_t H[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int t = s * 64 + lane;
+      H[s] = t < m ? frontier_key(__fmul_rn(w.msc[t], q0), d, w.src[t], 0) : 0;
+    }
+    auto insert = [&](uint64_t x) {
+      int pos = 0;
+#pragma unroll
+      for (int s = 0; s < SL; ++s) pos += __popcll(__ballot(H[s] > x));
+      uint64_t ck = 0;
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const uint64_t k63 = readlane_u64(H[s], 63);
+        const uint64_t shk = wave_shift_u64<kShr1>(H[s], ck);
+        const int P = s * 64 + lane;
+        H[s] = P < pos ? H[s] : (P == pos ? x : shk);
+        ck = k63;
+      }
+    };
+
+    // merge: children in selection order, while they make the first cap
+    int i = 0;
+    float C_sc[SL];
+    int C_mp[SL], C_rank[SL], C_pos[SL], sh[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      C_sc[s] = 0.f;
+      C_mp[s] = C_rank[s] = C_pos[s] = sh[s] = 0;
+    }
+    while (true) {
+      const uint64_t hk = readlane_u64(H[0], 0);
+      if (hk == 0) break;  // every member's children merged
+      const uint32_t wl = static_cast<uint32_t>(hk);
+      const int r = 127 - static_cast<int>(wl & 127);
+      const int mp = 255 - static_cast<int>((wl >> 7) & 255) - 1;
+      const float v = key_score(hk);
+      // kept nodes ahead of the child: every one of equal or higher score
+      int pos = 0;
+#pragma unroll
+      for (int s = 0; s < SL; ++s) pos += __popcll(__ballot((s * 64 + lane) < c && K_sc[s] >= v));
+      if (i + pos >= cap) break;
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        if (s == (i >> 6)) {
+          const bool me = lane == (i & 63);
+          C_sc[s] = me ? v : C_sc[s];
+          C_mp[s] = me ? mp : C_mp[s];
+          C_rank[s] = me ? r : C_rank[s];
+          C_pos[s] = me ? pos : C_pos[s];
+        }
+        sh[s] += pos <= s * 64 + lane ? 1 : 0;
+      }
+      ++i;
+      // drop the merged child, enter its next sibling
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const uint64_t nk = s + 1 < SL ? readlane_u64(H[s + 1 < SL ? s + 1 : s], 0) : 0;
+        H[s] = wave_shift_u64<kShl1>(H[s], nk);
+      }
+      // a child of rank >= cap trails its cap better-ranked siblings: never
+      // kept (and the list row in registers covers ranks below 64 * SL)
+      if (r + 1 < kr) {
+        const float smp = mp < 64 ? readlane_f32(K_sc[0], mp & 63) : readlane_f32(K_sc[SL - 1], mp & 63);
+        const int r1 = r + 1;
+        const float qn = r1 < 64 ? readlane_f32(qd[0], r1 & 63) : readlane_f32(qd[SL - 1], r1 & 63);
+        insert(frontier_key(__fmul_rn(smp, qn), d, mp, r1));
+      }
+    }
+    if (i == 0) break;  // nothing of depth d kept: nothing deeper either
+
+    // new places: a kept node moves down by the merged children ahead of it
+    // (child j is ahead of place P iff C_pos[j] <= P); parents follow
+    int npK[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) npK[s] = s * 64 + lane + sh[s];
+    auto newpos = [&](int old) {
+      const int a0 = __builtin_amdgcn_ds_bpermute((old & 63) << 2, npK[0]);
+      const int a1 = SL > 1 ? __builtin_amdgcn_ds_bpermute((old & 63) << 2, npK[SL - 1]) : a0;
+      return old < 0 ? -1 : (old < 64 ? a0 : a1);
+    };
+    int kp[SL], cp[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      kp[s] = newpos(meta_par(K_meta[s]));
+      cp[s] = newpos(C_mp[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      if (P < c && npK[s] < cap) {
+        w.sc[npK[s]] = K_sc[s];
+        w.meta[npK[s]] = meta_pack(kp[s], meta_dep(K_meta[s]), meta_rank(K_meta[s]));
+      }
+      if (P < i) {
+        const int q = P + C_pos[s];
+        w.sc[q] = C_sc[s];
+        w.meta[q] = meta_pack(cp[s], d, C_rank[s]);
+      }
+    }
+    c = cap < c + i ? cap : c + i;
+    wave_lds_sync();
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      K_sc[s] = P < c ? w.sc[P] : 0.f;
+      K_meta[s] = P < c ? w.meta[P] : 0;
+    }
+    if (other != 0) return -1;
+  }
+
+  if constexpr (!ADAPTIVE) {
+    return c;
+  } else {
+    // Stop rule over the kept list.  Phi at place P sums scores >= 2^-23 of
+    // at most 128 nodes, so every partial sum is an exact multiple of
+    // 2^(e-23), e >= -23, below 2^8: exact in fp64 in any order, equal to
+    // the sequential sum.  From the first smaller score on, the sums are
+    // taken one by one in order.
+    const double l = static_cast<double>(a.prefix_len[b]);
+    double inc[SL], ex[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      inc[s] = wave_incl_sum_f64(P < c ? static_cast<double>(K_sc[s]) : 0.0);
+    }
+    double carry = 0.0;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      inc[s] = __dadd_rn(inc[s], carry);
+      ex[s] = wave_shr1_f64(inc[s], carry);
+      carry = readlane_f64(inc[s], 63);
+    }
+    int t_ex = 0, stop = -1;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      const bool ok = P < c && K_sc[s] >= 0x1p-23f;
+      t_ex += __popcll(__ballot(ok));
+      const double th_in = __ddiv_rn(__dadd_rn(1.0, inc[s]), round_cost(a.cost, P + 1, l));
+      const double th_ex = __ddiv_rn(__dadd_rn(1.0, ex[s]), round_cost(a.cost, P, l));
+      const uint64_t sm = __ballot(ok && !(th_in > th_ex));
+      if (sm != 0 && stop < 0) stop = s * 64 + static_cast<int>(__builtin_ctzll(sm));
+    }
+    if (stop >= 0) return stop;
+    if (t_ex == c) return c;
+    double phi = t_ex < 64 ? readlane_f64(ex[0], t_ex & 63) : readlane_f64(ex[SL - 1], t_ex & 63);
+    double theta = __ddiv_rn(__dadd_rn(1.0, phi), round_cost(a.cost, t_ex, l));
+    int n = t_ex;
+    for (; n < c; ++n) {
+      const float sn = n < 64 ? readlane_f32(K_sc[0], n & 63) : readlane_f32(K_sc[SL - 1], n & 63);
+      const double phi2 = __dadd_rn(phi, static_cast<double>(sn));
+      const double th2 = __ddiv_rn(__dadd_rn(1.0, phi2), round_cost(a.cost, n + 1, l));
+      if (!(th2 > theta)) break;
+      phi = phi2;
+      theta = th2;
+    }
+    return n;
+  }
+}
+
+// ---- outputs: parent, token, depth, score, ancestor bits ------------------
+template <bool PER_NODE>
+__device__ __forceinline__ void write_tree(const TreeArgs& a, int b, int tid, int nth, int n, const int* s_i,
+                                           const NodeRecords& o) {
   const int W = (a.N_max + 31) >> 5;
   const size_t nb = static_cast<size_t>(b) * a.N_max;
-  for (int i = lane; i < a.N_max; i += 64) {
+  for (int i = tid; i < a.N_max; i += nth) {
     const bool v = i < n;
-    a.parent[nb + i] = v ? n_par[i] : -1;
-    const int trow = v ? (PER_NODE ? n_row[i] : n_dep[i] - 1) : 0;
-    a.token[nb + i] = v ? s_i[trow * a.k + n_rank[i]] : -1;
-    a.depth[nb + i] = v ? n_dep[i] : -1;
-    a.score[nb + i] = v ? n_sc[i] : 0.0f;
+    a.parent[nb + i] = v ? o.par[i] : -1;
+    const int trow = v ? (PER_NODE ? o.row[i] : o.dep[i] - 1) : 0;
+    a.token[nb + i] = v ? s_i[trow * a.k + o.rank[i]] : -1;
+    a.depth[nb + i] = v ? o.dep[i] : -1;
+    a.score[nb + i] = v ? o.sc[i] : 0.0f;
     uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
     if (v) {
       int j = i;
@@ -268,7 +572,7 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
         else if (wi == 1) w1 |= bit;
         else if (wi == 2) w2 |= bit;
         else w3 |= bit;
-        j = n_par[j];
+        j = o.par[j];
       }
     }
     unsigned* dst = a.anc_bits + (nb + i) * W;
@@ -277,29 +581,105 @@ __global__ __launch_bounds__(64) void best_first_kernel(TreeArgs a) {
     if (W > 2) dst[2] = w2;
     if (W > 3) dst[3] = w3;
   }
-  if (lane == 0) a.n_nodes[b] = n;
+  if (tid == 0) a.n_nodes[b] = n;
+}
+
+// Per-node lists: serial pops, one wavefront per request.
+template <int SL, bool ADAPTIVE>
+__global__ __launch_bounds__(64) void best_first_node_kernel(TreeArgs a) {
+  __shared__ float s_p[kMaxTopkTable];
+  __shared__ int s_i[kMaxTopkTable];
+  __shared__ int n_par[128], n_dep[128], n_rank[128], n_row[128];
+  __shared__ float n_sc[128];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  load_table(a, b, lane, 64, s_p, s_i);
+  __syncthreads();
+  float r_sc[SL];
+  int r_par[SL], r_dep[SL], r_rank[SL], r_row[SL];
+  const int n = serial_select<SL, true, ADAPTIVE, false>(a, b, lane, s_p, 0.f, nullptr, r_sc, r_par, r_dep, r_rank,
+                                                         r_row);
+  const NodeRecords o{n_par, n_dep, n_rank, n_row, n_sc};
+  store_serial_records<SL, true>(n, lane, r_sc, r_par, r_dep, r_rank, r_row, o);
+  __syncthreads();
+  write_tree<true>(a, b, lane, 64, n, s_i, o);
+}
+
+// Per-position lists: two wavefronts per request compute the same tree, the
+// serial pops (wavefront 0) and the level-by-level merge (wavefront 1); the
+// first to finish writes it.
+template <int SL, bool ADAPTIVE>
+__global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
+  __shared__ float s_p[kMaxTopkTable];
+  __shared__ int s_i[kMaxTopkTable];
+  __shared__ int n_par[128], n_dep[128], n_rank[128];
+  __shared__ float n_sc[128];
+  __shared__ float l_sc[128], l_msc[128];
+  __shared__ int l_meta[128], l_src[128];
+  __shared__ int s_winner, s_n;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the best child of a node at depth d has probability p[d][0]: lane d keeps it
+  const float q_first =
+      (wave == 0 && lane < a.gamma) ? a.tk_p[static_cast<size_t>(b) * a.rows * a.k + static_cast<size_t>(lane) * a.k]
+                                    : 0.f;
+  load_table(a, b, tid, 128, s_p, s_i);
+  if (tid == 0) s_winner = 0;
+  __syncthreads();
+  const NodeRecords o{n_par, n_dep, n_rank, nullptr, n_sc};
+  if (wave == 0) {
+    float r_sc[SL];
+    int r_par[SL], r_dep[SL], r_rank[SL], r_row[SL];
+    const int n = a.method == 2 ? -1
+                                : serial_select<SL, false, ADAPTIVE, true>(a, b, lane, s_p, q_first, &s_winner, r_sc,
+                                                                           r_par, r_dep, r_rank, r_row);
+    if (n >= 0 && claim(&s_winner, 1)) {
+      store_serial_records<SL, false>(n, lane, r_sc, r_par, r_dep, r_rank, r_row, o);
+      if (lane == 0) s_n = n;
+    }
+  } else {
+    float K_sc[SL];
+    int K_meta[SL];
+    const LevelScratch w{l_sc, l_meta, l_src, l_msc};
+    const int n = a.method == 1 ? -1 : level_select<SL, ADAPTIVE>(a, b, lane, s_p, w, &s_winner, K_sc, K_meta);
+    if (n >= 0 && claim(&s_winner, 2)) {
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const int i = s * 64 + lane;
+        if (i < n) {
+          n_par[i] = meta_par(K_meta[s]);
+          n_dep[i] = meta_dep(K_meta[s]);
+          n_rank[i] = meta_rank(K_meta[s]);
+          n_sc[i] = K_sc[s];
+        }
+      }
+      if (lane == 0) s_n = n;
+    }
+  }
+  __syncthreads();
+  write_tree<false>(a, b, tid, 128, s_n, s_i, o);
 }
 
 }  // namespace
 
 hipError_t launch_best_first(const TreeArgs& a, hipStream_t s) {
-  // sorted frontier of 64 or 128 places (at least cap); the stop rule only
+  // sorted frontiers of 64 or 128 places (at least cap); the stop rule only
   // in the adaptive instances
-  const dim3 g(a.B), blk(64);
-#define TSV_BF(SL, PN)                                                   \
-  if (a.adaptive) best_first_kernel<SL, PN, true><<<g, blk, 0, s>>>(a);  \
-  else best_first_kernel<SL, PN, false><<<g, blk, 0, s>>>(a);
+  const dim3 g(a.B);
+#define TSV_BF(KERNEL, SL, THREADS)                                     \
+  if (a.adaptive) KERNEL<SL, true><<<g, dim3(THREADS), 0, s>>>(a);      \
+  else KERNEL<SL, false><<<g, dim3(THREADS), 0, s>>>(a);
   if (a.per_node) {
     if (a.cap <= 64) {
-      TSV_BF(1, true)
+      TSV_BF(best_first_node_kernel, 1, 64)
     } else {
-      TSV_BF(2, true)
+      TSV_BF(best_first_node_kernel, 2, 64)
     }
   } else {
     if (a.cap <= 64) {
-      TSV_BF(1, false)
+      TSV_BF(best_first_pos_kernel, 1, 128)
     } else {
-      TSV_BF(2, false)
+      TSV_BF(best_first_pos_kernel, 2, 128)
     }
   }
 #undef TSV_BF

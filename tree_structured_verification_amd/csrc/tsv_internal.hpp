@@ -33,6 +33,9 @@ struct TreeArgs {
   // rows of top-k lists per request: gamma (one per position), or the
   // expanded nodes in level order when per_node is set
   int rows, per_node;
+  // per-position lists: 0 = serial pops and level merge side by side,
+  // 1 = serial pops only, 2 = level merge only
+  int method;
   tsv_cost_fitted cost;
   const int* prefix_len;
   int* n_nodes;
