@@ -83,36 +83,47 @@ constexpr int kShl1 = 0x130;  // lane l takes lane l + 1 (lane 63 takes the fill
 constexpr int kShr1 = 0x138;  // lane l takes lane l - 1 (lane 0 takes the fill)
 
 // ---- the table of top-k lists, staged in LDS ------------------------------
-// Loads are issued in batches of 8 per thread, all in flight together.
+// All loads of a batch are in flight together: U per thread (8 when that
+// covers the table, else 16, fewer masked-off instructions for small tables).
+template <int U>
+__device__ __forceinline__ void load_table_batch(const TreeArgs& a, size_t tbase, int gk, int e0, int tid, int nth,
+                                                 float* s_p, int* s_i) {
+  float p[U];
+  int ix[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = e0 + u * nth + tid;
+    p[u] = e < gk ? a.tk_p[tbase + e] : 0.f;
+    ix[u] = e < gk ? a.tk_idx[tbase + e] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e = e0 + u * nth + tid;
+    if (e < gk) {
+      s_p[e] = p[u];
+      s_i[e] = ix[u];
+    }
+  }
+}
 __device__ __forceinline__ void load_table(const TreeArgs& a, int b, int tid, int nth, float* s_p, int* s_i) {
   const int gk = a.rows * a.k;
   const size_t tbase = static_cast<size_t>(b) * gk;
-  for (int e0 = 0; e0 < gk; e0 += 8 * nth) {
-    float p[8];
-    int ix[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * nth + tid;
-      p[u] = e < gk ? a.tk_p[tbase + e] : 0.f;
-      ix[u] = e < gk ? a.tk_idx[tbase + e] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * nth + tid;
-      if (e < gk) {
-        s_p[e] = p[u];
-        s_i[e] = ix[u];
-      }
-    }
+  if (gk <= 8 * nth) {
+    load_table_batch<8>(a, tbase, gk, 0, tid, nth, s_p, s_i);
+  } else {
+    for (int e0 = 0; e0 < gk; e0 += 16 * nth) load_table_batch<16>(a, tbase, gk, e0, tid, nth, s_p, s_i);
   }
 }
 
 // Two wavefronts of a workgroup may compute the same tree by different
 // methods; the first to finish claims the result (an LDS word, 0 = open),
-// the other sees the claim and stops.
-__device__ __forceinline__ int claimed(int* w) {
-  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+// the other sees the claim and stops.  A loop reads the word at the top of
+// an iteration (claim_load) and tests it at the bottom (claim_seen), so the
+// read's latency hides behind the iteration's work.
+__device__ __forceinline__ int claim_load(int* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+__device__ __forceinline__ bool claim_seen(int v) { return __builtin_amdgcn_readfirstlane(v) != 0; }
 __device__ __forceinline__ bool claim(int* w, int id) {
   int won = 0;
   if (__lane_id() == 0) {
@@ -210,7 +221,7 @@ __device__ __forceinline__ int serial_select(const TreeArgs& a, int b, int lane,
   int m = 0;
   while (m < a.cap) {
     // the other wavefront's claim, read now and tested after this pop
-    const int other = RACE ? claimed(winner) : 0;
+    const int other = RACE ? claim_load(winner) : 0;
     const uint64_t hk = readlane_u64(fk[0], 0);
     if (hk == 0) break;  // every candidate taken
     const uint32_t wl = static_cast<uint32_t>(hk);
@@ -265,7 +276,7 @@ __device__ __forceinline__ int serial_select(const TreeArgs& a, int b, int lane,
       theta = th2;
     }
     ++m;
-    if (RACE && other != 0) return -1;
+    if (RACE && claim_seen(other)) return -1;
   }
   return m;
 }
@@ -337,8 +348,6 @@ __device__ __forceinline__ double wave_shr1_f64(double v, double fill) {
 struct LevelScratch {
   float* sc;     // merged list, scores
   int* meta;     // merged list, packed parent / depth / rank
-  int* src;      // members' places in K
-  float* msc;    // members' scores
 };
 
 template <int SL, bool ADAPTIVE>
@@ -355,36 +364,31 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
     K_meta[s] = P < c ? meta_pack(-1, 1, P) : 0;
   }
 
-  for (int d = 2; d <= a.gamma; ++d) {
-    const int other = claimed(winner);
-    // members: the kept nodes of depth d-1, in selection order
-    int m = 0, tix[SL];
-    bool mem[SL];
+  // members of the next level (lane t of slot s: member 64 s + t, in
+  // selection order): at depth 1 the whole kept list; afterwards the children
+  // merged at the level before, which all made the cut
+  int m = c;
+  float M_sc[SL];
+  int M_pos[SL];
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    M_sc[s] = K_sc[s];
+    M_pos[s] = s * 64 + lane;
+  }
+  // list of position d: lane r of slot s holds q[d][64 s + r]; the next
+  // level's list is read while this one merges
+  auto load_row = [&](int d, float (&q)[SL]) {
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const int P = s * 64 + lane;
-      mem[s] = P < c && meta_dep(K_meta[s]) == d - 1;
-      const uint64_t bm = __ballot(mem[s]);
-      tix[s] = m + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0u)));
-      m += __popcll(bm);
+      q[s] = (d <= a.gamma && P < k) ? s_p[(d - 1) * k + P] : 0.f;
     }
-    if (m == 0) break;
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      if (mem[s]) {
-        w.src[tix[s]] = s * 64 + lane;
-        w.msc[tix[s]] = K_sc[s];
-      }
-    }
-    // list of position d: lane r of slot s holds q[d][64 s + r]
-    float qd[SL];
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      const int P = s * 64 + lane;
-      qd[s] = P < k ? s_p[(d - 1) * k + P] : 0.f;
-    }
-    wave_lds_sync();
+  };
+  float qd[SL], qn[SL];
+  load_row(2, qd);
+
+  for (int d = 2; d <= a.gamma && m > 0; ++d) {
+    load_row(d + 1, qn);
     const float q0 = readlane_f32(qd[0], 0);
     // one frontier entry per member: its best unmerged child (the members'
     // first children are already in selection order)
@@ -392,7 +396,7 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
       const int t = s * 64 + lane;
-      H[s] = t < m ? frontier_key(__fmul_rn(w.msc[t], q0), d, w.src[t], 0) : 0;
+      H[s] = t < m ? frontier_key(__fmul_rn(M_sc[s], q0), d, M_pos[s], 0) : 0;
     }
     auto insert = [&](uint64_t x) {
       int pos = 0;
@@ -418,7 +422,14 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
       C_sc[s] = 0.f;
       C_mp[s] = C_rank[s] = C_pos[s] = sh[s] = 0;
     }
+    // lanes holding kept nodes
+    uint64_t kmask[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) kmask[s] = __ballot(s * 64 + lane < c);
+    bool stopped = false;
     while (true) {
+      // the serial wavefront's claim, read now and tested after this child
+      const int other = claim_load(winner);
       const uint64_t hk = readlane_u64(H[0], 0);
       if (hk == 0) break;  // every member's children merged
       const uint32_t wl = static_cast<uint32_t>(hk);
@@ -428,7 +439,7 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
       // kept nodes ahead of the child: every one of equal or higher score
       int pos = 0;
 #pragma unroll
-      for (int s = 0; s < SL; ++s) pos += __popcll(__ballot((s * 64 + lane) < c && K_sc[s] >= v));
+      for (int s = 0; s < SL; ++s) pos += __popcll(__ballot(K_sc[s] >= v) & kmask[s]);
       if (i + pos >= cap) break;
 #pragma unroll
       for (int s = 0; s < SL; ++s) {
@@ -451,12 +462,23 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
       // a child of rank >= cap trails its cap better-ranked siblings: never
       // kept (and the list row in registers covers ranks below 64 * SL)
       if (r + 1 < kr) {
-        const float smp = mp < 64 ? readlane_f32(K_sc[0], mp & 63) : readlane_f32(K_sc[SL - 1], mp & 63);
         const int r1 = r + 1;
-        const float qn = r1 < 64 ? readlane_f32(qd[0], r1 & 63) : readlane_f32(qd[SL - 1], r1 & 63);
-        insert(frontier_key(__fmul_rn(smp, qn), d, mp, r1));
+        float smp, qr;
+        if constexpr (SL == 1) {
+          smp = readlane_f32(K_sc[0], mp & 63);
+          qr = readlane_f32(qd[0], r1 & 63);
+        } else {
+          smp = mp < 64 ? readlane_f32(K_sc[0], mp & 63) : readlane_f32(K_sc[SL - 1], mp & 63);
+          qr = r1 < 64 ? readlane_f32(qd[0], r1 & 63) : readlane_f32(qd[SL - 1], r1 & 63);
+        }
+        insert(frontier_key(__fmul_rn(smp, qr), d, mp, r1));
+      }
+      if (claim_seen(other)) {
+        stopped = true;
+        break;
       }
     }
+    if (stopped) return -1;
     if (i == 0) break;  // nothing of depth d kept: nothing deeper either
 
     // new places: a kept node moves down by the merged children ahead of it
@@ -495,8 +517,12 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
       const int P = s * 64 + lane;
       K_sc[s] = P < c ? w.sc[P] : 0.f;
       K_meta[s] = P < c ? w.meta[P] : 0;
+      // the merged children, in order, at their new places
+      M_sc[s] = C_sc[s];
+      M_pos[s] = P + C_pos[s];
+      qd[s] = qn[s];
     }
-    if (other != 0) return -1;
+    m = i;
   }
 
   if constexpr (!ADAPTIVE) {
@@ -607,16 +633,17 @@ __global__ __launch_bounds__(64) void best_first_node_kernel(TreeArgs a) {
 
 // Per-position lists: two wavefronts per request compute the same tree, the
 // serial pops (wavefront 0) and the level-by-level merge (wavefront 1); the
-// first to finish writes it.
+// first to finish claims the result and writes the outputs, the other one
+// sees the claim after at most one more pop or merged child and exits.
 template <int SL, bool ADAPTIVE>
 __global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
   __shared__ float s_p[kMaxTopkTable];
   __shared__ int s_i[kMaxTopkTable];
   __shared__ int n_par[128], n_dep[128], n_rank[128];
   __shared__ float n_sc[128];
-  __shared__ float l_sc[128], l_msc[128];
-  __shared__ int l_meta[128], l_src[128];
-  __shared__ int s_winner, s_n;
+  __shared__ float l_sc[128];
+  __shared__ int l_meta[128];
+  __shared__ int s_winner;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // the best child of a node at depth d has probability p[d][0]: lane d keeps it
@@ -635,12 +662,13 @@ __global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
                                                                            r_par, r_dep, r_rank, r_row);
     if (n >= 0 && claim(&s_winner, 1)) {
       store_serial_records<SL, false>(n, lane, r_sc, r_par, r_dep, r_rank, r_row, o);
-      if (lane == 0) s_n = n;
+      wave_lds_sync();
+      write_tree<false>(a, b, lane, 64, n, s_i, o);
     }
   } else {
     float K_sc[SL];
     int K_meta[SL];
-    const LevelScratch w{l_sc, l_meta, l_src, l_msc};
+    const LevelScratch w{l_sc, l_meta};
     const int n = a.method == 1 ? -1 : level_select<SL, ADAPTIVE>(a, b, lane, s_p, w, &s_winner, K_sc, K_meta);
     if (n >= 0 && claim(&s_winner, 2)) {
 #pragma unroll
@@ -653,11 +681,11 @@ __global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
           n_sc[i] = K_sc[s];
         }
       }
-      if (lane == 0) s_n = n;
+      wave_lds_sync();
+      write_tree<false>(a, b, lane, 64, n, s_i, o);
     }
   }
-  __syncthreads();
-  write_tree<false>(a, b, tid, 128, s_n, s_i, o);
+  // the other wavefront stops at its next pop after the claim and exits
 }
 
 }  // namespace
