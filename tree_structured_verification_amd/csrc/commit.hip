@@ -7,7 +7,7 @@
 //
 // One workgroup per request: validate (device-side sizes), copy at most gamma
 // rows of K (and V) with 16-, 4- or 2-byte accesses, then bump the prefix
-// length after every thread has read the old one.
+// length (every thread has read the old one before the first barrier).
 
 #include "tsv_device.hpp"
 #include "tsv_internal.hpp"
@@ -15,13 +15,14 @@
 namespace tsv {
 namespace {
 
-template <typename U>
-__device__ void copy_row(char* dst, const char* src, size_t bytes) {
-  U* d = reinterpret_cast<U*>(dst);
-  const U* s = reinterpret_cast<const U*>(src);
-  const size_t n = bytes / sizeof(U);
-  for (size_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
-}
+// Every thread reads the sizes, thread j < gamma accepted node j; then each
+// thread copies one element column of up to kCopyBatch accepted rows at a
+// time, all its loads issued before its stores, so the copy costs one load
+// round trip rather than one per row.
+constexpr int kCopyBatch = 16;
+// 16-byte element as a plain vector type (an array of HIP's uint4 struct is
+// kept in scratch memory by the compiler)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename U>
 __global__ __launch_bounds__(256) void commit_kernel(
@@ -30,38 +31,44 @@ __global__ __launch_bounds__(256) void commit_kernel(
     const int* accept_nodes, int N_max, int L_cap, size_t k_bytes,
     size_t v_bytes, int gamma, int* status) {
   __shared__ int s_nodes[64];
-  __shared__ int s_state, s_l, s_m;
-  const int b = blockIdx.x;
-  if (threadIdx.x == 0) {
-    const int m = accept_len[b];
-    const int l = prefix_len[b];
-    int st = 0;
-    if (m < 0 || m > gamma || l < 0) {
-      st = 2;
-    } else {
-      for (int j = 0; j < m; ++j) {
-        const int v = accept_nodes[static_cast<size_t>(b) * gamma + j];
-        if (v < 0 || v >= N_max) st = 2;
-        s_nodes[j] = v;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int m = accept_len[b];
+  const int l = prefix_len[b];
+  const int v = tid < gamma ? accept_nodes[static_cast<size_t>(b) * gamma + tid] : 0;
+  const bool size_bad = m < 0 || m > gamma || l < 0;
+  if (tid < 64) s_nodes[tid] = v;
+  // also orders every thread's read of the prefix length before its update
+  const bool node_bad = __syncthreads_or(!size_bad && tid < m && (v < 0 || v >= N_max)) != 0;
+  const int st = (size_bad || node_bad) ? 2 : (static_cast<long>(l) + m > L_cap ? 1 : 0);
+  if (tid == 0) status[b] = st;
+  if (st != 0) return;
+
+  const int nk = static_cast<int>(k_bytes / sizeof(U));
+  const int nv = v_cache ? static_cast<int>(v_bytes / sizeof(U)) : 0;
+  const int per_row = nk + nv;   // a row's elements: K first, then V
+  for (int e0 = 0; e0 < per_row; e0 += static_cast<int>(blockDim.x)) {
+    const int e = e0 + tid;
+    const int ec = min(e, per_row - 1);   // loads past the row re-read its last element
+    const bool isk = ec < nk;
+    const size_t off = static_cast<size_t>(isk ? ec : ec - nk) * sizeof(U);
+    const char* tsrc = (isk ? k_tree : v_tree) + off;
+    char* tdst = (isk ? k_cache : v_cache) + off;
+    for (int j0 = 0; j0 < m; j0 += kCopyBatch) {
+      U val[kCopyBatch];
+#pragma unroll
+      for (int r = 0; r < kCopyBatch; ++r) {
+        const int j = min(j0 + r, m - 1);
+        val[r] = *reinterpret_cast<const U*>(tsrc + (static_cast<size_t>(b) * N_max + s_nodes[j]) * row_bytes);
       }
-      if (st == 0 && static_cast<long>(l) + m > L_cap) st = 1;
+#pragma unroll
+      for (int r = 0; r < kCopyBatch; ++r) {
+        const int j = j0 + r;
+        if (e < per_row && j < m)
+          *reinterpret_cast<U*>(tdst + (static_cast<size_t>(b) * L_cap + l + j) * row_bytes) = val[r];
+      }
     }
-    s_state = st;
-    s_l = l;
-    s_m = m;
-    status[b] = st;
   }
-  __syncthreads();
-  if (s_state != 0) return;
-  const int l = s_l, m = s_m;
-  for (int j = 0; j < m; ++j) {
-    const size_t src = (static_cast<size_t>(b) * N_max + s_nodes[j]) * row_bytes;
-    const size_t dst = (static_cast<size_t>(b) * L_cap + l + j) * row_bytes;
-    copy_row<U>(k_cache + dst, k_tree + src, k_bytes);
-    if (v_cache) copy_row<U>(v_cache + dst, v_tree + src, v_bytes);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) prefix_len[b] = l + m;
+  if (tid == 0) prefix_len[b] = l + m;
 }
 
 }  // namespace
@@ -86,7 +93,7 @@ hipError_t launch_commit(void* k_cache, void* v_cache, int* prefix_len,
   const char* vt = static_cast<const char*>(v_tree);
   dim3 grid(B), block(256);
   if (fits(16))
-    commit_kernel<uint4><<<grid, block, 0, s>>>(kc, vc, prefix_len, kt, vt, row_bytes, accept_len,
+    commit_kernel<u32x4><<<grid, block, 0, s>>>(kc, vc, prefix_len, kt, vt, row_bytes, accept_len,
                                                 accept_nodes, N_max, L_cap, k_bytes, v_bytes, gamma, status);
   else if (fits(4))
     commit_kernel<uint32_t><<<grid, block, 0, s>>>(kc, vc, prefix_len, kt, vt, row_bytes, accept_len,

@@ -130,25 +130,27 @@ __global__ __launch_bounds__(64) void walk_kernel(
     const int* __restrict__ token, int* __restrict__ accept_len,
     int* __restrict__ accept_nodes, int* __restrict__ out_tokens) {
   __shared__ int s_arg[129];
-  __shared__ int s_par[128], s_tok[128];
+  __shared__ int s_tok[128];
   const int b = blockIdx.x, lane = threadIdx.x;
   const int n = clampi(n_nodes[b], 0, N_max);
   const int rows_per_b = N_max + 1;
-  // every load of this lane in flight together: the tree (at most 128
-  // nodes, two per lane) and eight segment keys of each row at a time
+  // every load of this lane in flight together with the node count: the
+  // tree (at most 128 nodes, two per lane) and the first eight segment keys
+  // of the lane's first row (usually all of them: the walk then waits once),
+  // all addressed within the request's N_max nodes and N_max + 1 rows, the
+  // node count applied afterwards
   int par2[2], tok2[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int i = lane + 64 * h;
-    par2[h] = i < n ? parent[static_cast<size_t>(b) * N_max + i] : 0;
-    tok2[h] = i < n ? token[static_cast<size_t>(b) * N_max + i] : 0;
+    par2[h] = i < N_max ? parent[static_cast<size_t>(b) * N_max + i] : 0;
+    tok2[h] = i < N_max ? token[static_cast<size_t>(b) * N_max + i] : 0;
   }
-  // the first eight segment keys of the lane's first row go with them
-  // (usually all of them: the walk then waits once)
   uint64_t v0[8];
   const uint64_t* src0 = seg_best + (static_cast<size_t>(b) * rows_per_b + lane) * nseg;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) v0[u] = lane <= n && u < nseg ? src0[u] : 0;
+  for (int u = 0; u < 8; ++u) v0[u] = lane <= N_max && u < nseg ? src0[u] : 0;
+  int arg0 = -1;   // the argmax of row `lane` (rows 64.. go through LDS)
   for (int r = lane; r <= n; r += 64) {
     const uint64_t* src = seg_best + (static_cast<size_t>(b) * rows_per_b + r) * nseg;
     uint64_t best = 0;
@@ -159,23 +161,25 @@ __global__ __launch_bounds__(64) void walk_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) best = umax64(best, v[u]);
     }
-    s_arg[r] = best ? static_cast<int>(sel_key_index(best)) : -1;
+    const int arg = best ? static_cast<int>(sel_key_index(best)) : -1;
+    if (r == lane) arg0 = arg;
+    s_arg[r] = arg;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int i = lane + 64 * h;
-    if (i < n) {
-      s_par[i] = par2[h];
-      s_tok[i] = tok2[h];
-    }
+    if (i < n) s_tok[i] = tok2[h];
   }
   __syncthreads();
 
+  // each step: the child of the current node whose token is the argmax of
+  // the current node's row (lane i holds nodes i and i + 64 in registers)
+  const bool in0 = lane < n, in1 = lane + 64 < n;
   int cur = -1, m = 0, mine = -1;
   while (m < gamma) {
-    const int want = s_arg[cur + 1];
-    const bool h0 = lane < n && s_par[lane] == cur && s_tok[lane] == want;
-    const bool h1 = lane + 64 < n && s_par[lane + 64] == cur && s_tok[lane + 64] == want;
+    const int want = cur + 1 < 64 ? __builtin_amdgcn_readlane(arg0, cur + 1) : s_arg[cur + 1];
+    const bool h0 = in0 && par2[0] == cur && tok2[0] == want;
+    const bool h1 = in1 && par2[1] == cur && tok2[1] == want;
     const uint64_t m0 = __ballot(h0), m1 = __ballot(h1);
     int j = -1;
     if (m0) j = __ffsll(static_cast<long long>(m0)) - 1;
