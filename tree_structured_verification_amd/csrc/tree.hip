@@ -348,7 +348,22 @@ __device__ __forceinline__ double wave_shr1_f64(double v, double fill) {
 struct LevelScratch {
   float* sc;     // merged list, scores
   int* meta;     // merged list, packed parent / depth / rank
+  float* bsc;    // a batch's merged children in order / next members: scores
+  int* bmp;      //   ... parent places / places
+  int* brk;      //   ... ranks
+  int* bpos;     //   ... kept nodes ahead of them
 };
+
+// Children per member below which a level is merged in batches (one lane per
+// candidate child) rather than one child at a time.
+constexpr int kBatchK = 8;
+
+__device__ __forceinline__ int bperm_i(int src_lane, int v) {
+  return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
+}
+__device__ __forceinline__ float bperm_f(int src_lane, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
 
 template <int SL, bool ADAPTIVE>
 __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, const float* s_p, const LevelScratch& w,
@@ -387,8 +402,176 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
   float qd[SL], qn[SL];
   load_row(2, qd);
 
+  // Merge i children (in selection order: scores C_sc, parents' places C_mp,
+  // ranks C_rank, kept nodes ahead C_pos) of depth d into the kept list.  A
+  // kept node moves down by the children placed ahead of it (child j is
+  // ahead of place P iff C_pos[j] <= P, counted in sh); parents follow
+  // through the new places (npK, returned).
+  auto apply_merge = [&](int i, int d, const float (&C_sc)[SL], const int (&C_mp)[SL], const int (&C_rank)[SL],
+                         const int (&C_pos)[SL], const int (&sh)[SL], int (&npK)[SL]) {
+#pragma unroll
+    for (int s = 0; s < SL; ++s) npK[s] = s * 64 + lane + sh[s];
+    auto newpos = [&](int old) {
+      const int a0 = bperm_i(old & 63, npK[0]);
+      const int a1 = SL > 1 ? bperm_i(old & 63, npK[SL - 1]) : a0;
+      return old < 0 ? -1 : (old < 64 ? a0 : a1);
+    };
+    int kp[SL], cp[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      kp[s] = newpos(meta_par(K_meta[s]));
+      cp[s] = newpos(C_mp[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      if (P < c && npK[s] < cap) {
+        w.sc[npK[s]] = K_sc[s];
+        w.meta[npK[s]] = meta_pack(kp[s], meta_dep(K_meta[s]), meta_rank(K_meta[s]));
+      }
+      if (P < i) {
+        const int q = P + C_pos[s];
+        w.sc[q] = C_sc[s];
+        w.meta[q] = meta_pack(cp[s], d, C_rank[s]);
+      }
+    }
+    c = cap < c + i ? cap : c + i;
+    wave_lds_sync();
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int P = s * 64 + lane;
+      K_sc[s] = P < c ? w.sc[P] : 0.f;
+      K_meta[s] = P < c ? w.meta[P] : 0;
+    }
+  };
+
   for (int d = 2; d <= a.gamma && m > 0; ++d) {
     load_row(d + 1, qn);
+    if (kr <= kBatchK) {
+      // Batches of the members' children, one candidate per lane (member
+      // t0 + lane / kr, rank lane % kr), merged in member order: a child of a
+      // later batch ranks after an equal-score child of an earlier one (its
+      // parent comes later), which the merged list already holds, so the
+      // place rule stays "children of the batch ahead + kept nodes of equal
+      // or higher score".
+      const int per = 64 / kr;
+      const int tl = lane / kr, rl = lane - tl * kr;
+      bool stopped = false;
+      for (int t0 = 0; t0 < m; t0 += per) {
+        const int other = claim_load(winner);
+        const int nb = (m - t0 < per ? m - t0 : per) * kr;
+        const int t = t0 + tl;
+        float msc = bperm_f(t & 63, M_sc[0]);
+        int mpos = bperm_i(t & 63, M_pos[0]);
+        if constexpr (SL > 1) {
+          const float msc1 = bperm_f(t & 63, M_sc[SL - 1]);
+          const int mpos1 = bperm_i(t & 63, M_pos[SL - 1]);
+          msc = t < 64 ? msc : msc1;
+          mpos = t < 64 ? mpos : mpos1;
+        }
+        const float qr = bperm_f(rl, qd[0]);
+        // a member pushed out of the kept list by an earlier batch (place -1)
+        // has at least cap kept nodes of higher or equal score ahead of it,
+        // so none of its children can make the cut
+        const bool valid = lane < nb && mpos >= 0;
+        const float v = __fmul_rn(msc, qr);
+        const uint64_t key = valid ? frontier_key(v, d, mpos, rl) : 0;
+        // place among the batch's children (keys are distinct)
+        int rank = 0;
+        for (int j = 0; j < nb; ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
+        // kept nodes of equal or higher score: the kept list's scores do not
+        // increase along it, so the first place whose score is below v
+        int lo = 0, hi = c;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int mid = (lo + hi) >> 1;
+          float km = bperm_f(mid & 63, K_sc[0]);
+          if constexpr (SL > 1) {
+            const float km1 = bperm_f(mid & 63, K_sc[SL - 1]);
+            km = mid < 64 ? km : km1;
+          }
+          if (lo < hi) {
+            if (km >= v) lo = mid + 1;
+            else hi = mid;
+          }
+        }
+        const int pos = lo;
+        const bool enter = valid && rank + pos < cap;
+        const uint64_t em = __ballot(enter);
+        const int na = __popcll(em);
+        if (na == 0) {
+          // the batch's best child did not make the cut: the later batches'
+          // children score no higher (their members score no higher)
+          if (claim_seen(other)) stopped = true;
+          break;
+        }
+        if (enter) {
+          w.bsc[rank] = v;
+          w.bmp[rank] = mpos;
+          w.brk[rank] = rl;
+          w.bpos[rank] = pos;
+        }
+        wave_lds_sync();
+        float C_sc[SL];
+        int C_mp[SL], C_rank[SL], C_pos[SL], sh[SL], npK[SL];
+#pragma unroll
+        for (int s = 0; s < SL; ++s) {
+          const bool on = s == 0 && lane < na;
+          C_sc[s] = on ? w.bsc[lane] : 0.f;
+          C_mp[s] = on ? w.bmp[lane] : 0;
+          C_rank[s] = on ? w.brk[lane] : 0;
+          C_pos[s] = on ? w.bpos[lane] : 0;
+          sh[s] = 0;
+        }
+        for (int j = 0; j < na; ++j) {
+          const int pj = __builtin_amdgcn_readlane(C_pos[0], j);
+#pragma unroll
+          for (int s = 0; s < SL; ++s) sh[s] += pj <= s * 64 + lane ? 1 : 0;
+        }
+        apply_merge(na, d, C_sc, C_mp, C_rank, C_pos, sh, npK);
+        // members' places after the merge (-1 once pushed past place cap)
+#pragma unroll
+        for (int s = 0; s < SL; ++s) {
+          const int a0 = bperm_i(M_pos[s] & 63, npK[0]);
+          const int a1 = SL > 1 ? bperm_i(M_pos[s] & 63, npK[SL - 1]) : a0;
+          const int np = M_pos[s] < 64 ? a0 : a1;
+          M_pos[s] = (M_pos[s] >= 0 && np < cap) ? np : -1;
+        }
+        if (claim_seen(other)) {
+          stopped = true;
+          break;
+        }
+      }
+      if (stopped) return -1;
+      // next members: the kept nodes of depth d, in order
+      int nm = 0, tix[SL];
+      bool mem[SL];
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        mem[s] = s * 64 + lane < c && meta_dep(K_meta[s]) == d;
+        const uint64_t bm = __ballot(mem[s]);
+        tix[s] = nm + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0u)));
+        nm += __popcll(bm);
+      }
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        if (mem[s]) {
+          w.bsc[tix[s]] = K_sc[s];
+          w.bmp[tix[s]] = s * 64 + lane;
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const int t2 = s * 64 + lane;
+        M_sc[s] = t2 < nm ? w.bsc[t2] : 0.f;
+        M_pos[s] = t2 < nm ? w.bmp[t2] : 0;
+        qd[s] = qn[s];
+      }
+      m = nm;
+      continue;
+    }
     const float q0 = readlane_f32(qd[0], 0);
     // one frontier entry per member: its best unmerged child (the members'
     // first children are already in selection order)
@@ -481,45 +664,13 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
     if (stopped) return -1;
     if (i == 0) break;  // nothing of depth d kept: nothing deeper either
 
-    // new places: a kept node moves down by the merged children ahead of it
-    // (child j is ahead of place P iff C_pos[j] <= P); parents follow
     int npK[SL];
-#pragma unroll
-    for (int s = 0; s < SL; ++s) npK[s] = s * 64 + lane + sh[s];
-    auto newpos = [&](int old) {
-      const int a0 = __builtin_amdgcn_ds_bpermute((old & 63) << 2, npK[0]);
-      const int a1 = SL > 1 ? __builtin_amdgcn_ds_bpermute((old & 63) << 2, npK[SL - 1]) : a0;
-      return old < 0 ? -1 : (old < 64 ? a0 : a1);
-    };
-    int kp[SL], cp[SL];
+    apply_merge(i, d, C_sc, C_mp, C_rank, C_pos, sh, npK);
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
-      kp[s] = newpos(meta_par(K_meta[s]));
-      cp[s] = newpos(C_mp[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      const int P = s * 64 + lane;
-      if (P < c && npK[s] < cap) {
-        w.sc[npK[s]] = K_sc[s];
-        w.meta[npK[s]] = meta_pack(kp[s], meta_dep(K_meta[s]), meta_rank(K_meta[s]));
-      }
-      if (P < i) {
-        const int q = P + C_pos[s];
-        w.sc[q] = C_sc[s];
-        w.meta[q] = meta_pack(cp[s], d, C_rank[s]);
-      }
-    }
-    c = cap < c + i ? cap : c + i;
-    wave_lds_sync();
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      const int P = s * 64 + lane;
-      K_sc[s] = P < c ? w.sc[P] : 0.f;
-      K_meta[s] = P < c ? w.meta[P] : 0;
       // the merged children, in order, at their new places
       M_sc[s] = C_sc[s];
-      M_pos[s] = P + C_pos[s];
+      M_pos[s] = s * 64 + lane + C_pos[s];
       qd[s] = qn[s];
     }
     m = i;
@@ -641,8 +792,8 @@ __global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
   __shared__ int s_i[kMaxTopkTable];
   __shared__ int n_par[128], n_dep[128], n_rank[128];
   __shared__ float n_sc[128];
-  __shared__ float l_sc[128];
-  __shared__ int l_meta[128];
+  __shared__ float l_sc[128], l_bsc[128];
+  __shared__ int l_meta[128], l_bmp[128], l_brk[128], l_bpos[128];
   __shared__ int s_winner;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -668,7 +819,7 @@ __global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
   } else {
     float K_sc[SL];
     int K_meta[SL];
-    const LevelScratch w{l_sc, l_meta};
+    const LevelScratch w{l_sc, l_meta, l_bsc, l_bmp, l_brk, l_bpos};
     const int n = a.method == 1 ? -1 : level_select<SL, ADAPTIVE>(a, b, lane, s_p, w, &s_winner, K_sc, K_meta);
     if (n >= 0 && claim(&s_winner, 2)) {
 #pragma unroll
