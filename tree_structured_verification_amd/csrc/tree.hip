@@ -348,10 +348,8 @@ __device__ __forceinline__ double wave_shr1_f64(double v, double fill) {
 struct LevelScratch {
   float* sc;     // merged list, scores
   int* meta;     // merged list, packed parent / depth / rank
-  float* bsc;    // a batch's merged children in order / next members: scores
-  int* bmp;      //   ... parent places / places
-  int* brk;      //   ... ranks
-  int* bpos;     //   ... kept nodes ahead of them
+  float* bsc;    // next level's members: scores
+  int* bmp;      //   ... places in the kept list
 };
 
 // Children per member below which a level is merged in batches (one lane per
@@ -449,15 +447,27 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
     load_row(d + 1, qn);
     if (kr <= kBatchK) {
       // Batches of the members' children, one candidate per lane (member
-      // t0 + lane / kr, rank lane % kr), merged in member order: a child of a
-      // later batch ranks after an equal-score child of an earlier one (its
-      // parent comes later), which the merged list already holds, so the
-      // place rule stays "children of the batch ahead + kept nodes of equal
-      // or higher score".
+      // t0 + lane / kr, rank lane % kr), sorted across the lanes, merged in
+      // member order: a child of a later batch ranks after an equal-score
+      // child of an earlier one (its parent comes later), which the merged
+      // list already holds, so the place rule stays "children of the batch
+      // ahead + kept nodes of equal or higher score".
       const int per = 64 / kr;
       const int tl = lane / kr, rl = lane - tl * kr;
       bool stopped = false;
+      const float q0 = readlane_f32(qd[0], 0);
       for (int t0 = 0; t0 < m; t0 += per) {
+        // the batch's best possible child: the first child of its first
+        // member (members pushed out, place -1, are a suffix); with the kept
+        // list full it must beat the last kept node, else no later child can
+        {
+          const float ms0 = t0 < 64 ? readlane_f32(M_sc[0], t0 & 63) : readlane_f32(M_sc[SL - 1], t0 & 63);
+          const int mp0 = t0 < 64 ? __builtin_amdgcn_readlane(M_pos[0], t0 & 63)
+                                  : __builtin_amdgcn_readlane(M_pos[SL - 1], t0 & 63);
+          const float last = (cap - 1) < 64 ? readlane_f32(K_sc[0], (cap - 1) & 63)
+                                            : readlane_f32(K_sc[SL - 1], (cap - 1) & 63);
+          if (mp0 < 0 || (c == cap && !(__fmul_rn(ms0, q0) > last))) break;
+        }
         const int other = claim_load(winner);
         const int nb = (m - t0 < per ? m - t0 : per) * kr;
         const int t = t0 + tl;
@@ -474,11 +484,13 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
         // has at least cap kept nodes of higher or equal score ahead of it,
         // so none of its children can make the cut
         const bool valid = lane < nb && mpos >= 0;
-        const float v = __fmul_rn(msc, qr);
-        const uint64_t key = valid ? frontier_key(v, d, mpos, rl) : 0;
-        // place among the batch's children (keys are distinct)
-        int rank = 0;
-        for (int j = 0; j < nb; ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
+        // the batch's children in selection order: lane i holds the i-th
+        // (0 = none); the key carries score, parent place and rank
+        const uint64_t key = sort64_desc(valid ? frontier_key(__fmul_rn(msc, qr), d, mpos, rl) : 0, lane);
+        const uint32_t wl = static_cast<uint32_t>(key);
+        const int crank = 127 - static_cast<int>(wl & 127);
+        const int cpar = 255 - static_cast<int>((wl >> 7) & 255) - 1;
+        const float v = key_score(key);
         // kept nodes of equal or higher score: the kept list's scores do not
         // increase along it, so the first place whose score is below v
         int lo = 0, hi = c;
@@ -496,38 +508,46 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
           }
         }
         const int pos = lo;
-        const bool enter = valid && rank + pos < cap;
-        const uint64_t em = __ballot(enter);
-        const int na = __popcll(em);
+        const bool enter = key != 0 && lane + pos < cap;
+        const int na = __popcll(__ballot(enter));   // a prefix of the lanes
         if (na == 0) {
           // the batch's best child did not make the cut: the later batches'
           // children score no higher (their members score no higher)
           if (claim_seen(other)) stopped = true;
           break;
         }
-        if (enter) {
-          w.bsc[rank] = v;
-          w.bmp[rank] = mpos;
-          w.brk[rank] = rl;
-          w.bpos[rank] = pos;
-        }
-        wave_lds_sync();
         float C_sc[SL];
         int C_mp[SL], C_rank[SL], C_pos[SL], sh[SL], npK[SL];
 #pragma unroll
         for (int s = 0; s < SL; ++s) {
           const bool on = s == 0 && lane < na;
-          C_sc[s] = on ? w.bsc[lane] : 0.f;
-          C_mp[s] = on ? w.bmp[lane] : 0;
-          C_rank[s] = on ? w.brk[lane] : 0;
-          C_pos[s] = on ? w.bpos[lane] : 0;
-          sh[s] = 0;
+          C_sc[s] = on ? v : 0.f;
+          C_mp[s] = on ? cpar : 0;
+          C_rank[s] = on ? crank : 0;
+          C_pos[s] = on ? pos : 0;
         }
-        for (int j = 0; j < na; ++j) {
-          const int pj = __builtin_amdgcn_readlane(C_pos[0], j);
+        // children placed ahead of kept place P: those with C_pos <= P, a
+        // prefix of them (C_pos does not decrease along the children)
+        int slo[SL], shi[SL];
 #pragma unroll
-          for (int s = 0; s < SL; ++s) sh[s] += pj <= s * 64 + lane ? 1 : 0;
+        for (int s = 0; s < SL; ++s) {
+          slo[s] = 0;
+          shi[s] = na;
         }
+#pragma unroll
+        for (int it = 0; it < 7; ++it) {
+#pragma unroll
+          for (int s = 0; s < SL; ++s) {
+            const int mid = (slo[s] + shi[s]) >> 1;
+            const int pm = bperm_i(mid & 63, C_pos[0]);
+            if (slo[s] < shi[s]) {
+              if (pm <= s * 64 + lane) slo[s] = mid + 1;
+              else shi[s] = mid;
+            }
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < SL; ++s) sh[s] = slo[s];
         apply_merge(na, d, C_sc, C_mp, C_rank, C_pos, sh, npK);
         // members' places after the merge (-1 once pushed past place cap)
 #pragma unroll
@@ -793,7 +813,7 @@ __global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
   __shared__ int n_par[128], n_dep[128], n_rank[128];
   __shared__ float n_sc[128];
   __shared__ float l_sc[128], l_bsc[128];
-  __shared__ int l_meta[128], l_bmp[128], l_brk[128], l_bpos[128];
+  __shared__ int l_meta[128], l_bmp[128];
   __shared__ int s_winner;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -819,7 +839,7 @@ __global__ __launch_bounds__(128) void best_first_pos_kernel(TreeArgs a) {
   } else {
     float K_sc[SL];
     int K_meta[SL];
-    const LevelScratch w{l_sc, l_meta, l_bsc, l_bmp, l_brk, l_bpos};
+    const LevelScratch w{l_sc, l_meta, l_bsc, l_bmp};
     const int n = a.method == 1 ? -1 : level_select<SL, ADAPTIVE>(a, b, lane, s_p, w, &s_winner, K_sc, K_meta);
     if (n >= 0 && claim(&s_winner, 2)) {
 #pragma unroll

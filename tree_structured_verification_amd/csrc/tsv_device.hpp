@@ -117,6 +117,32 @@ __device__ __forceinline__ uint64_t reverse_lanes_u64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// One compare-exchange stage of a bitonic network over the 64 lanes: lanes
+// l and l ^ J swap so that the block of K lanes holding l ends up descending
+// (or ascending, for every other block when K < 64).
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t x, int lane) {
+  const uint64_t y = xor_lane_u64<J>(x);
+  const bool lower = (lane & J) == 0;
+  const bool desc = (lane & K) == 0;
+  return (lower == desc) ? umax64(x, y) : umin64(x, y);
+}
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_pass(uint64_t x, int lane) {
+  x = bitonic_stage<K, J>(x, lane);
+  if constexpr (J > 1) x = bitonic_pass<K, J / 2>(x, lane);
+  return x;
+}
+// Sorts one key per lane, descending over lanes 0..63.
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
+  x = bitonic_pass<2, 1>(x, lane);
+  x = bitonic_pass<4, 2>(x, lane);
+  x = bitonic_pass<8, 4>(x, lane);
+  x = bitonic_pass<16, 8>(x, lane);
+  x = bitonic_pass<32, 16>(x, lane);
+  return bitonic_pass<64, 32>(x, lane);
+}
+
 // max(a, b, c) of finite floats in one instruction.  Written as asm because
 // the compiler quiets signalling NaNs of loaded values before fmaxf (one
 // extra instruction per value); inputs here are finite by contract.
