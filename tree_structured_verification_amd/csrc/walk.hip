@@ -47,81 +47,113 @@ struct Vec16<uint16_t> {
 // (strict comparison, so ties stay with the earlier group); the first element
 // of that group equal to the maximum is found once at the end.  Ties across
 // lanes are settled by the key (lower index).
+constexpr int kMinSegments = 8;
+
+// Workgroups of one argmax launch at most: about what the compute units hold
+// at once (five of these workgroups per CU at the kernel's register use), so
+// that every task a wave steps to is taken without waiting for a later
+// workgroup's dispatch.
+constexpr int kArgmaxGrid = 1280;
+constexpr int kArgmaxStagedB = 1024;   // requests whose node counts go to LDS
+
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void argmax_segment_kernel(
     const T* __restrict__ logits, int B, int N_max, int V, int nseg, int seg_len,
     const int* __restrict__ n_nodes, uint64_t* __restrict__ seg_best) {
+  __shared__ int s_n[kArgmaxStagedB];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows_per_b = N_max + 1;
-  const int task = blockIdx.x * 4 + wave;
-  if (task >= B * rows_per_b * nseg) return;
-  const int row = task / nseg, seg = task - row * nseg;
-  const int b = row / rows_per_b, r = row - b * rows_per_b;
-  const int n = clampi(n_nodes[b], 0, N_max);
-  if (r > n) return;  // row never read by the walk
-  const int beg = seg * seg_len;
-  const int end = min(V, beg + seg_len);
-  const T* p = logits + static_cast<size_t>(row) * V;
+  const int tasks = B * rows_per_b * nseg;
+  // node counts staged once per workgroup (a task then skips without a
+  // global round trip); larger batches read them per task
+  const bool staged = B <= kArgmaxStagedB;
+  if (staged)
+    for (int i = threadIdx.x; i < B; i += blockDim.x) s_n[i] = clampi(n_nodes[i], 0, N_max);
+  __syncthreads();
+  // the grid holds at most kArgmaxGrid workgroups: a wave takes tasks
+  // task, task + 4 * gridDim.x, ... (rows past a request's node count are
+  // skipped in a few instructions, so small trees cost no dispatch); task =
+  // (b * rows_per_b + r) * nseg + seg, decoded once and then advanced by the
+  // stride's own (request, row, segment) steps with carries
+  const int t0 = blockIdx.x * 4 + wave, S = gridDim.x * 4;
+  int seg = t0 % nseg, r = (t0 / nseg) % rows_per_b, b = (t0 / nseg) / rows_per_b;
+  const int dseg = S % nseg, drow = S / nseg, dr = drow % rows_per_b, db = drow / rows_per_b;
+  for (int task = t0; task < tasks; task += S) {
+    const int cb = b, cr = r, cs = seg;   // this task
+    seg += dseg;                          // the wave's next task
+    const int c1 = seg >= nseg ? 1 : 0;
+    seg -= c1 * nseg;
+    r += dr + c1;
+    const int c2 = r >= rows_per_b ? 1 : 0;
+    r -= c2 * rows_per_b;
+    b += db + c2;
+    const int n = staged ? s_n[cb] : clampi(n_nodes[cb], 0, N_max);
+    if (cr > n) continue;  // row never read by the walk
+    const int row = cb * rows_per_b + cr;
+    const int beg = cs * seg_len;
+    const int end = min(V, beg + seg_len);
+    const T* p = logits + static_cast<size_t>(row) * V;
 
-  float bv = -INFINITY;
-  int bi = -1;
-  if (VEC) {
-    constexpr int N = Vec16<T>::N;
-    constexpr int STEP = 64 * N;
-    constexpr int BLK = 8 * STEP;  // elements per block of 8 loads per lane
-    int bg = -1;  // first element of the group holding this lane's maximum
-    // groups lie wholly inside or outside [beg, end) (V and the segment
-    // bounds are multiples of N); a group past the end re-reads the last
-    // group of the slice and is then ignored, so every load is in bounds and
-    // unconditional
-    auto load_block = [&](uint4 (&raw)[8], int base) {
+    float bv = -INFINITY;
+    int bi = -1;
+    if (VEC) {
+      constexpr int N = Vec16<T>::N;
+      constexpr int STEP = 64 * N;
+      constexpr int BLK = 8 * STEP;  // elements per block of 8 loads per lane
+      int bg = -1;  // first element of the group holding this lane's maximum
+      // groups lie wholly inside or outside [beg, end) (V and the segment
+      // bounds are multiples of N); a group past the end re-reads the last
+      // group of the slice and is then ignored, so every load is in bounds and
+      // unconditional
+      auto load_block = [&](uint4 (&raw)[8], int base) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = min(base + u * STEP + lane * N, end - N);
-        raw[u] = *reinterpret_cast<const uint4*>(p + e);
+        for (int u = 0; u < 8; ++u) {
+          const int e = min(base + u * STEP + lane * N, end - N);
+          raw[u] = *reinterpret_cast<const uint4*>(p + e);
+        }
+      };
+      auto process = [&](const uint4 (&raw)[8], int base) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float v[N];
+          Vec16<T>::widen(raw[u], v);
+          float m = vmax3(v[0], v[1], v[2]);
+#pragma unroll
+          for (int c = 3; c < N; c += 2) m = vmax3(m, v[c], v[c + 1 < N ? c + 1 : c]);
+          const int e = base + u * STEP + lane * N;
+          const bool up = e < end && m > bv;
+          bv = up ? m : bv;
+          bg = up ? e : bg;
+        }
+      };
+      // two register blocks in turn: one in flight while the other is scanned
+      uint4 b0[8], b1[8];
+      load_block(b0, beg);
+      for (int base = beg; base < end; base += 2 * BLK) {
+        if (base + BLK < end) load_block(b1, base + BLK);
+        process(b0, base);
+        if (base + BLK >= end) break;
+        if (base + 2 * BLK < end) load_block(b0, base + 2 * BLK);
+        process(b1, base + BLK);
       }
-    };
-    auto process = [&](const uint4 (&raw)[8], int base) {
+      if (bg >= 0) {
+        float w[N];
+        Vec16<T>::widen(*reinterpret_cast<const uint4*>(p + bg), w);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float v[N];
-        Vec16<T>::widen(raw[u], v);
-        float m = vmax3(v[0], v[1], v[2]);
-#pragma unroll
-        for (int c = 3; c < N; c += 2) m = vmax3(m, v[c], v[c + 1 < N ? c + 1 : c]);
-        const int e = base + u * STEP + lane * N;
-        const bool up = e < end && m > bv;
-        bv = up ? m : bv;
-        bg = up ? e : bg;
+        for (int c = N - 1; c >= 0; --c) bi = (w[c] == bv) ? bg + c : bi;
       }
-    };
-    // two register blocks in turn: one in flight while the other is scanned
-    uint4 b0[8], b1[8];
-    load_block(b0, beg);
-    for (int base = beg; base < end; base += 2 * BLK) {
-      if (base + BLK < end) load_block(b1, base + BLK);
-      process(b0, base);
-      if (base + BLK >= end) break;
-      if (base + 2 * BLK < end) load_block(b0, base + 2 * BLK);
-      process(b1, base + BLK);
+    } else {
+      for (int e = beg + lane; e < end; e += 64) {
+        float v = Vec16<T>::one(p + e);
+        bool better = v > bv || bi < 0;
+        bv = better ? v : bv;
+        bi = better ? e : bi;
+      }
     }
-    if (bg >= 0) {
-      float w[N];
-      Vec16<T>::widen(*reinterpret_cast<const uint4*>(p + bg), w);
-#pragma unroll
-      for (int c = N - 1; c >= 0; --c) bi = (w[c] == bv) ? bg + c : bi;
-    }
-  } else {
-    for (int e = beg + lane; e < end; e += 64) {
-      float v = Vec16<T>::one(p + e);
-      bool better = v > bv || bi < 0;
-      bv = better ? v : bv;
-      bi = better ? e : bi;
-    }
+    uint64_t key = bi < 0 ? 0 : sel_key(bv, static_cast<uint32_t>(bi));
+    key = wave_max_u64(key);
+    if (lane == 0) seg_best[task] = key;
   }
-  uint64_t key = bi < 0 ? 0 : sel_key(bv, static_cast<uint32_t>(bi));
-  key = wave_max_u64(key);
-  if (lane == 0) seg_best[task] = key;
 }
 
 __global__ __launch_bounds__(64) void walk_kernel(
@@ -208,7 +240,12 @@ ArgmaxPlan argmax_plan(int rows, int V, int dtype) {
   p.V = V;
   const int per16 = dtype == TSV_F32 ? 4 : 8;
   p.vec = (V % per16) == 0;
+  // enough waves when every row is read, and at least kMinSegments per row:
+  // the rows read are only those of each request's nodes (device-side
+  // counts), which may be far fewer than the rows the plan covers, and the
+  // waves of unread rows' segments end at once
   int want = (kScanWaves + rows - 1) / rows;
+  want = want > kMinSegments ? want : kMinSegments;
   int most = V / 4096 > 1 ? V / 4096 : 1;
   int nseg = want < most ? want : most;
   if (nseg < 1) nseg = 1;
@@ -226,7 +263,8 @@ hipError_t launch_accept_walk(const void* logits, int dtype, int B, int N_max,
                               int* out_tokens, uint64_t* seg_best,
                               const ArgmaxPlan& p, hipStream_t s) {
   const int tasks = B * (N_max + 1) * p.nseg;
-  dim3 grid((tasks + 3) / 4), block(256);
+  const int wgs = (tasks + 3) / 4;
+  dim3 grid(wgs < kArgmaxGrid ? wgs : kArgmaxGrid), block(256);
   if (dtype == TSV_F32) {
     if (p.vec)
       argmax_segment_kernel<float, true><<<grid, block, 0, s>>>(
