@@ -307,10 +307,11 @@ __device__ __forceinline__ void store_serial_records(int n, int lane, const floa
 // selection order (a sorted frontier of one entry per member: a member's
 // children are ranked by probability) until the next child would fall at or
 // beyond place cap; a child ranks after every kept node of equal or higher
-// score, since it is deeper than all of them.  Cheap when few nodes below
-// depth 1 make the cut (flat drafter distributions); a peaked distribution
-// re-merges many nodes at every level, which is why the serial pops run
-// beside it.
+// score, since it is deeper than all of them.  With short lists (k <= 8) a
+// level's children are merged in batches of up to 64 instead of one at a
+// time.  Cheap when few nodes below depth 1 make the cut (flat drafter
+// distributions); a peaked distribution re-merges many nodes at every level,
+// which is why the serial pops run beside it.
 __device__ __forceinline__ int meta_pack(int par, int dep, int rank) { return (par + 1) | (dep << 8) | (rank << 16); }
 __device__ __forceinline__ int meta_par(int v) { return (v & 255) - 1; }
 __device__ __forceinline__ int meta_dep(int v) { return (v >> 8) & 127; }
