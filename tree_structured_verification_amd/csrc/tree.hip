@@ -350,13 +350,38 @@ struct LevelScratch {
   float* sc;     // merged list, scores
   int* meta;     // merged list, packed parent / depth / rank
   float* bsc;    // next level's members: scores
-  int* bmp;      //   ... places in the kept list
+  int* bmp;      //   ... places in the kept list; during a batch, old place -> new place
 };
 
 // Children per member below which a level is merged in batches (one lane per
 // candidate child) rather than one child at a time.
 constexpr int kBatchK = 8;
 
+// Order of the batched merge (larger = earlier): score, then kept nodes ahead
+// of children, then a smaller index (kept place or child index) first.
+__device__ __forceinline__ uint64_t merge_key(float sc, bool kept, int idx) {
+  return (static_cast<uint64_t>(ord_f32(sc)) << 32) | (kept ? 0x80000000u : 0u) |
+         static_cast<uint32_t>(0xFFFF - idx);
+}
+// A bitonic sequence of 64 (key, origin) pairs across the lanes sorted
+// descending: compare-exchanges at lane distances 32 .. 1.
+template <int J>
+__device__ __forceinline__ void kv_stage(uint64_t& k, int& o, int lane) {
+  const uint64_t y = xor_lane_u64<J>(k);
+  const int yo = static_cast<int>(xor_lane_u32<J>(static_cast<uint32_t>(o)));
+  const bool lower = (lane & J) == 0;
+  const bool take = lower ? y > k : y < k;
+  k = take ? y : k;
+  o = take ? yo : o;
+}
+__device__ __forceinline__ void kv_merge64(uint64_t& k, int& o, int lane) {
+  kv_stage<32>(k, o, lane);
+  kv_stage<16>(k, o, lane);
+  kv_stage<8>(k, o, lane);
+  kv_stage<4>(k, o, lane);
+  kv_stage<2>(k, o, lane);
+  kv_stage<1>(k, o, lane);
+}
 __device__ __forceinline__ int bperm_i(int src_lane, int v) {
   return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
 }
@@ -491,73 +516,94 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
         const uint32_t wl = static_cast<uint32_t>(key);
         const int crank = 127 - static_cast<int>(wl & 127);
         const int cpar = 255 - static_cast<int>((wl >> 7) & 255) - 1;
-        const float v = key_score(key);
-        // kept nodes of equal or higher score: the kept list's scores do not
-        // increase along it, so the first place whose score is below v
-        int lo = 0, hi = c;
+        const float cv = key_score(key);
+        // Merge the batch into the kept list with one bitonic network: merge
+        // keys order by score, kept nodes ahead of children on equal scores,
+        // then by place / by child index; each entry carries its origin (kept
+        // place P, or 128 + child index).  The kept list and the reversed
+        // batch form a bitonic sequence whose larger half, taken place by
+        // place, holds the first 64 * SL entries, still bitonic.
+        uint64_t mk[SL];
+        int org[SL];
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int mid = (lo + hi) >> 1;
-          float km = bperm_f(mid & 63, K_sc[0]);
-          if constexpr (SL > 1) {
-            const float km1 = bperm_f(mid & 63, K_sc[SL - 1]);
-            km = mid < 64 ? km : km1;
-          }
-          if (lo < hi) {
-            if (km >= v) lo = mid + 1;
-            else hi = mid;
-          }
+        for (int s = 0; s < SL; ++s) {
+          const int P = s * 64 + lane;
+          mk[s] = P < c ? merge_key(K_sc[s], true, P) : 0;
+          org[s] = P;
         }
-        const int pos = lo;
-        const bool enter = key != 0 && lane + pos < cap;
-        const int na = __popcll(__ballot(enter));   // a prefix of the lanes
+        {
+          const uint64_t ckr = reverse_lanes_u64(key != 0 ? merge_key(cv, false, lane) : 0);
+          const bool t = ckr > mk[SL - 1];
+          mk[SL - 1] = t ? ckr : mk[SL - 1];
+          org[SL - 1] = t ? 128 + 63 - lane : org[SL - 1];
+        }
+        if constexpr (SL > 1) {
+          const bool t = mk[1] > mk[0];
+          const uint64_t k0 = mk[0];
+          const int o0 = org[0];
+          mk[0] = t ? mk[1] : mk[0];
+          org[0] = t ? org[1] : org[0];
+          mk[1] = t ? k0 : mk[1];
+          org[1] = t ? o0 : org[1];
+        }
+#pragma unroll
+        for (int s = 0; s < SL; ++s) kv_merge64(mk[s], org[s], lane);
+        // the new kept list: its first cap entries
+        int nk = 0, na = 0;
+#pragma unroll
+        for (int s = 0; s < SL; ++s) {
+          const bool keep = mk[s] != 0 && s * 64 + lane < cap;
+          nk += __popcll(__ballot(keep));
+          na += __popcll(__ballot(keep && org[s] >= 128));
+        }
         if (na == 0) {
-          // the batch's best child did not make the cut: the later batches'
-          // children score no higher (their members score no higher)
+          // no child of the batch made the cut (the kept list is unchanged):
+          // the later batches' children score no higher
           if (claim_seen(other)) stopped = true;
           break;
         }
-        float C_sc[SL];
-        int C_mp[SL], C_rank[SL], C_pos[SL], sh[SL], npK[SL];
+        // old place -> new place (-1: pushed past place cap)
+#pragma unroll
+        for (int s = 0; s < SL; ++s)
+          if (s * 64 + lane < c) w.bmp[s * 64 + lane] = -1;
+#pragma unroll
+        for (int s = 0; s < SL; ++s)
+          if (s * 64 + lane < nk && org[s] < 128) w.bmp[org[s]] = s * 64 + lane;
+        // the origins' data: a kept node's score and packed record, a
+        // child's parent place and rank (lane permutes of the old registers)
+        float nsc[SL];
+        int nmeta[SL];
 #pragma unroll
         for (int s = 0; s < SL; ++s) {
-          const bool on = s == 0 && lane < na;
-          C_sc[s] = on ? v : 0.f;
-          C_mp[s] = on ? cpar : 0;
-          C_rank[s] = on ? crank : 0;
-          C_pos[s] = on ? pos : 0;
-        }
-        // children placed ahead of kept place P: those with C_pos <= P, a
-        // prefix of them (C_pos does not decrease along the children)
-        int slo[SL], shi[SL];
-#pragma unroll
-        for (int s = 0; s < SL; ++s) {
-          slo[s] = 0;
-          shi[s] = na;
-        }
-#pragma unroll
-        for (int it = 0; it < 7; ++it) {
-#pragma unroll
-          for (int s = 0; s < SL; ++s) {
-            const int mid = (slo[s] + shi[s]) >> 1;
-            const int pm = bperm_i(mid & 63, C_pos[0]);
-            if (slo[s] < shi[s]) {
-              if (pm <= s * 64 + lane) slo[s] = mid + 1;
-              else shi[s] = mid;
-            }
+          const int o = org[s];
+          const int src = o & 63;
+          float ks = bperm_f(src, K_sc[0]);
+          int km = bperm_i(src, K_meta[0]);
+          if constexpr (SL > 1) {
+            const float ks1 = bperm_f(src, K_sc[SL - 1]);
+            const int km1 = bperm_i(src, K_meta[SL - 1]);
+            ks = (o & 64) ? ks1 : ks;
+            km = (o & 64) ? km1 : km;
           }
+          const int cp = bperm_i(src, cpar);
+          const int crk = bperm_i(src, crank);
+          const float cs = bperm_f(src, cv);
+          const bool kept = o < 128;
+          nsc[s] = kept ? ks : cs;
+          nmeta[s] = kept ? km : meta_pack(cp, d, crk);   // parent: old place for now
         }
-#pragma unroll
-        for (int s = 0; s < SL; ++s) sh[s] = slo[s];
-        apply_merge(na, d, C_sc, C_mp, C_rank, C_pos, sh, npK);
-        // members' places after the merge (-1 once pushed past place cap)
+        wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < SL; ++s) {
-          const int a0 = bperm_i(M_pos[s] & 63, npK[0]);
-          const int a1 = SL > 1 ? bperm_i(M_pos[s] & 63, npK[SL - 1]) : a0;
-          const int np = M_pos[s] < 64 ? a0 : a1;
-          M_pos[s] = (M_pos[s] >= 0 && np < cap) ? np : -1;
+          const int P = s * 64 + lane;
+          const int po = meta_par(nmeta[s]);   // garbage past the new count: index kept in range
+          const int pn = po < 0 ? -1 : w.bmp[po & 127];
+          K_sc[s] = P < nk ? nsc[s] : 0.f;
+          K_meta[s] = P < nk ? meta_pack(pn, meta_dep(nmeta[s]), meta_rank(nmeta[s])) : 0;
+          // members' places after the merge (-1 once pushed past place cap)
+          M_pos[s] = M_pos[s] >= 0 ? w.bmp[M_pos[s] & 127] : -1;
         }
+        c = nk;
         if (claim_seen(other)) {
           stopped = true;
           break;
