@@ -111,6 +111,28 @@ def test_peaked_drafter(sigma):
         _run(marg, top_k, cap, 128, cost, prefix)
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes(case):
+    """Seeded mix of shapes around the selection paths' boundaries: list
+    lengths on both sides of the batched merge (8 / 9), caps around 64 and
+    not multiples of the list length, one position, deep lists, flat and
+    peaked marginals, fixed and adaptive budgets."""
+    rng = np.random.default_rng(1000 + case)
+    gamma = int(rng.choice([1, 2, 5, 9, 16, 24]))
+    top_k = int(rng.choice([1, 2, 3, 7, 8, 9, 16, 33, 64]))
+    V = int(rng.choice([top_k, 97, 2000]))
+    V = max(V, top_k)
+    cap = int(rng.choice([1, 5, 31, 63, 64, 65, 100, 128]))
+    sigma = float(rng.choice([0.5, 3.0, 9.0]))
+    marg = _softmax_rows(rng, (3, gamma, V), sigma)
+    if case % 3 == 2:
+        cost = Cost(a=1.0, b=float(rng.choice([1e-6, 1e-3, 0.02])), c=1e-5, e=1e-7, c_d=0.5)
+        prefix = rng.integers(0, 40000, size=3).astype(np.int32)
+        _run(marg, top_k, cap, 128, cost, prefix)
+    else:
+        _run(marg, top_k, cap, 128)
+
+
 def test_adaptive_scores_below_exact_range():
     """Near-uniform marginals over a large vocabulary: depth-2 scores fall
     below 2^-23, so the throughput sums past them are taken one at a time;
