@@ -945,7 +945,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library runs on one GPU; sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
 
     global KV_LAYOUT
