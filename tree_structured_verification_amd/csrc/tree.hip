@@ -405,7 +405,9 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
 
   // members of the next level (lane t of slot s: member 64 s + t, in
   // selection order): at depth 1 the whole kept list; afterwards the children
-  // merged at the level before, which all made the cut
+  // merged at the level before, which all made the cut (the batched merge,
+  // whose later batches can push out earlier ones' children, compacts the
+  // kept nodes of the level's depth instead)
   int m = c;
   float M_sc[SL];
   int M_pos[SL];
