@@ -219,3 +219,19 @@ def test_contract_call_matches_variants(adaptive):
     for k in outs:
         assert torch.equal(outs[k], g_topk[k]), k
         assert torch.equal(outs[k], g_fit[k]), k
+
+
+@pytest.mark.parametrize("top_k", [1, 2, 4, 8, 6])
+def test_short_lists_deep_trees(top_k):
+    """Short per-position lists (the batched level merge: list lengths that
+    are powers of two take the rank-by-rank layout, 6 the full sort) in deep
+    trees, with quantised scores (equal children of different parents) and
+    flat and peaked marginals, capacities below, at and past 64."""
+    rng = np.random.default_rng(300 + top_k)
+    for sigma in (0.5, 3.0, 9.0):
+        marg = _softmax_rows(rng, (3, 16, 211), sigma)
+        for cap in (16, 64, 65, 128):
+            _run(marg, top_k, cap, 128)
+    marg = _quantised(rng, (3, 16, 211), 3)
+    for cap in (40, 128):
+        _run(marg, top_k, cap, 128)
