@@ -474,29 +474,14 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
   for (int d = 2; d <= a.gamma && m > 0; ++d) {
     load_row(d + 1, qn);
     if (kr <= kBatchK) {
-      // Batches of the members' children, one candidate per lane, sorted
-      // across the lanes, merged in member order: a child of a later batch
-      // ranks after an equal-score child of an earlier one (its parent comes
-      // later), which the merged list already holds, so the place rule stays
-      // "children of the batch ahead + kept nodes of equal or higher score".
-      // When kr is a power of two the lanes hold the batch rank by rank
-      // (rank lane / per), members in order, every other rank reversed: the
-      // children of one rank are already in selection order (members are,
-      // and a member's score times a fixed probability keeps their order,
-      // the parent's place breaking ties), so the lanes form bitonic runs
-      // and log2(kr) merge passes sort them.  Otherwise member t0 + lane /
-      // kr, rank lane % kr, and a full sort.
+      // Batches of the members' children, one candidate per lane (member
+      // t0 + lane / kr, rank lane % kr), sorted across the lanes, merged in
+      // member order: a child of a later batch ranks after an equal-score
+      // child of an earlier one (its parent comes later), which the merged
+      // list already holds, so the place rule stays "children of the batch
+      // ahead + kept nodes of equal or higher score".
       const int per = 64 / kr;
-      const bool runs = (kr & (kr - 1)) == 0;
-      int tl, rl;
-      if (runs) {
-        rl = lane / per;
-        const int c = lane - rl * per;
-        tl = (rl & 1) ? per - 1 - c : c;
-      } else {
-        tl = lane / kr;
-        rl = lane - tl * kr;
-      }
+      const int tl = lane / kr, rl = lane - tl * kr;
       bool stopped = false;
       const float q0 = readlane_f32(qd[0], 0);
       for (int t0 = 0; t0 < m; t0 += per) {
@@ -512,6 +497,7 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
           if (mp0 < 0 || (c == cap && !(__fmul_rn(ms0, q0) > last))) break;
         }
         const int other = claim_load(winner);
+        const int nb = (m - t0 < per ? m - t0 : per) * kr;
         const int t = t0 + tl;
         float msc = bperm_f(t & 63, M_sc[0]);
         int mpos = bperm_i(t & 63, M_pos[0]);
@@ -525,14 +511,10 @@ __device__ __forceinline__ int level_select(const TreeArgs& a, int b, int lane, 
         // a member pushed out of the kept list by an earlier batch (place -1)
         // has at least cap kept nodes of higher or equal score ahead of it,
         // so none of its children can make the cut
-        const bool valid = lane < per * kr && t < m && mpos >= 0;
+        const bool valid = lane < nb && mpos >= 0;
         // the batch's children in selection order: lane i holds the i-th
         // (0 = none); the key carries score, parent place and rank
-        uint64_t key = valid ? frontier_key(__fmul_rn(msc, qr), d, mpos, rl) : 0;
-        if (!runs) key = sort64_desc(key, lane);
-        else if (kr == 2) key = bitonic_pass<64, 32>(key, lane);
-        else if (kr == 4) key = bitonic_pass<64, 32>(bitonic_pass<32, 16>(key, lane), lane);
-        else if (kr == 8) key = bitonic_pass<64, 32>(bitonic_pass<32, 16>(bitonic_pass<16, 8>(key, lane), lane), lane);
+        const uint64_t key = sort64_desc(valid ? frontier_key(__fmul_rn(msc, qr), d, mpos, rl) : 0, lane);
         const uint32_t wl = static_cast<uint32_t>(key);
         const int crank = 127 - static_cast<int>(wl & 127);
         const int cpar = 255 - static_cast<int>((wl >> 7) & 255) - 1;
@@ -819,39 +801,31 @@ __device__ __forceinline__ void write_tree(const TreeArgs& a, int b, int tid, in
                                            const NodeRecords& o) {
   const int W = (a.N_max + 31) >> 5;
   const size_t nb = static_cast<size_t>(b) * a.N_max;
-  // a thread writes nodes i and i + nth; their ancestor chains (parents
-  // precede children) are walked side by side
-  for (int i = tid; i < a.N_max; i += 2 * nth) {
-    const int i2 = i + nth;
-    uint32_t w[2][4] = {};
-    int j[2] = {i < n ? i : -1, i2 < n ? i2 : -1};
-    while (j[0] >= 0 || j[1] >= 0) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (j[h] < 0) continue;
-        const uint32_t bit = 1u << (j[h] & 31);
-        const int wi = j[h] >> 5;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[h][q] |= wi == q ? bit : 0u;
-        j[h] = o.par[j[h]];
+  for (int i = tid; i < a.N_max; i += nth) {
+    const bool v = i < n;
+    a.parent[nb + i] = v ? o.par[i] : -1;
+    const int trow = v ? (PER_NODE ? o.row[i] : o.dep[i] - 1) : 0;
+    a.token[nb + i] = v ? s_i[trow * a.k + o.rank[i]] : -1;
+    a.depth[nb + i] = v ? o.dep[i] : -1;
+    a.score[nb + i] = v ? o.sc[i] : 0.0f;
+    uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+    if (v) {
+      int j = i;
+      while (j >= 0) {
+        const uint32_t bit = 1u << (j & 31);
+        const int wi = j >> 5;
+        if (wi == 0) w0 |= bit;
+        else if (wi == 1) w1 |= bit;
+        else if (wi == 2) w2 |= bit;
+        else w3 |= bit;
+        j = o.par[j];
       }
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int x = h == 0 ? i : i2;
-      if (x >= a.N_max) continue;
-      const bool v = x < n;
-      a.parent[nb + x] = v ? o.par[x] : -1;
-      const int trow = v ? (PER_NODE ? o.row[x] : o.dep[x] - 1) : 0;
-      a.token[nb + x] = v ? s_i[trow * a.k + o.rank[x]] : -1;
-      a.depth[nb + x] = v ? o.dep[x] : -1;
-      a.score[nb + x] = v ? o.sc[x] : 0.0f;
-      unsigned* dst = a.anc_bits + (nb + x) * W;
-      dst[0] = w[h][0];
-      if (W > 1) dst[1] = w[h][1];
-      if (W > 2) dst[2] = w[h][2];
-      if (W > 3) dst[3] = w[h][3];
-    }
+    unsigned* dst = a.anc_bits + (nb + i) * W;
+    dst[0] = w0;
+    if (W > 1) dst[1] = w1;
+    if (W > 2) dst[2] = w2;
+    if (W > 3) dst[3] = w3;
   }
   if (tid == 0) a.n_nodes[b] = n;
 }
