@@ -43,7 +43,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_EHIP; }
 
 struct BuildLayout {
   TopkPlan plan;
-  size_t off_seg, off_idx, off_p, bytes;
+  size_t off_idx, off_p, bytes;
 };
 // rows_per_b: top-k lists per request (gamma positions, or the expanded
 // nodes of build_tree_expand)
@@ -52,8 +52,6 @@ BuildLayout build_layout(int B, int rows_per_b, int V, int top_k) {
   const int rows = B * rows_per_b;
   L.plan = topk_plan(rows, V, top_k);
   size_t off = 0;
-  L.off_seg = off;
-  off = align_up(off + topk_ws_bytes(L.plan));
   L.off_idx = off;
   off = align_up(off + static_cast<size_t>(rows) * top_k * sizeof(int));
   L.off_p = off;
@@ -117,8 +115,7 @@ int launch_build(const float* probs, int B, int rows_per_b, int steps, int V, in
   char* w = static_cast<char*>(ws);
   int* tk_idx = topk_idx ? topk_idx : reinterpret_cast<int*>(w + L.off_idx);
   float* tk_p = topk_p ? topk_p : reinterpret_cast<float*>(w + L.off_p);
-  hipError_t e = launch_topk(probs, L.plan, reinterpret_cast<uint64_t*>(w + L.off_seg),
-                             tk_idx, tk_p, s);
+  hipError_t e = launch_topk(probs, L.plan, tk_idx, tk_p, s);
   if (e != hipSuccess) return TSV_EHIP;
   TreeArgs a;
   a.tk_idx = tk_idx;

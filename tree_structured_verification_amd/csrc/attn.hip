@@ -974,12 +974,6 @@ __device__ __forceinline__ void wait_all_mem() {
 }
 
 // s_waitcnt lgkmcnt(0): this wave's LDS writes done (DMA loads may remain)
-__device__ __forceinline__ void wait_lgkm0() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
-}
-
 // sum of v over the lanes l, l^16, l^32, l^48
 __device__ __forceinline__ float quad_group_sum(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -221,7 +221,7 @@ __device__ __forceinline__ void load_blk(float (&v)[32], const float* p, int bas
 // keeps its own list.
 template <int SLOTS, bool VEC>
 __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
-    const float* __restrict__ x, int rows, int V, int k, int nseg, int seg_len,
+    const float* __restrict__ x, int V, int k, int nseg,
     int* __restrict__ out_idx, float* __restrict__ out_p) {
   __shared__ uint64_t queue[kMaxSegments][64];
   __shared__ uint64_t cand[kMaxCand];
@@ -438,25 +438,21 @@ TopkPlan topk_plan(int rows, int V, int k) {
   const int nb = (V + kBlock - 1) / kBlock;
   const int most = rows > kComputeUnits ? kMaxSegments / 2 : kMaxSegments;
   p.nseg = nb < most ? nb : most;
-  p.seg_len = kBlock;
   return p;
 }
 
-size_t topk_ws_bytes(const TopkPlan&) { return 0; }
-
-hipError_t launch_topk(const float* x, const TopkPlan& p, uint64_t*, int* out_idx, float* out_p,
-                       hipStream_t s) {
+hipError_t launch_topk(const float* x, const TopkPlan& p, int* out_idx, float* out_p, hipStream_t s) {
   dim3 grid(p.rows), block(64 * p.nseg);
   if (p.slots == 1) {
     if (p.vec)
-      topk_row_kernel<1, true><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
+      topk_row_kernel<1, true><<<grid, block, 0, s>>>(x, p.V, p.k, p.nseg, out_idx, out_p);
     else
-      topk_row_kernel<1, false><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
+      topk_row_kernel<1, false><<<grid, block, 0, s>>>(x, p.V, p.k, p.nseg, out_idx, out_p);
   } else {
     if (p.vec)
-      topk_row_kernel<2, true><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
+      topk_row_kernel<2, true><<<grid, block, 0, s>>>(x, p.V, p.k, p.nseg, out_idx, out_p);
     else
-      topk_row_kernel<2, false><<<grid, block, 0, s>>>(x, p.rows, p.V, p.k, p.nseg, p.seg_len, out_idx, out_p);
+      topk_row_kernel<2, false><<<grid, block, 0, s>>>(x, p.V, p.k, p.nseg, out_idx, out_p);
   }
   return hipGetLastError();
 }

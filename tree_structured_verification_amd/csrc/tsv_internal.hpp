@@ -18,13 +18,11 @@ constexpr int kScanWaves = 4096;
 
 // ---- build_tree --------------------------------------------------------
 struct TopkPlan {
-  int rows, V, k, slots, nseg, seg_len;
+  int rows, V, k, slots, nseg;
   bool vec;
 };
 TopkPlan topk_plan(int rows, int V, int k);
-size_t topk_ws_bytes(const TopkPlan& p);  // segment lists only
-hipError_t launch_topk(const float* x, const TopkPlan& p, uint64_t* seg_keys,
-                       int* out_idx, float* out_p, hipStream_t s);
+hipError_t launch_topk(const float* x, const TopkPlan& p, int* out_idx, float* out_p, hipStream_t s);
 
 struct TreeArgs {
   const int* tk_idx;
