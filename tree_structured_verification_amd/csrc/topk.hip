@@ -238,7 +238,11 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
   // The first block is requested before anything else happens; the second
   // once the first has arrived, so that it is in flight while the first one
   // seeds the list (requested together, both land in one burst and nothing
-  // is in flight during the seed).
+  // is in flight during the seed).  A list of 128 takes two sorts and a
+  // merge to seed: its second block is requested after them, still in time
+  // for the first block's offers, leaving the memory path to the compute
+  // unit's other workgroup meanwhile (4-5 us less on 1024 rows of top-128;
+  // the same order costs 1 us with lists of 64).
   float b0[32], b1[32];
   int i0 = wave, i1 = wave + W;
   load_blk<VEC>(b0, p, i0 * kBlock, end, lane);
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only: the first block is here
   asm volatile("" ::: "memory");
-  load_blk<VEC>(b1, p, i1 * kBlock, end, lane);
+  if (SLOTS == 1) load_blk<VEC>(b1, p, i1 * kBlock, end, lane);
 
   WaveSelect<SLOTS> sel;
   sel.init(k, queue[wave], published, wave, W, lane);
@@ -344,6 +348,11 @@ __global__ __launch_bounds__(64 * kMaxSegments) void topk_row_kernel(
     sel.list.v[0] = sort64_desc(k1, lane);
     if (SLOTS > 1) sel.list.merge(sort64_desc(k2, lane));
     sel.set_tau();
+    if (SLOTS > 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_blk<VEC>(b1, p, i1 * kBlock, end, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     offer_block(b0, i0 * kBlock, sel.threshold(), j1, j2);
   }
   // two blocks in turn: one in flight while the other is scanned
