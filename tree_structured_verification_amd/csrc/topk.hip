@@ -443,9 +443,14 @@ TopkPlan topk_plan(int rows, int V, int k) {
   p.vec = (V % 4) == 0;
   // One wave per block of the row, at most kMaxSegments; with more rows than
   // compute units, half as many, so that two rows share a compute unit and
-  // one streams while the other merges.
+  // one streams while the other merges; with more than twice as many rows, a
+  // quarter, so that four rows share one (1024 rows of 151936: all resident
+  // at once, each wave seeding one list for 19 blocks; 136-138 against
+  // 147-148 us with top-128 lists, 117-118 against 122-124 with top-32).
   const int nb = (V + kBlock - 1) / kBlock;
-  const int most = rows > kComputeUnits ? kMaxSegments / 2 : kMaxSegments;
+  const int most = rows > 2 * kComputeUnits ? kMaxSegments / 4
+                   : rows > kComputeUnits   ? kMaxSegments / 2
+                                            : kMaxSegments;
   p.nseg = nb < most ? nb : most;
   return p;
 }
